@@ -1,0 +1,323 @@
+"""Float64 NumPy oracle of the recurrent block's T-loop (test infrastructure only).
+
+Every function states the passage it follows. "techbriefly" is the page
+"Projeto OpenMythos afirma que Claude Mythos e um transformador de profundidade
+recorrente"; "openclawapi" is "Introducao ao OpenMythos" (its Passo sections and
+troubleshooting list); "Dreamer summary" is the gist.science summary of
+"Depth-Recurrent Attention Mixtures" (its Metodologia section).
+
+Readings taken where the pages are silent (each one is listed in the design doc):
+  R1 the block consumes u = h_t + e and returns only its residual branch a + m;
+  R2 sequential pre-norm block: RMSNorm -> attention, RMSNorm -> MoE;
+  R3 RMSNorm eps 1e-6, gains given as inputs (ones);
+  R4 half-split RoPE (pair i with i + d/2), positions 0..S-1 per sequence;
+  R5 query head i reads kv head floor(i*KV/H); scale 1/sqrt(qk head dim);
+  R6 MLA: RMSNorm on both latents, one rope key per token shared by all heads;
+  R7 router: float64 logits, gates = softmax over all experts (no renorm),
+     selection on logits + bias row min(t, rows-1), decided in float32, ties to
+     the lower expert index; dropless experts; shared experts weight 1;
+  R8 depth-wise LoRA on the attention output projection, scale 1, adapter
+     index min(t, n_lora-1);
+  R9 ACT: p = sigmoid(w . h_{t+1}) after each update, cumulative in float32,
+     halt when c >= threshold; a halted token's state is frozen, it still
+     serves as key/value, and it leaves the router, experts and update.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ----------------------------------------------------------------------------
+# elementary pieces
+# ----------------------------------------------------------------------------
+def rmsnorm(x, g, eps=1e-6):
+    """RMSNorm on the residual stream (Dreamer summary, Metodologia; reading R3):
+    x / sqrt(mean(x^2) + eps) * g along the last axis."""
+    x = np.asarray(x, F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(g, F64)
+
+
+def rope_tables(seq, d_r, base):
+    """Rotary angles precomputed up to the sequence length (openclawapi Passo 2,
+    max_seq_len is the RoPE precompute bound): theta_i = base^(-2i/d_r)."""
+    i = np.arange(d_r // 2, dtype=F64)
+    inv_freq = np.power(F64(base), -2.0 * i / d_r)
+    ang = np.arange(seq, dtype=F64)[:, None] * inv_freq[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def apply_rope(x, pos, cos, sin):
+    """Rotate x [n, heads, d_r] at positions pos [n] (reading R4: element i pairs
+    with element i + d_r/2)."""
+    x = np.asarray(x, F64)
+    half = x.shape[-1] // 2
+    c = cos[pos][:, None, :]
+    s = sin[pos][:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def softmax(z, axis=-1):
+    z = np.asarray(z, F64)
+    z = z - np.max(z, axis=axis, keepdims=True)
+    p = np.exp(z)
+    return p / np.sum(p, axis=axis, keepdims=True)
+
+
+def attention_causal(q, k, v, scale):
+    """Causal softmax attention of one head of one sequence: q [S, dq], k [S, dq],
+    v [S, dv] -> [S, dv]; key j is visible to query i iff j <= i."""
+    s = (np.asarray(q, F64) @ np.asarray(k, F64).T) * scale
+    S = s.shape[0]
+    s[np.triu(np.ones((S, S), dtype=bool), 1)] = -np.inf
+    return softmax(s, axis=1) @ np.asarray(v, F64)
+
+
+def gqa_attention(q, k, v, batch, seq):
+    """Grouped-query attention (openclawapi Passo 5; bigsaas MLA vs GQA section):
+    q [N, H, d], k/v [N, KV, d]; query head i reads kv head floor(i*KV/H) (R5)."""
+    N, H, d = q.shape
+    KV = k.shape[1]
+    o = np.empty((N, H, v.shape[2]), F64)
+    for b in range(batch):
+        sl = slice(b * seq, (b + 1) * seq)
+        for i in range(H):
+            j = (i * KV) // H
+            o[sl, i] = attention_causal(q[sl, i], k[sl, j], v[sl, j], 1.0 / np.sqrt(d))
+    return o
+
+
+def mla_attention_explicit(cfg, W, n1, pos, cos, sin):
+    """Multi-latent attention with K and V reconstructed explicitly (openclawapi
+    Passo 5: kv_lora_rank / q_lora_rank latents, qk_rope_head_dim and
+    qk_nope_head_dim per head, v_head_dim; each step rebuilds K/V from the latent
+    by a linear projection). Readings R4-R6. Returns o [N, H, v]."""
+    H = cfg["n_heads"]
+    ql, kvl = cfg["q_lora_rank"], cfg["kv_lora_rank"]
+    r, nope, vd = cfg["qk_rope_head_dim"], cfg["qk_nope_head_dim"], cfg["v_head_dim"]
+    eps = cfg["norm_eps"]
+    N = n1.shape[0]
+    cq = rmsnorm(n1 @ W["Wdq"].astype(F64).T, W["gq"], eps)
+    q = (cq @ W["Wuq"].astype(F64).T).reshape(N, H, nope + r)
+    lat = n1 @ W["Wdkv"].astype(F64).T
+    ckv = rmsnorm(lat[:, :kvl], W["gkv"], eps)
+    kpe = apply_rope(lat[:, None, kvl:], pos, cos, sin)           # [N, 1, r]
+    q_pe = apply_rope(q[..., nope:], pos, cos, sin)                 # [N, H, r]
+    k_nope = (ckv @ W["Wuk"].astype(F64).T).reshape(N, H, nope)
+    v = (ckv @ W["Wuv"].astype(F64).T).reshape(N, H, vd)
+    k = np.concatenate([k_nope, np.broadcast_to(kpe, (N, H, r))], axis=-1)
+    qf = np.concatenate([q[..., :nope], q_pe], axis=-1)
+    o = np.empty((N, H, vd), F64)
+    B, S = cfg["batch"], cfg["seq"]
+    for b in range(B):
+        sl = slice(b * S, (b + 1) * S)
+        for i in range(H):
+            o[sl, i] = attention_causal(qf[sl, i], k[sl, i], v[sl, i],
+                                        1.0 / np.sqrt(nope + r))
+    return o
+
+
+def swiglu(x, wg, wu, wd):
+    """One expert FFN: (silu(x Wg^T) * (x Wu^T)) Wd^T, no biases (expert width
+    expert_dim, openclawapi Passo 2; SwiGLU activation as the workload states)."""
+    x = np.asarray(x, F64)
+    g = x @ wg.astype(F64).T
+    u = x @ wu.astype(F64).T
+    hmid = g / (1.0 + np.exp(-g)) * u
+    return hmid @ wd.astype(F64).T
+
+
+def route(n2, Wr, bias_row, k):
+    """Top-k router (techbriefly: an MoE layer picks a subset of experts per token;
+    openclawapi item 5 / Dreamer summary: a bias vector steers selection).
+    Reading R7. Returns idx [n, k] int64 (descending selection score), gates
+    [n, k] float64, gap [n] float32 (k-th minus (k+1)-th selection score; +inf
+    when k equals the expert count), sel [n, E] float32."""
+    logits = np.asarray(n2, F64) @ Wr.astype(F64).T
+    p = softmax(logits, axis=1)
+    sel = (logits + np.asarray(bias_row, F64)[None, :]).astype(np.float32)
+    order = np.argsort(-sel, axis=1, kind="stable")
+    idx = order[:, :k]
+    rows = np.arange(sel.shape[0])[:, None]
+    gates = p[rows, idx]
+    E = sel.shape[1]
+    if k < E:
+        gap = (sel[rows[:, 0], order[:, k - 1]] - sel[rows[:, 0], order[:, k]])
+    else:
+        gap = np.full(sel.shape[0], np.inf, np.float32)
+    return idx, gates, gap.astype(np.float32), sel
+
+
+def moe(n2, idx, gates, W, n_shared):
+    """Sparse MoE output: sum over a token's selected experts of gate * expert(x),
+    plus every always-on shared expert at weight 1 (openclawapi Passo 2,
+    n_shared_experts; reading R7)."""
+    n2 = np.asarray(n2, F64)
+    m = np.zeros_like(n2)
+    E = W["Wg"].shape[0]
+    for e in range(E):
+        rows, slot = np.nonzero(idx == e)
+        if rows.size == 0:
+            continue
+        y = swiglu(n2[rows], W["Wg"][e], W["Wu"][e], W["Wd"][e])
+        m[rows] += gates[rows, slot][:, None] * y
+    for s in range(n_shared):
+        m += swiglu(n2, W["Wsg"][s], W["Wsu"][s], W["Wsd"][s])
+    return m
+
+
+def spectral_radius(A):
+    """rho(A) for the per-channel A (openclawapi Passo 6 returns A with shape
+    (dim,)): a diagonal matrix's eigenvalues are its entries, so rho = max |A_i|."""
+    return float(np.max(np.abs(np.asarray(A, F64))))
+
+
+def kv_cache_bytes_per_token(cfg, elem_bytes=2):
+    """Cached bytes per token per loop step: GQA keeps KV heads of K and V
+    (openclawapi Passo 5: the cache shrinks by n_heads/n_kv_heads); MLA keeps the
+    kv latent plus the shared rope key (Passo 5: about 10-20x smaller)."""
+    if cfg["attn"] == "gqa":
+        return 2 * cfg["n_kv_heads"] * cfg["head_dim"] * elem_bytes
+    return (cfg["kv_lora_rank"] + cfg["qk_rope_head_dim"]) * elem_bytes
+
+
+# ----------------------------------------------------------------------------
+# one loop iteration and the T-loop
+# ----------------------------------------------------------------------------
+def _attn_out(cfg, W, n1, pos, cos, sin):
+    N = n1.shape[0]
+    if cfg["attn"] == "gqa":
+        H, KV, d = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+        q = (n1 @ W["Wq"].astype(F64).T).reshape(N, H, d)
+        k = (n1 @ W["Wk"].astype(F64).T).reshape(N, KV, d)
+        v = (n1 @ W["Wv"].astype(F64).T).reshape(N, KV, d)
+        q = apply_rope(q, pos, cos, sin)
+        k = apply_rope(k, pos, cos, sin)
+        o = gqa_attention(q, k, v, cfg["batch"], cfg["seq"])
+    else:
+        o = mla_attention_explicit(cfg, W, n1, pos, cos, sin)
+    return o.reshape(N, -1)
+
+
+def block_step(cfg, W, h, e, t, active, forced_idx=None, tables=None):
+    """Residual branch of one recurrent-block iteration (reading R1/R2):
+    u = h + e; a = attention-out-projection(RMSNorm(u)) [+ depth-wise LoRA];
+    x = u + a; n2 = RMSNorm(x); m = MoE(n2). Attention runs on every token (keys
+    of halted tokens use their frozen state); the router and experts run on the
+    active rows only. Returns a dict with a, n2, m [N, D] (rows of inactive
+    tokens of m are zero), idx [N, k] (-1 when inactive), gates, gap, counts."""
+    N, D = h.shape
+    S = cfg["seq"]
+    eps = cfg["norm_eps"]
+    pos = np.arange(N) % S
+    if tables is None:
+        d_r = cfg["head_dim"] if cfg["attn"] == "gqa" else cfg["qk_rope_head_dim"]
+        tables = rope_tables(S, d_r, cfg["rope_base"])
+    cos, sin = tables
+    u = np.asarray(h, F64) + np.asarray(e, F64)
+    n1 = rmsnorm(u, W["g1"], eps)
+    o = _attn_out(cfg, W, n1, pos, cos, sin)
+    a = o @ W["Wo"].astype(F64).T
+    if cfg["lora_rank"]:
+        # depth-wise LoRA on the output projection (techbriefly; openclawapi
+        # lora_rank and advanced direction 1); reading R8
+        tl = min(t, cfg["n_lora"] - 1)
+        a = a + (o @ W["lora_down"][tl].astype(F64).T) @ W["lora_up"][tl].astype(F64).T
+    x = u + a
+    n2 = rmsnorm(x, W["g2"], eps)
+
+    k = cfg["top_k"]
+    E = cfg["n_experts"]
+    act_rows = np.nonzero(active)[0]
+    bias_row = W["router_bias"][min(t, cfg["n_bias_rows"] - 1)]
+    idx_a, gates_a, gap_a, _ = route(n2[act_rows], W["Wr"], bias_row, k)
+    if forced_idx is not None:
+        idx_a = np.asarray(forced_idx, np.int64)[act_rows]
+        logits = n2[act_rows] @ W["Wr"].astype(F64).T
+        p = softmax(logits, axis=1)
+        gates_a = p[np.arange(act_rows.size)[:, None], idx_a]
+    m_a = moe(n2[act_rows], idx_a, gates_a, W, cfg["n_shared_experts"])
+    m = np.zeros((N, D), F64)
+    m[act_rows] = m_a
+    idx = np.full((N, k), -1, np.int64)
+    idx[act_rows] = idx_a
+    gates = np.zeros((N, k), F64)
+    gates[act_rows] = gates_a
+    gap = np.full(N, np.nan, np.float32)
+    gap[act_rows] = gap_a
+    counts = np.bincount(idx_a.reshape(-1), minlength=E)[:E].astype(np.int64)
+    return dict(a=a, n2=n2, m=m, idx=idx, gates=gates, gap=gap, counts=counts)
+
+
+def forward(cfg, W, h0=None, e=None, T=None, forced_idx=None, forced_loops=None,
+            record=False):
+    """The T-loop (techbriefly: h_{t+1} = A h_t + B e + Transformer(h_t, e), the
+    same weights reused every iteration, up to 16 iterations; openclawapi
+    Passo 3: the loop count is chosen at call time and may exceed the trained
+    count). A and B are per-channel (openclawapi Passo 6).
+
+    forced_idx: optional [T, N, k] expert indices used instead of the router's
+    own choice (gates are still this oracle's softmax at those indices).
+    forced_loops: optional [N]; token n takes exactly min(T, loops[n]) updates.
+
+    Returns dict(h [N, D] float64, loops [N] int64, and with record=True the
+    per-loop lists idx, gap, counts, cum, n2, h).
+    """
+    e = np.asarray(W["e"] if e is None else e, F64)
+    h = np.array(W["h0"] if h0 is None else h0, F64)
+    T = cfg["T"] if T is None else int(T)
+    if T < 0:
+        raise ValueError("T must be >= 0")
+    if spectral_radius(W["A"]) >= 1.0:
+        raise ValueError("unstable injection: rho(A) >= 1")
+    A = np.asarray(W["A"], F64)[None, :]
+    Bv = np.asarray(W["B"], F64)[None, :]
+    N = h.shape[0]
+    d_r = cfg["head_dim"] if cfg["attn"] == "gqa" else cfg["qk_rope_head_dim"]
+    tables = rope_tables(cfg["seq"], d_r, cfg["rope_base"])
+    active = np.ones(N, dtype=bool)
+    loops = np.zeros(N, np.int64)
+    cum = np.zeros(N, np.float32)
+    thr = np.float32(cfg["act_threshold"])
+    rec = dict(idx=[], gap=[], counts=[], cum=[], n2=[], h=[h.copy()])
+    for t in range(T):
+        if forced_loops is not None:
+            active = np.asarray(forced_loops) > t
+        if not active.any():
+            if record:
+                k = cfg["top_k"]
+                rec["idx"].append(np.full((N, k), -1, np.int64))
+                rec["gap"].append(np.full(N, np.nan, np.float32))
+                rec["counts"].append(np.zeros(cfg["n_experts"], np.int64))
+                rec["cum"].append(cum.copy())
+                rec["n2"].append(np.zeros_like(h))
+                rec["h"].append(h.copy())
+            continue
+        fi = None if forced_idx is None else forced_idx[t]
+        st = block_step(cfg, W, h, e, t, active, fi, tables)
+        rows = np.nonzero(active)[0]
+        # LTI injection plus the block's residual branch (techbriefly loop update)
+        h[rows] = A * h[rows] + Bv * e[rows] + st["a"][rows] + st["m"][rows]
+        loops[rows] += 1
+        if cfg["act"]:
+            # ACT halting (techbriefly; openclawapi item 4, threshold 0.99); R9
+            z = h[rows] @ np.asarray(W["w_halt"], F64)
+            p = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+            cum[rows] = (cum[rows] + p).astype(np.float32)
+            if forced_loops is None:
+                active = active.copy()
+                active[rows[cum[rows] >= thr]] = False
+        if record:
+            rec["idx"].append(st["idx"])
+            rec["gap"].append(st["gap"])
+            rec["counts"].append(st["counts"])
+            rec["cum"].append(cum.copy())
+            rec["n2"].append(st["n2"])
+            rec["h"].append(h.copy())
+    out = dict(h=h, loops=loops, cum=cum)
+    if record:
+        out.update(rec)
+    return out
