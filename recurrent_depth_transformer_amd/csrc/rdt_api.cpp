@@ -1,0 +1,535 @@
+// librdt C-ABI: argument checks, the rho(A) guard, the per-loop launch plan and
+// the cache of captured HIP graphs.
+//
+// One forward enqueues, per loop t (techbriefly: h_{t+1} = A h_t + B e +
+// Transformer(h_t, e)):
+//   RMSNorm(h + e) -> Q/K/V (GQA, RoPE in the epilogue) or the MLA latent
+//   chain -> causal flash attention -> output projection (+ depth-wise LoRA as
+//   a second K phase) -> RMSNorm -> router GEMM with softmax/top-k epilogue ->
+//   stable expert permutation -> grouped SwiGLU gate/up -> grouped down ->
+//   combine + injection (+ ACT) -> (ACT) active-list compaction.
+// Data-dependent sizes (active tokens, rows per expert) stay on the device;
+// grids are sized for the worst case and idle workgroups exit at once, so the
+// whole T-loop is a static graph.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/rdt.h"
+#include "rdt_launch.h"
+#include "rdt_plan.h"
+
+using namespace rdt;
+
+static thread_local std::string g_err;
+
+static rdt_status set_err(rdt_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+#define HIPCHK(x)                                                                                \
+  do {                                                                                           \
+    hipError_t e_ = (x);                                                                         \
+    if (e_ != hipSuccess) return set_err(RDT_E_HIP, std::string(#x) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+struct GraphKey {
+  const void* ptrs[48];
+  int T;
+  bool operator==(const GraphKey& o) const { return T == o.T && memcmp(ptrs, o.ptrs, sizeof(ptrs)) == 0; }
+};
+
+struct GraphEntry {
+  GraphKey key;
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+struct rdt_handle {
+  rdt_config cfg;
+  int device;
+  hipStream_t cap;
+  int graph_mode;
+  std::vector<const float*> checked_A;
+  std::vector<GraphEntry> graphs;
+};
+
+extern "C" const char* rdt_last_error(void) { return g_err.c_str(); }
+extern "C" const char* rdt_version(void) { return "librdt 0.1 gfx950"; }
+
+extern "C" rdt_status rdt_config_default(rdt_config* c) {
+  if (!c) return set_err(RDT_E_INVALID, "null config");
+  memset(c, 0, sizeof(*c));
+  c->attn_type = RDT_ATTN_GQA;
+  c->rope_base = 10000.f;
+  c->norm_eps = 1e-6f;
+  c->n_bias_rows = 1;
+  c->act_threshold = 0.99f;
+  c->dtype = RDT_BF16;
+  c->max_T = 16;
+  return RDT_OK;
+}
+
+extern "C" rdt_status rdt_config_validate(const rdt_config* c) {
+  if (!c) return set_err(RDT_E_INVALID, "null config");
+  std::string why;
+  rdt_status st = validate_config(*c, &why);
+  if (st != RDT_OK) return set_err(st, why);
+  return RDT_OK;
+}
+
+extern "C" rdt_status rdt_spectral_radius(const float* A, int32_t dim, float* rho) {
+  if (!A || !rho || dim <= 0) return set_err(RDT_E_INVALID, "rdt_spectral_radius: bad arguments");
+  float m = 0.f;
+  for (int i = 0; i < dim; ++i) {
+    const float v = fabsf(A[i]);
+    if (!(v <= m)) m = v;  // NaN propagates
+  }
+  *rho = m;
+  return RDT_OK;
+}
+
+extern "C" rdt_status rdt_create(const rdt_config* c, rdt_handle** out) {
+  if (!out) return set_err(RDT_E_INVALID, "null output handle");
+  *out = nullptr;
+  rdt_status st = rdt_config_validate(c);
+  if (st != RDT_OK) return st;
+  rdt_handle* h = new (std::nothrow) rdt_handle();
+  if (!h) return set_err(RDT_E_INVALID, "out of host memory");
+  h->cfg = *c;
+  h->graph_mode = 1;
+  if (hipGetDevice(&h->device) != hipSuccess ||
+      hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking) != hipSuccess) {
+    delete h;
+    return set_err(RDT_E_HIP, "rdt_create: cannot create the capture stream");
+  }
+  *out = h;
+  return RDT_OK;
+}
+
+extern "C" void rdt_destroy(rdt_handle* h) {
+  if (!h) return;
+  for (auto& g : h->graphs) {
+    (void)hipGraphExecDestroy(g.exec);
+    (void)hipGraphDestroy(g.graph);
+  }
+  (void)hipStreamDestroy(h->cap);
+  delete h;
+}
+
+extern "C" size_t rdt_workspace_size(const rdt_handle* h, int32_t T) {
+  if (!h || T < 0 || T > h->cfg.max_T) return 0;
+  return make_plan(h->cfg, T).total;
+}
+
+extern "C" rdt_status rdt_set_graph_mode(rdt_handle* h, int32_t enabled) {
+  if (!h) return set_err(RDT_E_INVALID, "null handle");
+  h->graph_mode = enabled != 0;
+  return RDT_OK;
+}
+
+// ------------------------------------------------------------------ enqueue
+struct Fwd {
+  const rdt_config* c;
+  Plan P;
+  const float* h0;
+  const float* e;
+  const rdt_weights* w;
+  int T;
+  float* out;
+  rdt_aux aux;
+  char* ws;
+};
+
+template <typename P>
+static P* at(char* ws, size_t off) { return reinterpret_cast<P*>(ws + off); }
+
+static const char* elt_ptr(const void* base, long long elems, int elt) {
+  return reinterpret_cast<const char*>(base) + elems * elt;
+}
+
+static void pick_tile(long long M, long long N, int min_bn, int* bm, int* bn) {
+  auto tiles = [&](int m, int n) { return ((M + m - 1) / m) * ((N + n - 1) / n); };
+  *bm = 128;
+  *bn = 128;
+  if (tiles(128, 128) >= 256) return;
+  if (tiles(64, 128) >= 256 || min_bn > 64) { *bm = 64; return; }
+  *bm = 64;
+  *bn = 64;
+}
+
+static rdt_status enqueue(const Fwd& f, hipStream_t s) {
+  const rdt_config& c = *f.c;
+  const Plan& P = f.P;
+  char* ws = f.ws;
+  const int N = P.N, D = P.D, dt = c.dtype == RDT_F32 ? DT_F32 : DT_BF16, elt = P.elt;
+  const rdt_weights& w = *f.w;
+  const bool act = c.act_enabled != 0;
+
+  if (f.out != f.h0) HIPCHK(hipMemcpyAsync(f.out, f.h0, (size_t)N * D * 4, hipMemcpyDeviceToDevice, s));
+  if (f.aux.h_dump) HIPCHK(launch_copy_f32(f.aux.h_dump, f.h0, (long long)N * D, s));
+  if (f.T == 0) {
+    if (f.aux.loops) HIPCHK(launch_fill_i32(f.aux.loops, 0, N, s));
+    return RDT_OK;
+  }
+  float* cosb = at<float>(ws, P.cosb);
+  float* sinb = at<float>(ws, P.sinb);
+  HIPCHK(launch_rope_tables(cosb, sinb, P.S, P.dr, c.rope_base, s));
+  if (P.mla) HIPCHK(launch_head_transpose(dt, at<char>(ws, P.wukT), w.Wuk, P.H, P.nope, P.kvl, s));
+
+  int* lists = at<int>(ws, P.lists);
+  int* ncount = at<int>(ws, P.ncount);
+  int* segs = at<int>(ws, P.seg);
+  float* cum = at<float>(ws, P.cum);
+  if (act) {
+    HIPCHK(launch_iota(lists, N, ncount, N, segs, P.B, P.S, s));
+    HIPCHK(launch_fill_f32(cum, 0.f, N, s));
+  }
+  const int k = P.k, E = P.E;
+  if (f.aux.loops) HIPCHK(launch_fill_i32(f.aux.loops, 0, N, s));
+  if (f.aux.route_idx) HIPCHK(launch_fill_i32(f.aux.route_idx, -1, (long long)f.T * N * k, s));
+  if (f.aux.route_gap) HIPCHK(launch_fill_f32(f.aux.route_gap, NAN, (long long)f.T * N, s));
+  if (f.aux.act_cum) HIPCHK(launch_fill_f32(f.aux.act_cum, NAN, (long long)f.T * N, s));
+  if (act && f.aux.n2_dump) {
+    if (dt == DT_F32) HIPCHK(launch_fill_f32((float*)f.aux.n2_dump, 0.f, (long long)f.T * N * D, s));
+    else HIPCHK(launch_fill_u16((uint16_t*)f.aux.n2_dump, 0, (long long)f.T * N * D, s));
+  }
+  if (act && f.aux.a_dump) HIPCHK(launch_fill_f32(f.aux.a_dump, 0.f, (long long)f.T * N * D, s));
+
+  char* n1 = at<char>(ws, P.n1);
+  char* o = at<char>(ws, P.o);
+  char* z = at<char>(ws, P.z);
+  float* abuf = at<float>(ws, P.a);
+  char* n2 = at<char>(ws, P.n2);
+  int* idx = at<int>(ws, P.idx);
+  float* gates = at<float>(ws, P.gates);
+  float* gap = at<float>(ws, P.gap);
+  int* counts = at<int>(ws, P.counts);
+  int* offs = at<int>(ws, P.offs);
+  int* ts_gu = at<int>(ws, P.ts_gu);
+  int* ts_dn = at<int>(ws, P.ts_dn);
+  int* perm = at<int>(ws, P.perm);
+  int* inv = at<int>(ws, P.inv);
+  char* hmid = at<char>(ws, P.hmid);
+  char* ybuf = at<char>(ws, P.y);
+
+  for (int t = 0; t < f.T; ++t) {
+    const int* cur = act ? lists + (size_t)t * N : nullptr;
+    const int* ncur = act ? ncount + t : nullptr;
+    const int tp = t > 0 ? t - 1 : 0;
+    const int* prev = act ? lists + (size_t)tp * N : nullptr;
+    const int* nprev = act ? ncount + tp : nullptr;
+    const int* seg = act ? segs + (size_t)t * (P.B + 1) : nullptr;
+
+    // a1: u = h + e, n1 = RMSNorm(u) * g1 (tokens whose state changed last loop)
+    NormArgs n1a{};
+    n1a.dtype = dt; n1a.h = f.out; n1a.e = f.e; n1a.a = nullptr; n1a.g = w.g1; n1a.eps = c.norm_eps; n1a.D = D;
+    n1a.rows = prev; n1a.ndev = nprev; n1a.n = N; n1a.out = n1; n1a.out_scatter = 1; n1a.dump = nullptr;
+    HIPCHK(launch_norm(n1a, s));
+
+    // a2-a4: attention
+    if (!P.mla) {
+      const int Hd = P.H * P.d, KVd = P.KV * P.d;
+      char* q = at<char>(ws, P.q);
+      char* kb = at<char>(ws, P.k_);
+      char* vb = at<char>(ws, P.v_);
+      GemmSeg sq{w.Wq, Hd, q, Hd, act ? 0 : 1, 1, 0};
+      GemmSeg sk{w.Wk, KVd, kb, KVd, 1, 1, 0};
+      GemmSeg sv{w.Wv, KVd, vb, KVd, 1, 0, 0};
+      DenseGemm g{};
+      g.dtype = dt; g.A = n1; g.lda = D; g.K = D; g.batch = 1;
+      g.cosb = cosb; g.sinb = sinb; g.rope_dim = P.d; g.seq = P.S; g.epi = EPI_STORE;
+      g.M = N;
+      if (!act) {
+        g.rows = nullptr; g.gather = 0; g.Mdev = nullptr;
+        g.nseg = 3; g.seg[0] = sq; g.seg[1] = sk; g.seg[2] = sv;
+        pick_tile(N, Hd + 2 * KVd, P.d, &g.bm, &g.bn);
+        HIPCHK(launch_dense_gemm(g, s));
+      } else {
+        DenseGemm gq = g;
+        gq.rows = cur; gq.gather = 1; gq.Mdev = ncur; gq.nseg = 1; gq.seg[0] = sq;
+        pick_tile(N, Hd, P.d, &gq.bm, &gq.bn);
+        HIPCHK(launch_dense_gemm(gq, s));
+        DenseGemm gkv = g;
+        gkv.rows = prev; gkv.gather = 1; gkv.Mdev = nprev; gkv.nseg = 2; gkv.seg[0] = sk; gkv.seg[1] = sv;
+        pick_tile(N, 2 * KVd, P.d, &gkv.bm, &gkv.bn);
+        HIPCHK(launch_dense_gemm(gkv, s));
+      }
+      AttnArgs aa{};
+      aa.dtype = dt; aa.dqk = P.d; aa.dv = P.d;
+      aa.q = q; aa.q_ld = Hd; aa.q_hs = P.d;
+      aa.k = kb; aa.k_ld = KVd; aa.k_hs = P.d;
+      aa.v = vb; aa.v_ld = KVd; aa.v_hs = P.d;
+      aa.o = o; aa.o_ld = Hd; aa.o_hs = P.d;
+      aa.H = P.H; aa.KV = P.KV; aa.rows = cur; aa.seg = seg; aa.B = P.B; aa.S = P.S;
+      aa.scale = 1.f / sqrtf((float)P.d);
+      HIPCHK(launch_attention(aa, s));
+    } else {
+      const int W = P.kvl + P.nr, qw = P.nope + P.nr;
+      char* cq_raw = at<char>(ws, P.cq_raw);
+      char* lat_raw = at<char>(ws, P.lat_raw);
+      char* cqn = at<char>(ws, P.cqn);
+      char* latent = at<char>(ws, P.latent);
+      char* qfull = at<char>(ws, P.qfull);
+      char* qattn = at<char>(ws, P.qattn);
+      char* olat = at<char>(ws, P.olat);
+      char* wukT = at<char>(ws, P.wukT);
+      // down projections of the query and kv latents (fp32 for the norms)
+      DenseGemm g1{};
+      g1.dtype = dt; g1.A = n1; g1.lda = D; g1.K = D; g1.batch = 1; g1.epi = EPI_STORE;
+      g1.rows = prev; g1.gather = act ? 1 : 0; g1.M = N; g1.Mdev = nprev;
+      g1.nseg = 2;
+      g1.seg[0] = GemmSeg{w.Wdq, P.ql, cq_raw, P.ql, 1, 0, 1};
+      g1.seg[1] = GemmSeg{w.Wdkv, W, lat_raw, W, 1, 0, 1};
+      pick_tile(N, P.ql + W, 16, &g1.bm, &g1.bn);
+      HIPCHK(launch_dense_gemm(g1, s));
+      MlaNormArgs mn{};
+      mn.dtype = dt; mn.cq_raw = (const float*)cq_raw; mn.ql = P.ql; mn.lat_raw = (const float*)lat_raw;
+      mn.kvl = P.kvl; mn.nr = P.nr; mn.gq = w.gq; mn.gkv = w.gkv; mn.eps = c.norm_eps;
+      mn.rows = prev; mn.ndev = nprev; mn.n = N; mn.cqn = cqn; mn.latent = latent;
+      mn.cosb = cosb; mn.sinb = sinb; mn.S = P.S;
+      HIPCHK(launch_mla_norm(mn, s));
+      // query up-projection (compacted rows)
+      DenseGemm g2{};
+      g2.dtype = dt; g2.A = cqn; g2.lda = P.ql; g2.K = P.ql; g2.batch = 1; g2.epi = EPI_STORE;
+      g2.rows = cur; g2.gather = act ? 1 : 0; g2.M = N; g2.Mdev = ncur;
+      g2.nseg = 1; g2.seg[0] = GemmSeg{w.Wuq, P.H * qw, qfull, P.H * qw, 0, 0, 0};
+      pick_tile(N, P.H * qw, 16, &g2.bm, &g2.bn);
+      HIPCHK(launch_dense_gemm(g2, s));
+      // absorb: q_lat[h] = q_nope[h] . Wuk[h]  (per head, B = Wuk[h]^T)
+      DenseGemm g3{};
+      g3.dtype = dt; g3.A = qfull; g3.lda = P.H * qw; g3.a_bstride = qw; g3.K = P.nope; g3.epi = EPI_STORE;
+      g3.rows = cur; g3.gather = 0; g3.M = N; g3.Mdev = ncur; g3.batch = P.H;
+      g3.nseg = 1; g3.seg[0] = GemmSeg{wukT, P.kvl, qattn, P.H * W, 0, 0, 0};
+      g3.b_bstride = (long long)P.kvl * P.nope; g3.c_bstride = W;
+      pick_tile(N, (long long)P.kvl * P.H, 16, &g3.bm, &g3.bn);
+      HIPCHK(launch_dense_gemm(g3, s));
+      QRopeArgs qr{};
+      qr.dtype = dt; qr.src = qfull; qr.src_ld = P.H * qw; qr.src_hs = qw; qr.src_off = P.nope;
+      qr.dst = qattn; qr.dst_ld = P.H * W; qr.dst_hs = W; qr.dst_off = P.kvl;
+      qr.H = P.H; qr.nr = P.nr; qr.rows = cur; qr.ndev = ncur; qr.n = N;
+      qr.cosb = cosb; qr.sinb = sinb; qr.S = P.S;
+      HIPCHK(launch_qrope(qr, s));
+      AttnArgs aa{};
+      aa.dtype = dt; aa.dqk = W; aa.dv = P.kvl;
+      aa.q = qattn; aa.q_ld = P.H * W; aa.q_hs = W;
+      aa.k = latent; aa.k_ld = W; aa.k_hs = 0;
+      aa.v = latent; aa.v_ld = W; aa.v_hs = 0;
+      aa.o = olat; aa.o_ld = P.H * P.kvl; aa.o_hs = P.kvl;
+      aa.H = P.H; aa.KV = 1; aa.rows = cur; aa.seg = seg; aa.B = P.B; aa.S = P.S;
+      aa.scale = 1.f / sqrtf((float)(P.nope + P.nr));
+      HIPCHK(launch_attention(aa, s));
+      // value up-projection per head: o[h] = o_lat[h] . Wuv[h]^T
+      DenseGemm g4{};
+      g4.dtype = dt; g4.A = olat; g4.lda = P.H * P.kvl; g4.a_bstride = P.kvl; g4.K = P.kvl; g4.epi = EPI_STORE;
+      g4.rows = cur; g4.gather = 0; g4.M = N; g4.Mdev = ncur; g4.batch = P.H;
+      g4.nseg = 1; g4.seg[0] = GemmSeg{w.Wuv, P.vd, o, P.hv, 0, 0, 0};
+      g4.b_bstride = (long long)P.vd * P.kvl; g4.c_bstride = P.vd;
+      pick_tile(N, (long long)P.vd * P.H, 16, &g4.bm, &g4.bn);
+      HIPCHK(launch_dense_gemm(g4, s));
+    }
+
+    // a5: output projection (+ depth-wise LoRA as a second K phase)
+    const int tl = P.r > 0 ? (t < P.L - 1 ? t : P.L - 1) : 0;
+    if (P.r > 0) {
+      DenseGemm gz{};
+      gz.dtype = dt; gz.A = o; gz.lda = P.hv; gz.K = P.hv; gz.batch = 1; gz.epi = EPI_STORE;
+      gz.rows = cur; gz.gather = 0; gz.M = N; gz.Mdev = ncur;
+      gz.nseg = 1;
+      gz.seg[0] = GemmSeg{elt_ptr(w.lora_down, (long long)tl * P.r * P.hv, elt), P.r, z, P.r, 0, 0, 0};
+      gz.bm = 128; gz.bn = 64;
+      if ((N + 127) / 128 < 256) gz.bm = 64;
+      HIPCHK(launch_dense_gemm(gz, s));
+    }
+    DenseGemm go{};
+    go.dtype = dt; go.A = o; go.lda = P.hv; go.K = P.hv; go.batch = 1; go.epi = EPI_STORE;
+    go.rows = cur; go.gather = 0; go.M = N; go.Mdev = ncur;
+    go.nseg = 1; go.seg[0] = GemmSeg{w.Wo, D, abuf, D, 0, 0, 1};
+    if (P.r > 0) {
+      go.A2 = z; go.lda2 = P.r; go.B2 = elt_ptr(w.lora_up, (long long)tl * D * P.r, elt); go.K2 = P.r;
+    }
+    pick_tile(N, D, 16, &go.bm, &go.bn);
+    HIPCHK(launch_dense_gemm(go, s));
+
+    // a5: x = u + a, n2 = RMSNorm(x) * g2 (compacted rows)
+    NormArgs n2a{};
+    n2a.dtype = dt; n2a.h = f.out; n2a.e = f.e; n2a.a = abuf; n2a.g = w.g2; n2a.eps = c.norm_eps; n2a.D = D;
+    n2a.rows = cur; n2a.ndev = ncur; n2a.n = N; n2a.out = n2; n2a.out_scatter = 0;
+    n2a.dump = f.aux.n2_dump ? (void*)elt_ptr(f.aux.n2_dump, (long long)t * N * D, elt) : nullptr;
+    HIPCHK(launch_norm(n2a, s));
+
+    // a6: router GEMM with softmax / top-k epilogue, then the stable permutation
+    DenseGemm gr{};
+    gr.dtype = dt; gr.A = n2; gr.lda = D; gr.K = D; gr.batch = 1; gr.epi = EPI_ROUTER;
+    gr.rows = cur; gr.gather = 0; gr.M = N; gr.Mdev = ncur;
+    gr.nseg = 1; gr.seg[0] = GemmSeg{w.Wr, E, nullptr, 0, 0, 0, 0};
+    gr.bm = ROUTER_BM; gr.bn = 64;
+    gr.router.bias = w.router_bias && c.n_bias_rows > 0
+                         ? w.router_bias + (size_t)(t < c.n_bias_rows - 1 ? t : c.n_bias_rows - 1) * E
+                         : nullptr;
+    gr.router.E = E; gr.router.k = k; gr.router.idx = idx; gr.router.gates = gates; gr.router.gap = gap;
+    gr.router.dump_idx = f.aux.route_idx ? f.aux.route_idx + (size_t)t * N * k : nullptr;
+    gr.router.dump_gap = f.aux.route_gap ? f.aux.route_gap + (size_t)t * N : nullptr;
+    HIPCHK(launch_dense_gemm(gr, s));
+
+    PermuteArgs pa{};
+    pa.idx = idx; pa.ndev = ncur; pa.n_static = N; pa.E = E; pa.Se = P.Se; pa.k = k;
+    pa.counts = counts; pa.offs = offs; pa.perm = perm; pa.inv = inv;
+    pa.ts_gu = ts_gu; pa.bm_gu = GU_BM; pa.ts_dn = ts_dn; pa.bm_dn = DN_BM;
+    pa.counts_dump = f.aux.expert_counts ? f.aux.expert_counts + (size_t)t * E : nullptr;
+    HIPCHK(launch_permute(pa, s));
+
+    // a7: grouped SwiGLU experts
+    GroupedGemm gu{};
+    gu.dtype = dt; gu.kind = 0; gu.A = n2; gu.lda = D;
+    gu.perm = perm; gu.offs = offs; gu.counts = counts; gu.tile_start = ts_gu; gu.ndev = ncur; gu.n_static = N;
+    gu.E = E; gu.Se = P.Se; gu.k = k; gu.W1 = w.Wg; gu.W2 = w.Wu; gu.S1 = w.Wsg; gu.S2 = w.Wsu;
+    gu.N = P.F; gu.K = D; gu.C = hmid; gu.ldc = P.F; gu.max_mtiles = P.gu_max_mtiles;
+    HIPCHK(launch_grouped_gemm(gu, s));
+    GroupedGemm gd{};
+    gd.dtype = dt; gd.kind = 1; gd.A = hmid; gd.lda = P.F;
+    gd.perm = perm; gd.offs = offs; gd.counts = counts; gd.tile_start = ts_dn; gd.ndev = ncur; gd.n_static = N;
+    gd.E = E; gd.Se = P.Se; gd.k = k; gd.W1 = w.Wd; gd.W2 = nullptr; gd.S1 = w.Wsd; gd.S2 = nullptr;
+    gd.N = D; gd.K = P.F; gd.C = ybuf; gd.ldc = D; gd.max_mtiles = P.dn_max_mtiles;
+    HIPCHK(launch_grouped_gemm(gd, s));
+
+    // a8: combine + LTI injection (+ ACT)
+    CombineArgs ca{};
+    ca.dtype = dt; ca.h = f.out; ca.e = f.e; ca.a = abuf; ca.A = w.A; ca.B = w.B;
+    ca.Y = ybuf; ca.gates = gates; ca.inv = inv; ca.k = k; ca.Se = P.Se; ca.D = D;
+    ca.rows = cur; ca.ndev = ncur; ca.n = N;
+    ca.act = act; ca.w_halt = w.w_halt; ca.thr = c.act_threshold; ca.cum = cum; ca.loops = f.aux.loops; ca.t = t;
+    ca.cum_dump = f.aux.act_cum ? f.aux.act_cum + (size_t)t * N : nullptr;
+    ca.a_dump = f.aux.a_dump ? f.aux.a_dump + (size_t)t * N * D : nullptr;
+    HIPCHK(launch_combine(ca, s));
+    if (act) {
+      CompactArgs cp{};
+      cp.rows_in = cur; cp.n_in = ncur; cp.cum = cum; cp.thr = c.act_threshold;
+      cp.rows_out = lists + (size_t)(t + 1) * N; cp.n_out = ncount + t + 1;
+      cp.seg_out = segs + (size_t)(t + 1) * (P.B + 1); cp.B = P.B; cp.S = P.S;
+      HIPCHK(launch_compact(cp, s));
+    }
+    if (f.aux.h_dump) HIPCHK(launch_copy_f32(f.aux.h_dump + (size_t)(t + 1) * N * D, f.out, (long long)N * D, s));
+  }
+  return RDT_OK;
+}
+
+static bool misaligned(const void* p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+static rdt_status check_weights(const rdt_config& c, const rdt_weights* w) {
+  if (!w) return set_err(RDT_E_INVALID, "null weights");
+  const void* need[32];
+  const char* names[32];
+  int n = 0;
+  auto req = [&](const void* p, const char* nm) { need[n] = p; names[n] = nm; ++n; };
+  req(w->g1, "g1"); req(w->g2, "g2"); req(w->Wo, "Wo"); req(w->Wr, "Wr");
+  req(w->Wg, "Wg"); req(w->Wu, "Wu"); req(w->Wd, "Wd"); req(w->A, "A"); req(w->B, "B");
+  if (c.attn_type == RDT_ATTN_GQA) {
+    req(w->Wq, "Wq"); req(w->Wk, "Wk"); req(w->Wv, "Wv");
+  } else {
+    req(w->Wdq, "Wdq"); req(w->gq, "gq"); req(w->Wuq, "Wuq"); req(w->Wdkv, "Wdkv");
+    req(w->gkv, "gkv"); req(w->Wuk, "Wuk"); req(w->Wuv, "Wuv");
+  }
+  if (c.n_shared_experts > 0) { req(w->Wsg, "Wsg"); req(w->Wsu, "Wsu"); req(w->Wsd, "Wsd"); }
+  if (c.lora_rank > 0) { req(w->lora_down, "lora_down"); req(w->lora_up, "lora_up"); }
+  if (c.act_enabled) req(w->w_halt, "w_halt");
+  for (int i = 0; i < n; ++i) {
+    if (!need[i]) return set_err(RDT_E_INVALID, std::string("null weight pointer: ") + names[i]);
+    if (misaligned(need[i], 16)) return set_err(RDT_E_INVALID, std::string("weight not 16-byte aligned: ") + names[i]);
+  }
+  if (misaligned(w->router_bias, 4)) return set_err(RDT_E_INVALID, "router_bias misaligned");
+  return RDT_OK;
+}
+
+static rdt_status check_rho(rdt_handle* h, const float* A, hipStream_t s) {
+  for (const float* p : h->checked_A)
+    if (p == A) return RDT_OK;
+  std::vector<float> host((size_t)h->cfg.dim);
+  HIPCHK(hipMemcpyAsync(host.data(), A, host.size() * 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  float rho = 0.f;
+  rdt_spectral_radius(host.data(), h->cfg.dim, &rho);
+  if (!(rho < 1.f)) {
+    char buf[96];
+    snprintf(buf, sizeof buf, "unstable injection: rho(A) = %.6g >= 1", (double)rho);
+    return set_err(RDT_E_UNSTABLE, buf);
+  }
+  h->checked_A.push_back(A);
+  return RDT_OK;
+}
+
+extern "C" rdt_status rdt_recurrent_forward(rdt_handle* h, const float* h0, const float* e, const rdt_weights* w,
+                                            int32_t T, float* out, const rdt_aux* aux, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  if (!h) return set_err(RDT_E_INVALID, "null handle");
+  const rdt_config& c = h->cfg;
+  if (T < 0 || T > c.max_T) return set_err(RDT_E_INVALID, "T must be in [0, max_T]");
+  if (!h0 || !e || !out) return set_err(RDT_E_INVALID, "null h0, e or out");
+  if (misaligned(h0, 16) || misaligned(e, 16) || misaligned(out, 16))
+    return set_err(RDT_E_INVALID, "h0, e and out must be 16-byte aligned");
+  const size_t bytes = (size_t)c.batch * c.seq * c.dim * 4;
+  auto overlap = [&](const void* a, const void* b) {
+    const char* x = (const char*)a;
+    const char* y = (const char*)b;
+    return x < y + bytes && y < x + bytes;
+  };
+  if (out != h0 && overlap(out, h0)) return set_err(RDT_E_INVALID, "out partially overlaps h0");
+  if (overlap(out, e)) return set_err(RDT_E_INVALID, "out overlaps e");
+  rdt_status st = check_weights(c, w);
+  if (st != RDT_OK) return st;
+  Fwd f{};
+  f.c = &c;
+  f.P = make_plan(c, T);
+  if (!ws || ws_bytes < f.P.total) return set_err(RDT_E_WORKSPACE, "workspace missing or too small");
+  if (misaligned(ws, 256)) return set_err(RDT_E_INVALID, "workspace must be 256-byte aligned");
+  f.h0 = h0; f.e = e; f.w = w; f.T = T; f.out = out; f.ws = (char*)ws;
+  if (aux) f.aux = *aux;
+  hipStream_t s = (hipStream_t)stream;
+  st = check_rho(h, w->A, s);
+  if (st != RDT_OK) return st;
+  if (!h->graph_mode || T == 0) return enqueue(f, s);
+
+  GraphKey key{};
+  int nk = 0;
+  const void* wp = w;
+  (void)wp;
+  const void* const* wv = reinterpret_cast<const void* const*>(w);
+  for (size_t i = 0; i < sizeof(rdt_weights) / sizeof(void*); ++i) key.ptrs[nk++] = wv[i];
+  const void* const* av = reinterpret_cast<const void* const*>(&f.aux);
+  for (size_t i = 0; i < sizeof(rdt_aux) / sizeof(void*); ++i) key.ptrs[nk++] = av[i];
+  key.ptrs[nk++] = h0; key.ptrs[nk++] = e; key.ptrs[nk++] = out; key.ptrs[nk++] = ws;
+  key.T = T;
+  for (auto& g : h->graphs)
+    if (g.key == key) {
+      HIPCHK(hipGraphLaunch(g.exec, s));
+      return RDT_OK;
+    }
+  HIPCHK(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
+  st = enqueue(f, h->cap);
+  hipGraph_t graph = nullptr;
+  hipError_t ce = hipStreamEndCapture(h->cap, &graph);
+  if (st != RDT_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st;
+  }
+  if (ce != hipSuccess) return set_err(RDT_E_HIP, std::string("graph capture failed: ") + hipGetErrorString(ce));
+  hipGraphExec_t exec = nullptr;
+  ce = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (ce != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return set_err(RDT_E_HIP, std::string("graph instantiate failed: ") + hipGetErrorString(ce));
+  }
+  if (h->graphs.size() >= 16) {
+    (void)hipGraphExecDestroy(h->graphs.front().exec);
+    (void)hipGraphDestroy(h->graphs.front().graph);
+    h->graphs.erase(h->graphs.begin());
+  }
+  h->graphs.push_back(GraphEntry{key, graph, exec});
+  HIPCHK(hipGraphLaunch(exec, s));
+  return RDT_OK;
+}

@@ -1,0 +1,169 @@
+// Internal launch interface between the host orchestration (rdt_api.cpp) and
+// the HIP kernels (rdt_kernels.hip). Plain structs of device pointers and sizes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rdt {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+// Tile shapes the host must know to plan grids and the expert tile schedule.
+constexpr int GU_BM = 128;   // grouped gate/up GEMM rows per tile
+constexpr int GU_BN = 128;   // columns of [gate | up] per tile (64 outputs)
+constexpr int DN_BM = 64;    // grouped down GEMM rows per tile
+constexpr int DN_BN = 128;
+constexpr int ROUTER_BM = 64;
+constexpr int MAX_EXPERTS = 64;
+
+// ---------------------------------------------------------------- dense GEMM
+// C[i, :] = A[row(i), :K] . B^T (+ A2[i, :K2] . B2^T), fp32 accumulation.
+// B is split by output column into up to three segments, each with its own
+// weight matrix and destination.
+struct GemmSeg {
+  const void* B;   // [ncols, K] row-major (row stride K)
+  int ncols;
+  void* C;         // destination base
+  int ldc;         // destination row stride in elements
+  int scatter;     // 1: destination row = token id of row i; 0: row i
+  int rope;        // apply half-split RoPE per head of width rope_dim
+  int out_f32;     // write float instead of the storage type
+};
+
+enum { EPI_STORE = 0, EPI_ROUTER = 1 };
+
+struct RouterEpi {
+  const float* bias;     // [E] selection bias row, may be null
+  int E, k;
+  int* idx;              // [n, k] compacted
+  float* gates;          // [n, k]
+  float* gap;            // [n]
+  int* dump_idx;         // [N, k] by token, may be null
+  float* dump_gap;       // [N] by token, may be null
+};
+
+struct DenseGemm {
+  int dtype;
+  const void* A; int lda; long long a_bstride;
+  const int* rows;       // token id of compacted row i (null: identity)
+  int gather;            // A row = rows[i] (1) or i (0)
+  int M; const int* Mdev;
+  int K;
+  int nseg; GemmSeg seg[3];
+  long long b_bstride, c_bstride;
+  int batch;
+  const void* A2; int lda2; const void* B2; int K2;   // optional second K phase
+  const float* cosb; const float* sinb; int rope_dim; int seq;
+  int epi;
+  RouterEpi router;
+  int bm, bn;            // tile shape (64 or 128 each)
+};
+hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s);
+
+// --------------------------------------------------------------- grouped GEMM
+// Experts 0..E-1 (routed, rows gathered through perm) and E..E+Se-1 (shared,
+// every active row). Output rows are in permuted order: routed rows of expert
+// g start at offs[g]; shared expert s starts at n*k + s*n.
+struct GroupedGemm {
+  int dtype;
+  int kind;              // 0: gate/up + SwiGLU, 1: down projection
+  const void* A; int lda;
+  const int* perm; const int* offs; const int* counts; const int* tile_start;
+  const int* ndev; int n_static;
+  int E, Se, k;
+  const void* W1; const void* W2;  // routed weights (gate/up: Wg, Wu; down: Wd)
+  const void* S1; const void* S2;  // shared weights (gate/up: Wsg, Wsu; down: Wsd)
+  int N, K;
+  void* C; int ldc;
+  int max_mtiles;
+};
+hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+struct AttnArgs {
+  int dtype;
+  int dqk, dv;           // per-head q/k width and v width
+  const void* q; int q_ld, q_hs;
+  const void* k; int k_ld, k_hs;
+  const void* v; int v_ld, v_hs;
+  void* o; int o_ld, o_hs;
+  int H, KV;
+  const int* rows;       // token id of compacted query row (null: identity)
+  const int* seg;        // [B+1] start of each sequence in the query list (null: b*S)
+  int B, S;
+  float scale;           // softmax scale (multiplies q.k)
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- row kernels
+struct NormArgs {
+  int dtype;
+  const float* h; const float* e; const float* a;  // a optional: x = h + e + a[i]
+  const float* g; float eps; int D;
+  const int* rows; const int* ndev; int n;
+  void* out; int out_scatter;
+  void* dump;            // optional copy of the output scattered by token
+};
+hipError_t launch_norm(const NormArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  int dtype;
+  float* h; const float* e; const float* a; const float* A; const float* B;
+  const void* Y; const float* gates; const int* inv;
+  int k, Se, D;
+  const int* rows; const int* ndev; int n;
+  int act; const float* w_halt; float thr; float* cum; int* loops; int t;
+  float* cum_dump;       // [N] by token, may be null
+  float* a_dump;         // [N, D] by token, may be null
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+struct PermuteArgs {
+  const int* idx; const int* ndev; int n_static;
+  int E, Se, k;
+  int* counts; int* offs; int* perm; int* inv;
+  int* ts_gu; int bm_gu; int* ts_dn; int bm_dn;
+  int* counts_dump;      // [E] may be null
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+struct CompactArgs {
+  const int* rows_in; const int* n_in; const float* cum; float thr;
+  int* rows_out; int* n_out; int* seg_out; int B, S;
+};
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------- MLA helpers
+struct MlaNormArgs {
+  int dtype;
+  const float* cq_raw; int ql;        // [N, ql] by token
+  const float* lat_raw; int kvl, nr;  // [N, kvl+nr] by token
+  const float* gq; const float* gkv; float eps;
+  const int* rows; const int* ndev; int n;
+  void* cqn; void* latent;            // T [N, ql], T [N, kvl+nr] by token
+  const float* cosb; const float* sinb; int S;
+};
+hipError_t launch_mla_norm(const MlaNormArgs& a, hipStream_t s);
+
+struct QRopeArgs {
+  int dtype;
+  const void* src; int src_ld, src_hs, src_off;   // q_pe of row i head h at src + i*ld + h*hs + off
+  void* dst; int dst_ld, dst_hs, dst_off;
+  int H, nr;
+  const int* rows; const int* ndev; int n;
+  const float* cosb; const float* sinb; int S;
+};
+hipError_t launch_qrope(const QRopeArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ utilities
+hipError_t launch_rope_tables(float* cosb, float* sinb, int S, int dr, float base, hipStream_t s);
+hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t s);
+hipError_t launch_fill_f32(float* p, float v, long long n, hipStream_t s);
+hipError_t launch_fill_u16(uint16_t* p, uint16_t v, long long n, hipStream_t s);
+hipError_t launch_iota(int* p, int n, int* count, int count_val, int* seg, int B, int S, hipStream_t s);
+hipError_t launch_copy_f32(float* dst, const float* src, long long n, hipStream_t s);
+// dst[h][c][i] = src[h*rows + i][c]: per-head transpose of an [H*rows, cols] matrix
+hipError_t launch_head_transpose(int dtype, void* dst, const void* src, int H, int rows, int cols,
+                                 hipStream_t s);
+
+}  // namespace rdt

@@ -1,0 +1,127 @@
+// Config validation and workspace planning (host-only C++).
+#include "rdt_plan.h"
+
+#include <stdio.h>
+
+namespace rdt {
+
+// Tile heights of the grouped expert GEMMs (kept in step with rdt_launch.h,
+// which this file does not include so that it builds without HIP).
+static constexpr int kGuBM = 128;
+static constexpr int kDnBM = 64;
+
+static rdt_status fail(std::string* why, rdt_status st, const char* msg) {
+  if (why) *why = msg;
+  return st;
+}
+
+rdt_status validate_config(const rdt_config& c, std::string* why) {
+  if (c.batch <= 0 || c.seq <= 0 || c.dim <= 0) return fail(why, RDT_E_INVALID, "batch, seq and dim must be positive");
+  if (c.n_heads <= 0) return fail(why, RDT_E_INVALID, "n_heads must be positive");
+  if (c.n_experts <= 0 || c.top_k <= 0) return fail(why, RDT_E_INVALID, "n_experts and top_k must be positive");
+  if (c.top_k > c.n_experts) return fail(why, RDT_E_INVALID, "top_k exceeds n_experts");
+  if (c.expert_dim <= 0) return fail(why, RDT_E_INVALID, "expert_dim must be positive");
+  if (c.n_shared_experts < 0) return fail(why, RDT_E_INVALID, "n_shared_experts is negative");
+  if (c.n_bias_rows < 0) return fail(why, RDT_E_INVALID, "n_bias_rows is negative");
+  if (c.lora_rank < 0 || c.n_lora < 0) return fail(why, RDT_E_INVALID, "lora_rank and n_lora must be >= 0");
+  if (c.lora_rank > 0 && c.n_lora <= 0) return fail(why, RDT_E_INVALID, "lora_rank > 0 needs n_lora >= 1");
+  if (c.max_T < 0) return fail(why, RDT_E_INVALID, "max_T is negative");
+  if (!(c.norm_eps >= 0.f)) return fail(why, RDT_E_INVALID, "norm_eps must be >= 0");
+  if (!(c.rope_base > 0.f)) return fail(why, RDT_E_INVALID, "rope_base must be positive");
+  if (c.dtype != RDT_F32 && c.dtype != RDT_BF16) return fail(why, RDT_E_INVALID, "unknown dtype");
+  if (c.act_enabled && !(c.act_threshold > 0.f)) return fail(why, RDT_E_INVALID, "act_threshold must be positive");
+  if (c.attn_type == RDT_ATTN_GQA) {
+    if (c.n_kv_heads <= 0 || c.n_heads % c.n_kv_heads)
+      return fail(why, RDT_E_INVALID, "n_heads must be a positive multiple of n_kv_heads");
+    if (c.head_dim <= 0 || (c.head_dim & 1)) return fail(why, RDT_E_INVALID, "head_dim must be positive and even");
+    if (c.head_dim != 16 && c.head_dim != 32 && c.head_dim != 64 && c.head_dim != 128)
+      return fail(why, RDT_E_UNSUPPORTED, "head_dim must be 16, 32, 64 or 128");
+  } else if (c.attn_type == RDT_ATTN_MLA) {
+    if (c.q_lora_rank <= 0 || c.kv_lora_rank <= 0 || c.qk_rope_head_dim <= 0 || c.qk_nope_head_dim <= 0 ||
+        c.v_head_dim <= 0)
+      return fail(why, RDT_E_INVALID, "MLA ranks and head widths must be positive");
+    if (c.qk_rope_head_dim & 1) return fail(why, RDT_E_INVALID, "qk_rope_head_dim must be even");
+    const int dq = c.kv_lora_rank + c.qk_rope_head_dim;
+    if (!((dq == 160 && c.kv_lora_rank == 128) || (dq == 96 && c.kv_lora_rank == 64)))
+      return fail(why, RDT_E_UNSUPPORTED, "MLA latent must be kv_lora_rank 128 + rope 32 or 64 + 32");
+    if (c.q_lora_rank % 8 || c.qk_nope_head_dim % 8 || c.v_head_dim % 8 || c.qk_rope_head_dim % 8)
+      return fail(why, RDT_E_UNSUPPORTED, "MLA widths must be multiples of 8");
+  } else {
+    return fail(why, RDT_E_INVALID, "unknown attn_type");
+  }
+  if (c.dim % 8) return fail(why, RDT_E_UNSUPPORTED, "dim must be a multiple of 8");
+  if (c.dim > 4096) return fail(why, RDT_E_UNSUPPORTED, "dim above 4096");
+  if (c.expert_dim % 8) return fail(why, RDT_E_UNSUPPORTED, "expert_dim must be a multiple of 8");
+  if (c.n_experts > 64) return fail(why, RDT_E_UNSUPPORTED, "more than 64 routed experts");
+  if (c.lora_rank % 8) return fail(why, RDT_E_UNSUPPORTED, "lora_rank must be a multiple of 8");
+  const long long N = (long long)c.batch * c.seq;
+  if (N * (c.top_k + c.n_shared_experts) > (1ll << 30)) return fail(why, RDT_E_UNSUPPORTED, "too many token rows");
+  return RDT_OK;
+}
+
+static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Plan make_plan(const rdt_config& c, int T) {
+  Plan p{};
+  p.B = c.batch; p.S = c.seq; p.N = c.batch * c.seq; p.D = c.dim;
+  p.H = c.n_heads; p.E = c.n_experts; p.Se = c.n_shared_experts; p.k = c.top_k;
+  p.F = c.expert_dim; p.r = c.lora_rank; p.L = c.n_lora; p.T = T;
+  p.elt = c.dtype == RDT_F32 ? 4 : 2;
+  p.mla = c.attn_type == RDT_ATTN_MLA;
+  if (p.mla) {
+    p.KV = 1; p.d = 0;
+    p.ql = c.q_lora_rank; p.kvl = c.kv_lora_rank; p.nr = c.qk_rope_head_dim;
+    p.nope = c.qk_nope_head_dim; p.vd = c.v_head_dim;
+    p.dq = p.kvl + p.nr; p.dv = p.kvl; p.hv = p.H * p.vd; p.dr = p.nr;
+  } else {
+    p.KV = c.n_kv_heads; p.d = c.head_dim;
+    p.dq = p.d; p.dv = p.d; p.hv = p.H * p.d; p.dr = p.d;
+  }
+  const size_t N = p.N, D = p.D, e = p.elt;
+  const int G = p.E + p.Se;
+  p.gu_max_mtiles = (int)((N * p.k) / kGuBM + p.E + p.Se * ((N + kGuBM - 1) / kGuBM));
+  p.dn_max_mtiles = (int)((N * p.k) / kDnBM + p.E + p.Se * ((N + kDnBM - 1) / kDnBM));
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+  p.cosb = take((size_t)p.S * (p.dr / 2) * 4);
+  p.sinb = take((size_t)p.S * (p.dr / 2) * 4);
+  p.n1 = take(N * D * e);
+  if (p.mla) {
+    p.cq_raw = take(N * p.ql * 4);
+    p.lat_raw = take(N * (p.kvl + p.nr) * 4);
+    p.cqn = take(N * p.ql * e);
+    p.latent = take(N * (p.kvl + p.nr) * e);
+    p.qfull = take(N * p.H * (p.nope + p.nr) * e);
+    p.qattn = take(N * p.H * (p.kvl + p.nr) * e);
+    p.olat = take(N * p.H * p.kvl * e);
+    p.wukT = take((size_t)p.H * p.kvl * p.nope * e);
+  } else {
+    p.q = take(N * p.H * p.d * e);
+    p.k_ = take(N * p.KV * p.d * e);
+    p.v_ = take(N * p.KV * p.d * e);
+  }
+  p.o = take(N * p.hv * e);
+  p.z = take(N * (p.r > 0 ? p.r : 1) * e);
+  p.a = take(N * D * 4);
+  p.n2 = take(N * D * e);
+  p.idx = take(N * p.k * 4);
+  p.gates = take(N * p.k * 4);
+  p.gap = take(N * 4);
+  p.counts = take((size_t)(p.E + 1) * 4);
+  p.offs = take((size_t)(p.E + 1) * 4);
+  p.ts_gu = take((size_t)(G + 1) * 4);
+  p.ts_dn = take((size_t)(G + 1) * 4);
+  p.perm = take(N * p.k * 4);
+  p.inv = take(N * p.k * 4);
+  p.hmid = take(N * (p.k + p.Se) * p.F * e);
+  p.y = take(N * (p.k + p.Se) * D * e);
+  const size_t Tp = (size_t)(T > 0 ? T : 0) + 1;
+  p.lists = take(Tp * N * 4);
+  p.ncount = take(Tp * 4);
+  p.seg = take(Tp * (p.B + 1) * 4);
+  p.cum = take(N * 4);
+  p.total = off;
+  return p;
+}
+
+}  // namespace rdt

@@ -1,0 +1,37 @@
+// Host-only planning for librdt: config validation and the device workspace
+// layout. No HIP dependency, so it builds and tests with a plain C++ compiler.
+#pragma once
+#include <stddef.h>
+#include <string>
+
+#include "../../include/rdt.h"
+
+namespace rdt {
+
+struct Plan {
+  // shapes
+  int B, S, N, D, H, KV, d, E, Se, k, F, r, L, T;
+  int mla;                  // 1 for multi-latent attention
+  int ql, kvl, nr, nope, vd;
+  int dq;                   // per-head query/key width seen by attention
+  int dv;                   // per-head value width seen by attention
+  int hv;                   // width of the concatenated attention output
+  int dr;                   // rope width
+  int elt;                  // bytes per stored element (2 or 4)
+  int gu_max_mtiles, dn_max_mtiles;
+  // workspace byte offsets
+  size_t cosb, sinb, n1, q, k_, v_, o, z, a, n2;
+  size_t cq_raw, lat_raw, cqn, latent, qfull, qattn, olat, wukT;
+  size_t idx, gates, gap, counts, offs, ts_gu, ts_dn, perm, inv;
+  size_t hmid, y;
+  size_t lists, ncount, seg, cum;
+  size_t total;
+};
+
+// RDT_OK, RDT_E_INVALID or RDT_E_UNSUPPORTED; *why receives a message.
+rdt_status validate_config(const rdt_config& c, std::string* why);
+
+// Layout for loop counts up to T (T >= 0). Requires a validated config.
+Plan make_plan(const rdt_config& c, int T);
+
+}  // namespace rdt

@@ -1,0 +1,443 @@
+// Bandwidth-bound row kernels of the recurrent block: the two RMSNorms, the MoE
+// combine fused with the LTI injection and ACT halting, the stable expert
+// permutation, the active-list compaction, and small utilities.
+//
+// Row kernels give one wave64 to one token row; each lane moves 16-byte
+// vectors, so a row of D floats is read in D/256 fully coalesced passes.
+#include "rdt_device.h"
+#include "rdt_launch.h"
+
+namespace rdt {
+
+constexpr int MAXV = 16;  // float4 vectors per lane: rows up to 4096 wide
+
+// ------------------------------------------------------------------ RMSNorm
+// x = h[tok] + e[tok] (+ a[i]); out = x / sqrt(mean(x^2) + eps) * g
+template <typename T>
+__global__ __launch_bounds__(256) void k_norm(NormArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave;
+  const int n = a.ndev ? *a.ndev : a.n;
+  if (i >= n) return;
+  const int tok = a.rows ? a.rows[i] : i;
+  const int D = a.D;
+  float x[MAXV][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < MAXV; ++c) {
+    const int col = (c * 64 + lane) * 4;
+    if (col < D) {
+      const float4 hv = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + col);
+      const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
+      x[c][0] = hv.x + ev.x; x[c][1] = hv.y + ev.y; x[c][2] = hv.z + ev.z; x[c][3] = hv.w + ev.w;
+      if (a.a) {
+        const float4 av = *reinterpret_cast<const float4*>(a.a + (long long)i * D + col);
+        x[c][0] += av.x; x[c][1] += av.y; x[c][2] += av.z; x[c][3] += av.w;
+      }
+      ss += x[c][0] * x[c][0] + x[c][1] * x[c][1] + x[c][2] * x[c][2] + x[c][3] * x[c][3];
+    }
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.f / sqrtf(ss / (float)D + a.eps);
+  T* out = reinterpret_cast<T*>(a.out) + (long long)(a.out_scatter ? tok : i) * D;
+  T* dump = a.dump ? reinterpret_cast<T*>(a.dump) + (long long)tok * D : nullptr;
+#pragma unroll
+  for (int c = 0; c < MAXV; ++c) {
+    const int col = (c * 64 + lane) * 4;
+    if (col < D) {
+      const float4 gv = *reinterpret_cast<const float4*>(a.g + col);
+      float y[4] = {x[c][0] * inv * gv.x, x[c][1] * inv * gv.y, x[c][2] * inv * gv.z,
+                    x[c][3] * inv * gv.w};
+      store4<T>(out + col, y);
+      if (dump) store4<T>(dump + col, y);
+    }
+  }
+}
+
+hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  dim3 grid((a.n + 3) / 4);
+  if (a.dtype == DT_F32) hipLaunchKernelGGL(k_norm<float>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_norm<bf16_t>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------- combine + inject
+// m = sum_j gate_j * Y[inv_j] + sum_s Y_shared_s;  h = A*h + B*e + a + m
+// ACT: cum += sigmoid(w . h); loops = t + 1.
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave;
+  const int n = a.ndev ? *a.ndev : a.n;
+  if (i >= n) return;
+  const int tok = a.rows ? a.rows[i] : i;
+  const int D = a.D, k = a.k;
+  const T* Y = reinterpret_cast<const T*>(a.Y);
+  float z = 0.f;
+#pragma unroll 1
+  for (int c = 0; c < MAXV; ++c) {
+    const int col = (c * 64 + lane) * 4;
+    if (col >= D) break;
+    float m[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int p = a.inv[(long long)i * k + j];
+      const float gt = a.gates[(long long)i * k + j];
+      float y[4];
+      load4f<T>(Y + (long long)p * D + col, y);
+      m[0] += gt * y[0]; m[1] += gt * y[1]; m[2] += gt * y[2]; m[3] += gt * y[3];
+    }
+    for (int s = 0; s < a.Se; ++s) {
+      const long long p = (long long)n * k + (long long)s * n + i;
+      float y[4];
+      load4f<T>(Y + p * D + col, y);
+      m[0] += y[0]; m[1] += y[1]; m[2] += y[2]; m[3] += y[3];
+    }
+    float* hp = a.h + (long long)tok * D + col;
+    const float4 hv = *reinterpret_cast<const float4*>(hp);
+    const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
+    const float4 av = *reinterpret_cast<const float4*>(a.a + (long long)i * D + col);
+    const float4 Av = *reinterpret_cast<const float4*>(a.A + col);
+    const float4 Bv = *reinterpret_cast<const float4*>(a.B + col);
+    float4 hn;
+    hn.x = Av.x * hv.x + Bv.x * ev.x + av.x + m[0];
+    hn.y = Av.y * hv.y + Bv.y * ev.y + av.y + m[1];
+    hn.z = Av.z * hv.z + Bv.z * ev.z + av.z + m[2];
+    hn.w = Av.w * hv.w + Bv.w * ev.w + av.w + m[3];
+    *reinterpret_cast<float4*>(hp) = hn;
+    if (a.a_dump) *reinterpret_cast<float4*>(a.a_dump + (long long)tok * D + col) = av;
+    if (a.act) {
+      const float4 wv = *reinterpret_cast<const float4*>(a.w_halt + col);
+      z += wv.x * hn.x + wv.y * hn.y + wv.z * hn.z + wv.w * hn.w;
+    }
+  }
+  if (a.act) {
+    z = wave_sum(z);
+    if (lane == 0) {
+      const float p = 1.f / (1.f + expf(-z));
+      const float c = a.cum[tok] + p;
+      a.cum[tok] = c;
+      if (a.cum_dump) a.cum_dump[tok] = c;
+    }
+  }
+  if (lane == 0 && a.loops) a.loops[tok] = a.t + 1;
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  dim3 grid((a.n + 3) / 4);
+  if (a.dtype == DT_F32) hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_combine<bf16_t>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ expert permutation
+// One workgroup of 1024 threads. Rows are taken in chunks of 1024; a ballot per
+// expert ranks the rows of one wave that chose it, wave totals are scanned per
+// expert, and a running count carries across chunks. Positions inside an
+// expert therefore follow row order (a stable counting sort, no atomics).
+__global__ __launch_bounds__(1024) void k_permute(PermuteArgs a) {
+  __shared__ unsigned long long wmask[16][MAX_EXPERTS];
+  __shared__ int wbase[16][MAX_EXPERTS];
+  __shared__ int run[MAX_EXPERTS];
+  __shared__ int offs_s[MAX_EXPERTS + 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = a.ndev ? *a.ndev : a.n_static;
+  const int E = a.E, k = a.k;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  if (tid < MAX_EXPERTS) run[tid] = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < n; c0 += 1024) {
+    const int i = c0 + tid;
+    unsigned long long sel = 0;
+    if (i < n)
+      for (int j = 0; j < k; ++j) sel |= 1ull << a.idx[(long long)i * k + j];
+    for (int e = 0; e < E; ++e) {
+      const unsigned long long m = __ballot((sel >> e) & 1ull);
+      if (lane == 0) wmask[wave][e] = m;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int acc = run[tid];
+      for (int w = 0; w < 16; ++w) {
+        wbase[w][tid] = acc;
+        acc += __popcll(wmask[w][tid]);
+      }
+      run[tid] = acc;
+    }
+    __syncthreads();
+    if (i < n)
+      for (int j = 0; j < k; ++j) {
+        const int e = a.idx[(long long)i * k + j];
+        a.inv[(long long)i * k + j] = wbase[wave][e] + __popcll(wmask[wave][e] & lt);
+      }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+      offs_s[e] = acc;
+      acc += run[e];
+    }
+    offs_s[E] = acc;
+    const int G = E + a.Se;
+    int tg = 0, td = 0;
+    for (int g = 0; g < G; ++g) {
+      const int cnt = g < E ? run[g] : n;
+      a.ts_gu[g] = tg;
+      a.ts_dn[g] = td;
+      tg += (cnt + a.bm_gu - 1) / a.bm_gu;
+      td += (cnt + a.bm_dn - 1) / a.bm_dn;
+    }
+    a.ts_gu[G] = tg;
+    a.ts_dn[G] = td;
+  }
+  __syncthreads();
+  if (tid < E) {
+    a.counts[tid] = run[tid];
+    a.offs[tid] = offs_s[tid];
+    if (a.counts_dump) a.counts_dump[tid] = run[tid];
+  }
+  if (tid == 0) a.offs[E] = offs_s[E];
+  for (int i = tid; i < n; i += 1024)
+    for (int j = 0; j < k; ++j) {
+      const long long q = (long long)i * k + j;
+      const int p = offs_s[a.idx[q]] + a.inv[q];
+      a.inv[q] = p;
+      a.perm[p] = i;
+    }
+}
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------- ACT compaction
+// Stable filter of the active list (tokens whose cumulative halting sum is
+// still below the threshold) plus the start of every sequence in the new list.
+__global__ __launch_bounds__(1024) void k_compact(CompactArgs a) {
+  __shared__ int wtot[16];
+  __shared__ int woff[16];
+  __shared__ int total_s;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = *a.n_in;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int running = 0;
+  for (int c0 = 0; c0 < n; c0 += 1024) {
+    const int i = c0 + tid;
+    int tok = -1;
+    bool keep = false;
+    if (i < n) {
+      tok = a.rows_in[i];
+      keep = a.cum[tok] < a.thr;
+    }
+    const unsigned long long m = __ballot(keep);
+    if (lane == 0) wtot[wave] = __popcll(m);
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int w = 0; w < 16; ++w) {
+        woff[w] = acc;
+        acc += wtot[w];
+      }
+      total_s = acc;
+    }
+    __syncthreads();
+    if (keep) a.rows_out[running + woff[wave] + __popcll(m & lt)] = tok;
+    running += total_s;
+    __syncthreads();
+  }
+  if (tid == 0) *a.n_out = running;
+  __syncthreads();
+  // seg[b] = first list position whose token belongs to sequence >= b
+  if (tid <= a.B) {
+    const int target = tid * a.S;
+    int lo = 0, hi = running;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a.rows_out[mid] < target) lo = mid + 1;
+      else hi = mid;
+    }
+    a.seg_out[tid] = lo;
+  }
+}
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------- MLA latents
+// cqn = RMSNorm(c_q) * gq;  latent = [RMSNorm(c_kv) * gkv | rope(k_rope)]
+template <typename T>
+__global__ __launch_bounds__(256) void k_mla_norm(MlaNormArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave;
+  const int n = a.ndev ? *a.ndev : a.n;
+  if (i >= n) return;
+  const int tok = a.rows ? a.rows[i] : i;
+  // c_q
+  {
+    const float* src = a.cq_raw + (long long)tok * a.ql;
+    float ss = 0.f;
+    for (int c = lane; c < a.ql; c += 64) ss += src[c] * src[c];
+    ss = wave_sum(ss);
+    const float inv = 1.f / sqrtf(ss / (float)a.ql + a.eps);
+    T* dst = reinterpret_cast<T*>(a.cqn) + (long long)tok * a.ql;
+    for (int c = lane; c < a.ql; c += 64) dst[c] = ST<T>::from_f(src[c] * inv * a.gq[c]);
+  }
+  const int W = a.kvl + a.nr;
+  const float* src = a.lat_raw + (long long)tok * W;
+  T* dst = reinterpret_cast<T*>(a.latent) + (long long)tok * W;
+  {
+    float ss = 0.f;
+    for (int c = lane; c < a.kvl; c += 64) ss += src[c] * src[c];
+    ss = wave_sum(ss);
+    const float inv = 1.f / sqrtf(ss / (float)a.kvl + a.eps);
+    for (int c = lane; c < a.kvl; c += 64) dst[c] = ST<T>::from_f(src[c] * inv * a.gkv[c]);
+  }
+  const int half = a.nr >> 1;
+  const int pos = tok % a.S;
+  for (int j = lane; j < half; j += 64) {
+    const float x1 = src[a.kvl + j], x2 = src[a.kvl + j + half];
+    const float cs = a.cosb[pos * half + j], sn = a.sinb[pos * half + j];
+    dst[a.kvl + j] = ST<T>::from_f(x1 * cs - x2 * sn);
+    dst[a.kvl + j + half] = ST<T>::from_f(x1 * sn + x2 * cs);
+  }
+}
+
+hipError_t launch_mla_norm(const MlaNormArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  dim3 grid((a.n + 3) / 4);
+  if (a.dtype == DT_F32) hipLaunchKernelGGL(k_mla_norm<float>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_mla_norm<bf16_t>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// rope of the per-head query rope slice into the attention query buffer
+template <typename T>
+__global__ __launch_bounds__(256) void k_qrope(QRopeArgs a) {
+  const int half = a.nr >> 1;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int n = a.ndev ? *a.ndev : a.n;
+  const long long per_row = (long long)a.H * half;
+  const int i = (int)(gid / per_row);
+  if (i >= n) return;
+  const int rem = (int)(gid % per_row);
+  const int h = rem / half, j = rem % half;
+  const int tok = a.rows ? a.rows[i] : i;
+  const int pos = tok % a.S;
+  const T* s = reinterpret_cast<const T*>(a.src) + (long long)i * a.src_ld + (long long)h * a.src_hs + a.src_off;
+  T* d = reinterpret_cast<T*>(a.dst) + (long long)i * a.dst_ld + (long long)h * a.dst_hs + a.dst_off;
+  const float x1 = ST<T>::to_f(s[j]), x2 = ST<T>::to_f(s[j + half]);
+  const float cs = a.cosb[pos * half + j], sn = a.sinb[pos * half + j];
+  d[j] = ST<T>::from_f(x1 * cs - x2 * sn);
+  d[j + half] = ST<T>::from_f(x1 * sn + x2 * cs);
+}
+
+hipError_t launch_qrope(const QRopeArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  const long long tot = (long long)a.n * a.H * (a.nr / 2);
+  dim3 grid((unsigned)((tot + 255) / 256));
+  if (a.dtype == DT_F32) hipLaunchKernelGGL(k_qrope<float>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_qrope<bf16_t>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------- utilities
+// RoPE angles in double precision: angle(s, i) = s * base^(-2i/dr)
+__global__ void k_rope_tables(float* cosb, float* sinb, int S, int dr, float base) {
+  const int half = dr >> 1;
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  if (gid >= S * half) return;
+  const int s = gid / half, i = gid % half;
+  const double inv = pow((double)base, -2.0 * (double)i / (double)dr);
+  const double ang = (double)s * inv;
+  cosb[gid] = (float)cos(ang);
+  sinb[gid] = (float)sin(ang);
+}
+
+hipError_t launch_rope_tables(float* cosb, float* sinb, int S, int dr, float base, hipStream_t s) {
+  const int tot = S * (dr / 2);
+  hipLaunchKernelGGL(k_rope_tables, dim3((tot + 255) / 256), dim3(256), 0, s, cosb, sinb, S, dr, base);
+  return hipGetLastError();
+}
+
+template <typename V>
+__global__ void k_fill(V* p, V v, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = v;
+}
+
+static unsigned fill_blocks(long long n) {
+  long long b = (n + 255) / 256;
+  return (unsigned)(b < 4096 ? (b < 1 ? 1 : b) : 4096);
+}
+
+hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill<int>, dim3(fill_blocks(n)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+hipError_t launch_fill_f32(float* p, float v, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill<float>, dim3(fill_blocks(n)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+hipError_t launch_fill_u16(uint16_t* p, uint16_t v, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill<uint16_t>, dim3(fill_blocks(n)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+__global__ void k_iota(int* p, int n, int* count, int count_val, int* seg, int B, int S) {
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  if (gid < n) p[gid] = gid;
+  if (gid == 0 && count) *count = count_val;
+  if (seg && gid <= B) seg[gid] = gid * S;
+}
+
+hipError_t launch_iota(int* p, int n, int* count, int count_val, int* seg, int B, int S, hipStream_t s) {
+  const int tot = n > B + 1 ? n : B + 1;
+  hipLaunchKernelGGL(k_iota, dim3((tot + 255) / 256), dim3(256), 0, s, p, n, count, count_val, seg, B, S);
+  return hipGetLastError();
+}
+
+__global__ void k_copy_f32(float4* dst, const float4* src, long long n4) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy_f32(float* dst, const float* src, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const long long n4 = n / 4;  // callers pass multiples of 4
+  hipLaunchKernelGGL(k_copy_f32, dim3(fill_blocks(n4)), dim3(256), 0, s, reinterpret_cast<float4*>(dst),
+                     reinterpret_cast<const float4*>(src), n4);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ void k_head_transpose(T* dst, const T* src, int H, int rows, int cols) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long tot = (long long)H * rows * cols;
+  if (gid >= tot) return;
+  const int i = (int)(gid % rows);
+  const long long r = gid / rows;
+  const int c = (int)(r % cols);
+  const int h = (int)(r / cols);
+  dst[gid] = src[((long long)h * rows + i) * cols + c];
+}
+
+hipError_t launch_head_transpose(int dtype, void* dst, const void* src, int H, int rows, int cols,
+                                 hipStream_t s) {
+  const long long tot = (long long)H * rows * cols;
+  dim3 grid((unsigned)((tot + 255) / 256));
+  if (dtype == DT_F32)
+    hipLaunchKernelGGL(k_head_transpose<float>, grid, dim3(256), 0, s, (float*)dst, (const float*)src, H, rows, cols);
+  else
+    hipLaunchKernelGGL(k_head_transpose<bf16_t>, grid, dim3(256), 0, s, (bf16_t*)dst, (const bf16_t*)src, H, rows,
+                       cols);
+  return hipGetLastError();
+}
+
+}  // namespace rdt

@@ -1,0 +1,137 @@
+"""GPU parity of librdt against the CPU oracle (needs an MI355X)."""
+import numpy as np
+import pytest
+
+from oracle import rdt_oracle as ro
+from rdt_inputs import get_config, make_inputs, n_tokens
+
+from rdt_gpu_run import check_routing_teacher_forced, rms, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2  # max |dh| <= TOL * RMS(h_T) after T loops, routing and halting forced
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from recurrent_depth_transformer_amd import load_library
+    load_library()
+
+
+def _report(name, **kw):
+    print(f"[parity] {name}: " + ", ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa_small", "wide_small", "act_small", "mla_small"])
+def test_closed_form_injection(name):
+    cfg = get_config(name)
+    inp = make_inputs(cfg)
+    inp["Wo"] = np.zeros_like(inp["Wo"])
+    inp["Wd"] = np.zeros_like(inp["Wd"])
+    if cfg["n_shared_experts"]:
+        inp["Wsd"] = np.zeros_like(inp["Wsd"])
+    if cfg["lora_rank"]:
+        inp["lora_up"] = np.zeros_like(inp["lora_up"])
+    cfg["act"] = False
+    T = 5
+    res, *_ = run_gpu(cfg, inp, T=T, dumps=False)
+    A, B = inp["A"].astype(np.float64), inp["B"].astype(np.float64)
+    closed = A ** T * inp["h0"] + B * inp["e"] * (1 - A ** T) / (1 - A)
+    err = np.max(np.abs(res["h"] - closed))
+    _report(f"closed-form {name}", max_abs=err)
+    assert err <= 1e-5 * max(1.0, np.max(np.abs(closed)))
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_bf16", "gqa_small", "wide_small", "act_small", "mla_small"])
+def test_end_to_end_forced(name):
+    cfg = get_config(name)
+    T = cfg["T"]
+    res, inp, *_ = run_gpu(cfg, T=T)
+    mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro)
+    forced_loops = res["loops"] if cfg["act"] else None
+    ref = ro.forward(cfg, inp, T=T, forced_idx=res["route_idx"], forced_loops=forced_loops)
+    err = np.max(np.abs(res["h"] - ref["h"]))
+    scale = rms(ref["h"])
+    _report(name, max_abs=f"{err:.3e}", rms=f"{scale:.3f}", ratio=f"{err / scale:.3e}",
+            route_mismatch=mism, near_ties=near, compared=comp,
+            loops_mean=float(np.mean(res["loops"])))
+    assert mism == 0
+    assert err <= TOL * scale
+    if cfg["act"]:
+        # halting decisions from the GPU's own states, loop by loop
+        thr = np.float32(cfg["act_threshold"])
+        cum = np.zeros(n_tokens(cfg), np.float32)
+        bad = 0
+        for t in range(T):
+            act_rows = np.nonzero(res["loops"] > t)[0]
+            z = res["h_dump"][t + 1][act_rows].astype(np.float64) @ inp["w_halt"].astype(np.float64)
+            cum[act_rows] = (cum[act_rows] + (1 / (1 + np.exp(-z))).astype(np.float32)).astype(np.float32)
+            halt_o = cum[act_rows] >= thr
+            halt_g = res["loops"][act_rows] == t + 1
+            clear = np.abs(cum[act_rows] - thr) >= 1e-3
+            bad += int(np.sum((halt_o != halt_g) & clear))
+            np.testing.assert_allclose(res["act_cum"][t][act_rows], cum[act_rows], rtol=1e-4, atol=1e-4)
+        assert bad == 0
+        assert 0 < res["loops"].min() <= res["loops"].max() <= T
+
+
+@pytest.mark.parametrize("name", ["gqa_small", "act_small"])
+def test_graph_matches_eager_bitwise(name):
+    cfg = get_config(name)
+    r1, inp, _, W = run_gpu(cfg, dumps=False, graph=True)
+    r2, *_ = run_gpu(cfg, inp, dumps=False, graph=False, weights=W)
+    assert np.array_equal(r1["h"], r2["h"])
+
+
+def test_repeat_runs_bitwise():
+    cfg = get_config("wide_small")
+    r1, inp, blk, W = run_gpu(cfg, dumps=True)
+    r2, *_ = run_gpu(cfg, inp, dumps=True, weights=W, block=blk)
+    for k in ("h", "route_idx", "expert_counts", "loops"):
+        assert np.array_equal(r1[k], r2[k]), k
+
+
+def test_T0_and_extrapolation():
+    cfg = get_config("gqa_small")
+    r0, inp, blk, W = run_gpu(cfg, T=0, dumps=False)
+    assert np.array_equal(r0["h"], inp["h0"])
+    # more loops than the workload's T (depth extrapolation); LoRA-free so any T is fine
+    res, *_ = run_gpu(cfg, inp, T=cfg["T"] + 2, dumps=True, weights=W)
+    ref = ro.forward(cfg, inp, T=cfg["T"] + 2, forced_idx=res["route_idx"])
+    assert np.max(np.abs(res["h"] - ref["h"])) <= TOL * rms(ref["h"])
+
+
+def test_error_paths():
+    import torch
+
+    from recurrent_depth_transformer_amd import RdtError, RecurrentBlock
+    cfg = get_config("tiny")
+    inp = make_inputs(cfg)
+    inp["A"] = inp["A"].copy()
+    inp["A"][5] = 1.0
+    with pytest.raises(RdtError) as ei:
+        run_gpu(cfg, inp, dumps=False)
+    assert "RDT_E_UNSTABLE" in str(ei.value)
+    inp = make_inputs(cfg)
+    _, _, blk, W = run_gpu(cfg, inp, dumps=False)
+    with pytest.raises(RdtError) as ei:
+        blk.forward(W["h0"], W["e"], W, T=-1)
+    assert "RDT_E_INVALID" in str(ei.value)
+    small = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(RdtError) as ei:
+        blk.forward(W["h0"], W["e"], W, T=2, workspace=small)
+    assert "RDT_E_WORKSPACE" in str(ei.value)
+    W2 = dict(W)
+    W2["Wq"] = None
+    with pytest.raises(RdtError) as ei:
+        blk.forward(W["h0"], W["e"], W2, T=1)
+    assert "RDT_E_INVALID" in str(ei.value)
+    # out may alias h0 exactly
+    h = W["h0"].clone()
+    blk.forward(h, W["e"], W, T=2, out=h)
+    ref = blk.forward(W["h0"], W["e"], W, T=2)
+    torch.cuda.synchronize()
+    assert torch.equal(h, ref)
