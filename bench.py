@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Recurrent-block throughput on one MI355X.
+
+One step = one rdt_recurrent_forward: the whole T-loop of the recurrent block
+(RMSNorm, causal attention, output projection, router, grouped SwiGLU experts,
+combine + LTI injection) over one batch of seeded synthetic inputs that are
+already resident in HBM, replayed as a captured HIP graph.
+
+Default workload: the GQA recurrent block -- batch 1, seq 512, dim 1024, 16/4
+heads of 64, 8 experts top-2 with SwiGLU hidden 2816, T = 3, bf16 weights and
+activations with fp32 accumulation and fp32 state.
+
+Prints one JSON line. `value` is token-loops per second (batch*seq*T tokens
+through one loop each, per forward); `roofline` describes the dominant kernel
+(the grouped gate/up expert GEMM), timed with HIP events around its launches on
+the stream they run on; `cpu_baseline` times the float64 CPU oracle on the
+host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "recurrent-block token-loops/sec at 1 MI355X; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+DOMINANT_STAGE = "expert_gate_up"
+DOMINANT_SOURCES = ["rdt_gemm.hip", "rdt_device.h"]
+
+
+def describe(cfg: dict) -> str:
+    att = (f"GQA {cfg['n_heads']}/{cfg['n_kv_heads']} heads of {cfg['head_dim']}" if cfg["attn"] == "gqa"
+           else f"MLA {cfg['n_heads']} heads, kv latent {cfg['kv_lora_rank']}+rope {cfg['qk_rope_head_dim']}, "
+                f"q latent {cfg['q_lora_rank']}")
+    moe = f"{cfg['n_experts']} experts top-{cfg['top_k']}"
+    if cfg["n_shared_experts"]:
+        moe += f" + {cfg['n_shared_experts']} shared"
+    extra = ""
+    if cfg["lora_rank"]:
+        extra += f", depth-wise LoRA r{cfg['lora_rank']}"
+    if cfg["act"]:
+        extra += f", ACT halting at {cfg['act_threshold']}"
+    return (f"{cfg['name']}: batch {cfg['batch']}, seq {cfg['seq']}, dim {cfg['dim']}, {att}, {moe}, "
+            f"SwiGLU hidden {cfg['expert_dim']}, T={cfg['T']}{extra}, {cfg['dtype']}")
+
+
+def flops_per_token_loop(cfg: dict) -> dict:
+    """Algorithmic FLOPs of one token through one loop (causal attention counts
+    the average (S+1)/2 visible keys; MLA is counted in absorbed form)."""
+    D, H, S = cfg["dim"], cfg["n_heads"], cfg["seq"]
+    keys = (S + 1) / 2.0
+    f = {}
+    if cfg["attn"] == "gqa":
+        d, KV = cfg["head_dim"], cfg["n_kv_heads"]
+        f["qkv"] = 2 * D * (H + 2 * KV) * d
+        f["attention"] = 2 * 2 * H * d * keys
+        hv = H * d
+    else:
+        ql, kvl, nr = cfg["q_lora_rank"], cfg["kv_lora_rank"], cfg["qk_rope_head_dim"]
+        nope, vd = cfg["qk_nope_head_dim"], cfg["v_head_dim"]
+        f["qkv"] = 2 * D * (ql + kvl + nr) + 2 * ql * H * (nope + nr) + 2 * H * nope * kvl
+        f["attention"] = 2 * H * (kvl + nr) * keys + 2 * H * kvl * keys + 2 * H * kvl * vd
+        hv = H * vd
+    f["out_proj"] = 2 * hv * D + (2 * cfg["lora_rank"] * (hv + D) if cfg["lora_rank"] else 0)
+    f["router"] = 2 * D * cfg["n_experts"]
+    f["experts"] = (cfg["top_k"] + cfg["n_shared_experts"]) * 6 * D * cfg["expert_dim"]
+    return f
+
+
+def gate_up_bytes(cfg: dict, counts_per_loop, elt: int) -> float:
+    """Algorithmic HBM bytes of the grouped gate/up GEMM, averaged per launch:
+    the gate and up matrices of every expert that received a row (and of every
+    shared expert), the routed rows read once, the SwiGLU output written once."""
+    D, F = cfg["dim"], cfg["expert_dim"]
+    tot = 0.0
+    for counts in counts_per_loop:
+        rows = int(sum(counts))
+        n_tok = rows // cfg["top_k"]
+        used = sum(1 for c in counts if c > 0) + cfg["n_shared_experts"]
+        all_rows = rows + cfg["n_shared_experts"] * n_tok
+        tot += used * 2 * F * D * elt + all_rows * D * elt + all_rows * F * elt
+    return tot / max(1, len(counts_per_loop))
+
+
+def source_hash(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "recurrent_depth_transformer_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """Per-launch HBM bytes of the dominant kernel from committed rocprofv3
+    counter runs, or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"expert_gate_up_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != source_hash(DOMINANT_SOURCES):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg: dict, inputs: dict, T: int, budget_s: float):
+    """Time the float64 CPU oracle on this host (repeats of the full forward
+    until the budget is used, at least one)."""
+    import numpy as np  # noqa: F401
+    from oracle import rdt_oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    runs, t_used = 0, 0.0
+    while runs == 0 or (t_used < budget_s and runs < 50):
+        t0 = time.perf_counter()
+        rdt_oracle.forward(cfg, inputs, T=T)
+        t_used += time.perf_counter() - t0
+        runs += 1
+    N = cfg["batch"] * cfg["seq"]
+    return {"value": N * T * runs / t_used, "unit": "token-loops/s", "cores": threads, "kind": "oracle",
+            "sample": f"{runs} full forward(s) of the {cfg['name']} workload (T={T}, {N} tokens) in float64 "
+                      f"NumPy, {t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa")
+    ap.add_argument("--profile-steps", type=int, default=10, help="eager forwards timed per stage")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stages", action="store_true", help="also print the per-stage breakdown to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import recurrent_depth_transformer_amd as rdt
+    from rdt_inputs import get_config, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = get_config(args.workload)
+    T, N = cfg["T"], cfg["batch"] * cfg["seq"]
+    inputs = make_inputs(cfg)
+    W = rdt.device_weights(inputs, cfg, "cuda")
+    blk = rdt.RecurrentBlock(cfg, graph=True)
+    out = torch.empty_like(W["h0"])
+    ws = blk.workspace(T)
+    stream = torch.cuda.current_stream()
+    print(f"[bench] {describe(cfg)}; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+
+    # executed token-loops (ACT halts tokens early) and per-loop expert counts
+    loops = torch.empty(N, dtype=torch.int32, device="cuda")
+    counts = torch.empty(T, cfg["n_experts"], dtype=torch.int32, device="cuda")
+    blk.forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws, aux={"loops": loops, "expert_counts": counts})
+    torch.cuda.synchronize()
+    executed = int(loops.sum().item())
+    counts_np = counts.cpu().numpy()
+
+    for _ in range(args.warmup):
+        blk.forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        blk.forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = executed / (ms * 1e-3)
+    print(f"[bench] {ms:.4f} ms per forward (wall {wall * 1e3 / args.steps:.4f} ms)", file=sys.stderr, flush=True)
+
+    # per-stage device time: kernels launched one by one with HIP events around
+    # each launch on the launch stream
+    acc = {}
+    for _ in range(max(1, args.profile_steps)):
+        _, st = blk.profile_forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws)
+        for k, (t_ms, n) in st.items():
+            a = acc.setdefault(k, [0.0, 0])
+            a[0] += t_ms
+            a[1] += n
+    stage_avg = {k: (v[0] / v[1] if v[1] else 0.0, v[1] // max(1, args.profile_steps)) for k, v in acc.items()}
+    if args.stages:
+        for k, (avg, n) in stage_avg.items():
+            print(f"[stage] {k:16s} {avg * 1e3:9.2f} us/launch x {n}", file=sys.stderr)
+
+    elt = 4 if cfg["dtype"] == "f32" else 2
+    fl = flops_per_token_loop(cfg)
+    flops = sum(fl.values()) * executed
+    peak_tf = PEAK_F32_TFLOPS if cfg["dtype"] == "f32" else PEAK_BF16_TFLOPS
+    gu_ms = stage_avg[DOMINANT_STAGE][0]
+    gu_bytes = gate_up_bytes(cfg, counts_np, elt)
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_from_profiles(args.workload),
+                "kernel": "k_grouped_gemm<bf16,128,128,0> (expert gate/up + SwiGLU)",
+                "avg_launch_us": round(gu_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(gu_bytes)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, inputs, T, args.cpu_budget)
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "token-loops/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
+        "data": "synthetic (seeded PCG64 draws, random-init weights)",
+        "config": {"workload": describe(cfg), "batch": cfg["batch"], "seq": cfg["seq"], "dim": cfg["dim"],
+                   "T": T, "token_loops_per_step": executed, "parallelism": "single GPU"},
+        "mfma_peak_frac": round(flops / (ms * 1e-3) / (peak_tf * 1e12), 5),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages_us": {k: round(v[0] * 1e3, 2) for k, v in stage_avg.items() if v[1]},
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

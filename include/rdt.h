@@ -221,6 +221,40 @@ rdt_status rdt_recurrent_forward(rdt_handle* h, const float* h0, const float* e,
                                  const rdt_aux* aux, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* Stages of one loop iteration, for rdt_profile_forward. */
+typedef enum rdt_stage {
+  RDT_STAGE_NORM1 = 0,    /* u = h + e, RMSNorm */
+  RDT_STAGE_QKV = 1,      /* q/k/v projections (+RoPE); MLA latent projections and norms */
+  RDT_STAGE_ATTN = 2,     /* causal flash attention (+ MLA value up-projection) */
+  RDT_STAGE_OPROJ = 3,    /* output projection (+ depth-wise LoRA) */
+  RDT_STAGE_NORM2 = 4,    /* x = u + a, RMSNorm */
+  RDT_STAGE_ROUTER = 5,   /* router logits, softmax, top-k */
+  RDT_STAGE_PERMUTE = 6,  /* per-expert counts, offsets, stable permutation */
+  RDT_STAGE_EXPERT_GU = 7,   /* grouped gate/up GEMM + SwiGLU */
+  RDT_STAGE_EXPERT_DOWN = 8, /* grouped down GEMM */
+  RDT_STAGE_COMBINE = 9,  /* MoE combine + LTI injection (+ ACT) */
+  RDT_STAGE_COMPACT = 10, /* ACT active-list compaction */
+  RDT_STAGE_OTHER = 11,   /* per-forward set-up, fills and dump copies */
+  RDT_N_STAGES = 12
+} rdt_stage;
+
+/*
+ * Profiling variant of rdt_recurrent_forward (same arguments and result):
+ * launches the kernels one by one on `stream` with a HIP event pair around
+ * each launch, waits for completion, and writes for every rdt_stage the summed
+ * device time in milliseconds (stage_ms) and the number of launches
+ * (stage_launches); both arrays hold n_stages >= RDT_N_STAGES entries (host
+ * memory). RDT_E_INVALID on null arrays or n_stages < RDT_N_STAGES.
+ */
+rdt_status rdt_profile_forward(rdt_handle* h, const float* h0, const float* e,
+                               const rdt_weights* w, int32_t T, float* out,
+                               const rdt_aux* aux, void* ws, size_t ws_bytes,
+                               void* stream, float* stage_ms, int32_t* stage_launches,
+                               int32_t n_stages);
+
+/* Short name of a stage ("" when out of range). */
+const char* rdt_stage_name(int32_t stage);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* rdt_last_error(void);
 

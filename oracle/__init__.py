@@ -31,5 +31,5 @@ reference.
 from .rdt_oracle import (  # noqa: F401
     rmsnorm, rope_tables, apply_rope, attention_causal, gqa_attention,
     mla_attention_explicit, swiglu, route, moe, block_step, forward,
-    spectral_radius, kv_cache_bytes_per_token,
+    spectral_radius, kv_cache_bytes_per_token, step_rows,
 )

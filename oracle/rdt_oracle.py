@@ -321,3 +321,66 @@ def forward(cfg, W, h0=None, e=None, T=None, forced_idx=None, forced_loops=None,
     if record:
         out.update(rec)
     return out
+
+
+def step_rows(cfg, W, h, e, t, rows, forced_idx_rows, tables=None):
+    """One loop update h_{t+1}[rows] for a sample of active tokens, given the
+    state h of every token (same definitions as block_step and forward; keys
+    and values come from every token of the sequence, queries only from the
+    sampled rows). forced_idx_rows: [len(rows), k] expert indices. Returns
+    (h_new_rows, a_rows, n2_rows)."""
+    h = np.asarray(h, F64)
+    e = np.asarray(e, F64)
+    rows = np.asarray(rows)
+    N, D = h.shape
+    S, eps = cfg["seq"], cfg["norm_eps"]
+    H = cfg["n_heads"]
+    if tables is None:
+        d_r = cfg["head_dim"] if cfg["attn"] == "gqa" else cfg["qk_rope_head_dim"]
+        tables = rope_tables(S, d_r, cfg["rope_base"])
+    cos, sin = tables
+    pos_all = np.arange(N) % S
+    u = h + e
+    n1 = rmsnorm(u, W["g1"], eps)
+    o = np.empty((rows.size, cfg["n_heads"] * (cfg["head_dim"] if cfg["attn"] == "gqa" else cfg["v_head_dim"])))
+    if cfg["attn"] == "gqa":
+        KV, d = cfg["n_kv_heads"], cfg["head_dim"]
+        k = apply_rope((n1 @ W["Wk"].astype(F64).T).reshape(N, KV, d), pos_all, cos, sin)
+        v = (n1 @ W["Wv"].astype(F64).T).reshape(N, KV, d)
+        q = apply_rope((n1[rows] @ W["Wq"].astype(F64).T).reshape(rows.size, H, d), pos_all[rows], cos, sin)
+        for r, n in enumerate(rows):
+            b0 = (n // S) * S
+            for i in range(H):
+                j = (i * KV) // H
+                s = (k[b0:n + 1, j] @ q[r, i]) / np.sqrt(d)
+                p = softmax(s)
+                o[r, i * d:(i + 1) * d] = p @ v[b0:n + 1, j]
+    else:
+        ql, kvl = cfg["q_lora_rank"], cfg["kv_lora_rank"]
+        nr, nope, vd = cfg["qk_rope_head_dim"], cfg["qk_nope_head_dim"], cfg["v_head_dim"]
+        lat = n1 @ W["Wdkv"].astype(F64).T
+        ckv = rmsnorm(lat[:, :kvl], W["gkv"], eps)
+        kpe = apply_rope(lat[:, None, kvl:], pos_all, cos, sin)[:, 0]
+        kn = (ckv @ W["Wuk"].astype(F64).T).reshape(N, H, nope)
+        vv = (ckv @ W["Wuv"].astype(F64).T).reshape(N, H, vd)
+        cq = rmsnorm(n1[rows] @ W["Wdq"].astype(F64).T, W["gq"], eps)
+        q = (cq @ W["Wuq"].astype(F64).T).reshape(rows.size, H, nope + nr)
+        qpe = apply_rope(q[..., nope:], pos_all[rows], cos, sin)
+        for r, n in enumerate(rows):
+            b0 = (n // S) * S
+            for i in range(H):
+                s = (kn[b0:n + 1, i] @ q[r, i, :nope] + kpe[b0:n + 1] @ qpe[r, i]) / np.sqrt(nope + nr)
+                p = softmax(s)
+                o[r, i * vd:(i + 1) * vd] = p @ vv[b0:n + 1, i]
+    a = o @ W["Wo"].astype(F64).T
+    if cfg["lora_rank"]:
+        tl = min(t, cfg["n_lora"] - 1)
+        a = a + (o @ W["lora_down"][tl].astype(F64).T) @ W["lora_up"][tl].astype(F64).T
+    x = u[rows] + a
+    n2 = rmsnorm(x, W["g2"], eps)
+    idx = np.asarray(forced_idx_rows, np.int64)
+    p = softmax(n2 @ W["Wr"].astype(F64).T, axis=1)
+    gates = p[np.arange(rows.size)[:, None], idx]
+    m = moe(n2, idx, gates, W, cfg["n_shared_experts"])
+    h_new = np.asarray(W["A"], F64) * h[rows] + np.asarray(W["B"], F64) * e[rows] + a + m
+    return h_new, a, n2

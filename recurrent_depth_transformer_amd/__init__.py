@@ -22,8 +22,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librdt.so")
 EXPORTED_SYMBOLS = [
     "rdt_config_default", "rdt_config_validate", "rdt_create", "rdt_destroy",
     "rdt_workspace_size", "rdt_spectral_radius", "rdt_set_graph_mode",
-    "rdt_recurrent_forward", "rdt_last_error", "rdt_version",
+    "rdt_recurrent_forward", "rdt_profile_forward", "rdt_stage_name", "rdt_last_error", "rdt_version",
 ]
+N_STAGES = 12
 
 RDT_OK, RDT_E_INVALID, RDT_E_UNSUPPORTED, RDT_E_UNSTABLE, RDT_E_WORKSPACE, RDT_E_HIP = 0, -1, -2, -3, -4, -5
 _STATUS = {RDT_E_INVALID: "RDT_E_INVALID", RDT_E_UNSUPPORTED: "RDT_E_UNSUPPORTED",
@@ -86,10 +87,15 @@ def load_library(path: str = LIB_PATH):
     lib.rdt_set_graph_mode.argtypes = [_vp, _i32]
     lib.rdt_recurrent_forward.argtypes = [_vp, _vp, _vp, ctypes.POINTER(RdtWeights), _i32, _vp,
                                           ctypes.POINTER(RdtAux), _vp, ctypes.c_size_t, _vp]
+    lib.rdt_profile_forward.argtypes = [_vp, _vp, _vp, ctypes.POINTER(RdtWeights), _i32, _vp,
+                                        ctypes.POINTER(RdtAux), _vp, ctypes.c_size_t, _vp,
+                                        ctypes.POINTER(_f32), ctypes.POINTER(_i32), _i32]
+    lib.rdt_stage_name.argtypes = [_i32]
+    lib.rdt_stage_name.restype = ctypes.c_char_p
     lib.rdt_last_error.restype = ctypes.c_char_p
     lib.rdt_version.restype = ctypes.c_char_p
     for name in ["rdt_config_default", "rdt_config_validate", "rdt_create", "rdt_spectral_radius",
-                 "rdt_set_graph_mode", "rdt_recurrent_forward"]:
+                 "rdt_set_graph_mode", "rdt_recurrent_forward", "rdt_profile_forward"]:
         getattr(lib, name).restype = _i32
     _lib = lib
     return lib
@@ -192,6 +198,15 @@ class RecurrentBlock:
                 workspace=None, stream=None):
         """out = h_T. Tensors live on the GPU; aux maps rdt_aux field names to
         preallocated device tensors."""
+        return self._run(False, h0, e, weights, T, out, aux, workspace, stream)[0]
+
+    def profile_forward(self, h0, e, weights: dict, T: int | None = None, out=None, aux: dict | None = None,
+                        workspace=None, stream=None):
+        """Kernel-by-kernel forward with HIP events around every launch.
+        Returns (out, {stage name: (device ms, launches)}); waits for the GPU."""
+        return self._run(True, h0, e, weights, T, out, aux, workspace, stream)
+
+    def _run(self, profile, h0, e, weights, T, out, aux, workspace, stream):
         import torch
         T = int(self.cfg.get("T", 1) if T is None else T)
         if out is None:
@@ -206,6 +221,13 @@ class RecurrentBlock:
         ws = self.workspace(T, h0.device) if workspace is None else workspace
         if stream is None:
             stream = torch.cuda.current_stream(h0.device).cuda_stream
-        _check(self.lib.rdt_recurrent_forward(self.h, _ptr(h0), _ptr(e), ctypes.byref(w), T, _ptr(out),
-                                              ctypes.byref(a), _ptr(ws), ws.numel(), stream))
-        return out
+        if not profile:
+            _check(self.lib.rdt_recurrent_forward(self.h, _ptr(h0), _ptr(e), ctypes.byref(w), T, _ptr(out),
+                                                  ctypes.byref(a), _ptr(ws), ws.numel(), stream))
+            return out, None
+        ms = (_f32 * N_STAGES)()
+        cnt = (_i32 * N_STAGES)()
+        _check(self.lib.rdt_profile_forward(self.h, _ptr(h0), _ptr(e), ctypes.byref(w), T, _ptr(out),
+                                            ctypes.byref(a), _ptr(ws), ws.numel(), stream, ms, cnt, N_STAGES))
+        stages = {self.lib.rdt_stage_name(i).decode(): (float(ms[i]), int(cnt[i])) for i in range(N_STAGES)}
+        return out, stages

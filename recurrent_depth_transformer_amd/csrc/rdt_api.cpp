@@ -146,6 +146,33 @@ struct Fwd {
   char* ws;
 };
 
+// Event pairs around launches (rdt_profile_forward only).
+struct Prof {
+  struct Rec { int stage; hipEvent_t a, b; };
+  std::vector<Rec> recs;
+  int cur = -1;
+  ~Prof() {
+    for (auto& r : recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
+  }
+};
+
+static hipError_t prof_begin(Prof* p, int stage, hipStream_t s) {
+  Prof::Rec r{stage, nullptr, nullptr};
+  hipError_t e = hipEventCreate(&r.a);
+  if (e == hipSuccess) e = hipEventCreate(&r.b);
+  if (e != hipSuccess) return e;
+  p->recs.push_back(r);
+  return hipEventRecord(r.a, s);
+}
+static hipError_t prof_end(Prof* p, hipStream_t s) { return hipEventRecord(p->recs.back().b, s); }
+
+#define LAUNCH(STG, X)                                   \
+  do {                                                   \
+    if (prof) HIPCHK(prof_begin(prof, (STG), s));        \
+    HIPCHK(X);                                           \
+    if (prof) HIPCHK(prof_end(prof, s));                 \
+  } while (0)
+
 template <typename P>
 static P* at(char* ws, size_t off) { return reinterpret_cast<P*>(ws + off); }
 
@@ -163,7 +190,7 @@ static void pick_tile(long long M, long long N, int min_bn, int* bm, int* bn) {
   *bn = 64;
 }
 
-static rdt_status enqueue(const Fwd& f, hipStream_t s) {
+static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   const rdt_config& c = *f.c;
   const Plan& P = f.P;
   char* ws = f.ws;
@@ -171,35 +198,35 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
   const rdt_weights& w = *f.w;
   const bool act = c.act_enabled != 0;
 
-  if (f.out != f.h0) HIPCHK(hipMemcpyAsync(f.out, f.h0, (size_t)N * D * 4, hipMemcpyDeviceToDevice, s));
-  if (f.aux.h_dump) HIPCHK(launch_copy_f32(f.aux.h_dump, f.h0, (long long)N * D, s));
+  if (f.out != f.h0) LAUNCH(RDT_STAGE_OTHER, hipMemcpyAsync(f.out, f.h0, (size_t)N * D * 4, hipMemcpyDeviceToDevice, s));
+  if (f.aux.h_dump) LAUNCH(RDT_STAGE_OTHER, launch_copy_f32(f.aux.h_dump, f.h0, (long long)N * D, s));
   if (f.T == 0) {
-    if (f.aux.loops) HIPCHK(launch_fill_i32(f.aux.loops, 0, N, s));
+    if (f.aux.loops) LAUNCH(RDT_STAGE_OTHER, launch_fill_i32(f.aux.loops, 0, N, s));
     return RDT_OK;
   }
   float* cosb = at<float>(ws, P.cosb);
   float* sinb = at<float>(ws, P.sinb);
-  HIPCHK(launch_rope_tables(cosb, sinb, P.S, P.dr, c.rope_base, s));
-  if (P.mla) HIPCHK(launch_head_transpose(dt, at<char>(ws, P.wukT), w.Wuk, P.H, P.nope, P.kvl, s));
+  LAUNCH(RDT_STAGE_OTHER, launch_rope_tables(cosb, sinb, P.S, P.dr, c.rope_base, s));
+  if (P.mla) LAUNCH(RDT_STAGE_OTHER, launch_head_transpose(dt, at<char>(ws, P.wukT), w.Wuk, P.H, P.nope, P.kvl, s));
 
   int* lists = at<int>(ws, P.lists);
   int* ncount = at<int>(ws, P.ncount);
   int* segs = at<int>(ws, P.seg);
   float* cum = at<float>(ws, P.cum);
   if (act) {
-    HIPCHK(launch_iota(lists, N, ncount, N, segs, P.B, P.S, s));
-    HIPCHK(launch_fill_f32(cum, 0.f, N, s));
+    LAUNCH(RDT_STAGE_OTHER, launch_iota(lists, N, ncount, N, segs, P.B, P.S, s));
+    LAUNCH(RDT_STAGE_OTHER, launch_fill_f32(cum, 0.f, N, s));
   }
   const int k = P.k, E = P.E;
-  if (f.aux.loops) HIPCHK(launch_fill_i32(f.aux.loops, 0, N, s));
-  if (f.aux.route_idx) HIPCHK(launch_fill_i32(f.aux.route_idx, -1, (long long)f.T * N * k, s));
-  if (f.aux.route_gap) HIPCHK(launch_fill_f32(f.aux.route_gap, NAN, (long long)f.T * N, s));
-  if (f.aux.act_cum) HIPCHK(launch_fill_f32(f.aux.act_cum, NAN, (long long)f.T * N, s));
+  if (f.aux.loops) LAUNCH(RDT_STAGE_OTHER, launch_fill_i32(f.aux.loops, 0, N, s));
+  if (f.aux.route_idx) LAUNCH(RDT_STAGE_OTHER, launch_fill_i32(f.aux.route_idx, -1, (long long)f.T * N * k, s));
+  if (f.aux.route_gap) LAUNCH(RDT_STAGE_OTHER, launch_fill_f32(f.aux.route_gap, NAN, (long long)f.T * N, s));
+  if (f.aux.act_cum) LAUNCH(RDT_STAGE_OTHER, launch_fill_f32(f.aux.act_cum, NAN, (long long)f.T * N, s));
   if (act && f.aux.n2_dump) {
-    if (dt == DT_F32) HIPCHK(launch_fill_f32((float*)f.aux.n2_dump, 0.f, (long long)f.T * N * D, s));
-    else HIPCHK(launch_fill_u16((uint16_t*)f.aux.n2_dump, 0, (long long)f.T * N * D, s));
+    if (dt == DT_F32) LAUNCH(RDT_STAGE_OTHER, launch_fill_f32((float*)f.aux.n2_dump, 0.f, (long long)f.T * N * D, s));
+    else LAUNCH(RDT_STAGE_OTHER, launch_fill_u16((uint16_t*)f.aux.n2_dump, 0, (long long)f.T * N * D, s));
   }
-  if (act && f.aux.a_dump) HIPCHK(launch_fill_f32(f.aux.a_dump, 0.f, (long long)f.T * N * D, s));
+  if (act && f.aux.a_dump) LAUNCH(RDT_STAGE_OTHER, launch_fill_f32(f.aux.a_dump, 0.f, (long long)f.T * N * D, s));
 
   char* n1 = at<char>(ws, P.n1);
   char* o = at<char>(ws, P.o);
@@ -230,7 +257,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
     NormArgs n1a{};
     n1a.dtype = dt; n1a.h = f.out; n1a.e = f.e; n1a.a = nullptr; n1a.g = w.g1; n1a.eps = c.norm_eps; n1a.D = D;
     n1a.rows = prev; n1a.ndev = nprev; n1a.n = N; n1a.out = n1; n1a.out_scatter = 1; n1a.dump = nullptr;
-    HIPCHK(launch_norm(n1a, s));
+    LAUNCH(RDT_STAGE_NORM1, launch_norm(n1a, s));
 
     // a2-a4: attention
     if (!P.mla) {
@@ -249,16 +276,16 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
         g.rows = nullptr; g.gather = 0; g.Mdev = nullptr;
         g.nseg = 3; g.seg[0] = sq; g.seg[1] = sk; g.seg[2] = sv;
         pick_tile(N, Hd + 2 * KVd, P.d, &g.bm, &g.bn);
-        HIPCHK(launch_dense_gemm(g, s));
+        LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g, s));
       } else {
         DenseGemm gq = g;
         gq.rows = cur; gq.gather = 1; gq.Mdev = ncur; gq.nseg = 1; gq.seg[0] = sq;
         pick_tile(N, Hd, P.d, &gq.bm, &gq.bn);
-        HIPCHK(launch_dense_gemm(gq, s));
+        LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(gq, s));
         DenseGemm gkv = g;
         gkv.rows = prev; gkv.gather = 1; gkv.Mdev = nprev; gkv.nseg = 2; gkv.seg[0] = sk; gkv.seg[1] = sv;
         pick_tile(N, 2 * KVd, P.d, &gkv.bm, &gkv.bn);
-        HIPCHK(launch_dense_gemm(gkv, s));
+        LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(gkv, s));
       }
       AttnArgs aa{};
       aa.dtype = dt; aa.dqk = P.d; aa.dv = P.d;
@@ -268,7 +295,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
       aa.o = o; aa.o_ld = Hd; aa.o_hs = P.d;
       aa.H = P.H; aa.KV = P.KV; aa.rows = cur; aa.seg = seg; aa.B = P.B; aa.S = P.S;
       aa.scale = 1.f / sqrtf((float)P.d);
-      HIPCHK(launch_attention(aa, s));
+      LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, s));
     } else {
       const int W = P.kvl + P.nr, qw = P.nope + P.nr;
       char* cq_raw = at<char>(ws, P.cq_raw);
@@ -287,20 +314,20 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
       g1.seg[0] = GemmSeg{w.Wdq, P.ql, cq_raw, P.ql, 1, 0, 1};
       g1.seg[1] = GemmSeg{w.Wdkv, W, lat_raw, W, 1, 0, 1};
       pick_tile(N, P.ql + W, 16, &g1.bm, &g1.bn);
-      HIPCHK(launch_dense_gemm(g1, s));
+      LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g1, s));
       MlaNormArgs mn{};
       mn.dtype = dt; mn.cq_raw = (const float*)cq_raw; mn.ql = P.ql; mn.lat_raw = (const float*)lat_raw;
       mn.kvl = P.kvl; mn.nr = P.nr; mn.gq = w.gq; mn.gkv = w.gkv; mn.eps = c.norm_eps;
       mn.rows = prev; mn.ndev = nprev; mn.n = N; mn.cqn = cqn; mn.latent = latent;
       mn.cosb = cosb; mn.sinb = sinb; mn.S = P.S;
-      HIPCHK(launch_mla_norm(mn, s));
+      LAUNCH(RDT_STAGE_QKV, launch_mla_norm(mn, s));
       // query up-projection (compacted rows)
       DenseGemm g2{};
       g2.dtype = dt; g2.A = cqn; g2.lda = P.ql; g2.K = P.ql; g2.batch = 1; g2.epi = EPI_STORE;
       g2.rows = cur; g2.gather = act ? 1 : 0; g2.M = N; g2.Mdev = ncur;
       g2.nseg = 1; g2.seg[0] = GemmSeg{w.Wuq, P.H * qw, qfull, P.H * qw, 0, 0, 0};
       pick_tile(N, P.H * qw, 16, &g2.bm, &g2.bn);
-      HIPCHK(launch_dense_gemm(g2, s));
+      LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g2, s));
       // absorb: q_lat[h] = q_nope[h] . Wuk[h]  (per head, B = Wuk[h]^T)
       DenseGemm g3{};
       g3.dtype = dt; g3.A = qfull; g3.lda = P.H * qw; g3.a_bstride = qw; g3.K = P.nope; g3.epi = EPI_STORE;
@@ -308,13 +335,13 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
       g3.nseg = 1; g3.seg[0] = GemmSeg{wukT, P.kvl, qattn, P.H * W, 0, 0, 0};
       g3.b_bstride = (long long)P.kvl * P.nope; g3.c_bstride = W;
       pick_tile(N, (long long)P.kvl * P.H, 16, &g3.bm, &g3.bn);
-      HIPCHK(launch_dense_gemm(g3, s));
+      LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g3, s));
       QRopeArgs qr{};
       qr.dtype = dt; qr.src = qfull; qr.src_ld = P.H * qw; qr.src_hs = qw; qr.src_off = P.nope;
       qr.dst = qattn; qr.dst_ld = P.H * W; qr.dst_hs = W; qr.dst_off = P.kvl;
       qr.H = P.H; qr.nr = P.nr; qr.rows = cur; qr.ndev = ncur; qr.n = N;
       qr.cosb = cosb; qr.sinb = sinb; qr.S = P.S;
-      HIPCHK(launch_qrope(qr, s));
+      LAUNCH(RDT_STAGE_QKV, launch_qrope(qr, s));
       AttnArgs aa{};
       aa.dtype = dt; aa.dqk = W; aa.dv = P.kvl;
       aa.q = qattn; aa.q_ld = P.H * W; aa.q_hs = W;
@@ -323,7 +350,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
       aa.o = olat; aa.o_ld = P.H * P.kvl; aa.o_hs = P.kvl;
       aa.H = P.H; aa.KV = 1; aa.rows = cur; aa.seg = seg; aa.B = P.B; aa.S = P.S;
       aa.scale = 1.f / sqrtf((float)(P.nope + P.nr));
-      HIPCHK(launch_attention(aa, s));
+      LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, s));
       // value up-projection per head: o[h] = o_lat[h] . Wuv[h]^T
       DenseGemm g4{};
       g4.dtype = dt; g4.A = olat; g4.lda = P.H * P.kvl; g4.a_bstride = P.kvl; g4.K = P.kvl; g4.epi = EPI_STORE;
@@ -331,7 +358,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
       g4.nseg = 1; g4.seg[0] = GemmSeg{w.Wuv, P.vd, o, P.hv, 0, 0, 0};
       g4.b_bstride = (long long)P.vd * P.kvl; g4.c_bstride = P.vd;
       pick_tile(N, (long long)P.vd * P.H, 16, &g4.bm, &g4.bn);
-      HIPCHK(launch_dense_gemm(g4, s));
+      LAUNCH(RDT_STAGE_ATTN, launch_dense_gemm(g4, s));
     }
 
     // a5: output projection (+ depth-wise LoRA as a second K phase)
@@ -344,7 +371,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
       gz.seg[0] = GemmSeg{elt_ptr(w.lora_down, (long long)tl * P.r * P.hv, elt), P.r, z, P.r, 0, 0, 0};
       gz.bm = 128; gz.bn = 64;
       if ((N + 127) / 128 < 256) gz.bm = 64;
-      HIPCHK(launch_dense_gemm(gz, s));
+      LAUNCH(RDT_STAGE_OPROJ, launch_dense_gemm(gz, s));
     }
     DenseGemm go{};
     go.dtype = dt; go.A = o; go.lda = P.hv; go.K = P.hv; go.batch = 1; go.epi = EPI_STORE;
@@ -354,14 +381,14 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
       go.A2 = z; go.lda2 = P.r; go.B2 = elt_ptr(w.lora_up, (long long)tl * D * P.r, elt); go.K2 = P.r;
     }
     pick_tile(N, D, 16, &go.bm, &go.bn);
-    HIPCHK(launch_dense_gemm(go, s));
+    LAUNCH(RDT_STAGE_OPROJ, launch_dense_gemm(go, s));
 
     // a5: x = u + a, n2 = RMSNorm(x) * g2 (compacted rows)
     NormArgs n2a{};
     n2a.dtype = dt; n2a.h = f.out; n2a.e = f.e; n2a.a = abuf; n2a.g = w.g2; n2a.eps = c.norm_eps; n2a.D = D;
     n2a.rows = cur; n2a.ndev = ncur; n2a.n = N; n2a.out = n2; n2a.out_scatter = 0;
     n2a.dump = f.aux.n2_dump ? (void*)elt_ptr(f.aux.n2_dump, (long long)t * N * D, elt) : nullptr;
-    HIPCHK(launch_norm(n2a, s));
+    LAUNCH(RDT_STAGE_NORM2, launch_norm(n2a, s));
 
     // a6: router GEMM with softmax / top-k epilogue, then the stable permutation
     DenseGemm gr{};
@@ -375,14 +402,14 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
     gr.router.E = E; gr.router.k = k; gr.router.idx = idx; gr.router.gates = gates; gr.router.gap = gap;
     gr.router.dump_idx = f.aux.route_idx ? f.aux.route_idx + (size_t)t * N * k : nullptr;
     gr.router.dump_gap = f.aux.route_gap ? f.aux.route_gap + (size_t)t * N : nullptr;
-    HIPCHK(launch_dense_gemm(gr, s));
+    LAUNCH(RDT_STAGE_ROUTER, launch_dense_gemm(gr, s));
 
     PermuteArgs pa{};
     pa.idx = idx; pa.ndev = ncur; pa.n_static = N; pa.E = E; pa.Se = P.Se; pa.k = k;
     pa.counts = counts; pa.offs = offs; pa.perm = perm; pa.inv = inv;
     pa.ts_gu = ts_gu; pa.bm_gu = GU_BM; pa.ts_dn = ts_dn; pa.bm_dn = DN_BM;
     pa.counts_dump = f.aux.expert_counts ? f.aux.expert_counts + (size_t)t * E : nullptr;
-    HIPCHK(launch_permute(pa, s));
+    LAUNCH(RDT_STAGE_PERMUTE, launch_permute(pa, s));
 
     // a7: grouped SwiGLU experts
     GroupedGemm gu{};
@@ -390,13 +417,13 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
     gu.perm = perm; gu.offs = offs; gu.counts = counts; gu.tile_start = ts_gu; gu.ndev = ncur; gu.n_static = N;
     gu.E = E; gu.Se = P.Se; gu.k = k; gu.W1 = w.Wg; gu.W2 = w.Wu; gu.S1 = w.Wsg; gu.S2 = w.Wsu;
     gu.N = P.F; gu.K = D; gu.C = hmid; gu.ldc = P.F; gu.max_mtiles = P.gu_max_mtiles;
-    HIPCHK(launch_grouped_gemm(gu, s));
+    LAUNCH(RDT_STAGE_EXPERT_GU, launch_grouped_gemm(gu, s));
     GroupedGemm gd{};
     gd.dtype = dt; gd.kind = 1; gd.A = hmid; gd.lda = P.F;
     gd.perm = perm; gd.offs = offs; gd.counts = counts; gd.tile_start = ts_dn; gd.ndev = ncur; gd.n_static = N;
     gd.E = E; gd.Se = P.Se; gd.k = k; gd.W1 = w.Wd; gd.W2 = nullptr; gd.S1 = w.Wsd; gd.S2 = nullptr;
     gd.N = D; gd.K = P.F; gd.C = ybuf; gd.ldc = D; gd.max_mtiles = P.dn_max_mtiles;
-    HIPCHK(launch_grouped_gemm(gd, s));
+    LAUNCH(RDT_STAGE_EXPERT_DOWN, launch_grouped_gemm(gd, s));
 
     // a8: combine + LTI injection (+ ACT)
     CombineArgs ca{};
@@ -406,15 +433,15 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s) {
     ca.act = act; ca.w_halt = w.w_halt; ca.thr = c.act_threshold; ca.cum = cum; ca.loops = f.aux.loops; ca.t = t;
     ca.cum_dump = f.aux.act_cum ? f.aux.act_cum + (size_t)t * N : nullptr;
     ca.a_dump = f.aux.a_dump ? f.aux.a_dump + (size_t)t * N * D : nullptr;
-    HIPCHK(launch_combine(ca, s));
+    LAUNCH(RDT_STAGE_COMBINE, launch_combine(ca, s));
     if (act) {
       CompactArgs cp{};
       cp.rows_in = cur; cp.n_in = ncur; cp.cum = cum; cp.thr = c.act_threshold;
       cp.rows_out = lists + (size_t)(t + 1) * N; cp.n_out = ncount + t + 1;
       cp.seg_out = segs + (size_t)(t + 1) * (P.B + 1); cp.B = P.B; cp.S = P.S;
-      HIPCHK(launch_compact(cp, s));
+      LAUNCH(RDT_STAGE_COMPACT, launch_compact(cp, s));
     }
-    if (f.aux.h_dump) HIPCHK(launch_copy_f32(f.aux.h_dump + (size_t)(t + 1) * N * D, f.out, (long long)N * D, s));
+    if (f.aux.h_dump) LAUNCH(RDT_STAGE_OTHER, launch_copy_f32(f.aux.h_dump + (size_t)(t + 1) * N * D, f.out, (long long)N * D, s));
   }
   return RDT_OK;
 }
@@ -463,9 +490,9 @@ static rdt_status check_rho(rdt_handle* h, const float* A, hipStream_t s) {
   return RDT_OK;
 }
 
-extern "C" rdt_status rdt_recurrent_forward(rdt_handle* h, const float* h0, const float* e, const rdt_weights* w,
-                                            int32_t T, float* out, const rdt_aux* aux, void* ws, size_t ws_bytes,
-                                            void* stream) {
+// Argument checks shared by the forward entry points; fills *f.
+static rdt_status prepare(rdt_handle* h, const float* h0, const float* e, const rdt_weights* w, int32_t T,
+                          float* out, const rdt_aux* aux, void* ws, size_t ws_bytes, Fwd& f) {
   if (!h) return set_err(RDT_E_INVALID, "null handle");
   const rdt_config& c = h->cfg;
   if (T < 0 || T > c.max_T) return set_err(RDT_E_INVALID, "T must be in [0, max_T]");
@@ -482,13 +509,55 @@ extern "C" rdt_status rdt_recurrent_forward(rdt_handle* h, const float* h0, cons
   if (overlap(out, e)) return set_err(RDT_E_INVALID, "out overlaps e");
   rdt_status st = check_weights(c, w);
   if (st != RDT_OK) return st;
-  Fwd f{};
-  f.c = &c;
+  f = Fwd{};
+  f.c = &h->cfg;
   f.P = make_plan(c, T);
   if (!ws || ws_bytes < f.P.total) return set_err(RDT_E_WORKSPACE, "workspace missing or too small");
   if (misaligned(ws, 256)) return set_err(RDT_E_INVALID, "workspace must be 256-byte aligned");
   f.h0 = h0; f.e = e; f.w = w; f.T = T; f.out = out; f.ws = (char*)ws;
   if (aux) f.aux = *aux;
+  return RDT_OK;
+}
+
+static const char* kStageNames[RDT_N_STAGES] = {"norm1", "qkv", "attention", "out_proj", "norm2", "router",
+                                                "permute", "expert_gate_up", "expert_down", "combine",
+                                                "compact", "other"};
+
+extern "C" const char* rdt_stage_name(int32_t stage) {
+  return (stage >= 0 && stage < RDT_N_STAGES) ? kStageNames[stage] : "";
+}
+
+extern "C" rdt_status rdt_profile_forward(rdt_handle* h, const float* h0, const float* e, const rdt_weights* w,
+                                          int32_t T, float* out, const rdt_aux* aux, void* ws, size_t ws_bytes,
+                                          void* stream, float* stage_ms, int32_t* stage_launches, int32_t n_stages) {
+  if (!stage_ms || !stage_launches || n_stages < RDT_N_STAGES)
+    return set_err(RDT_E_INVALID, "rdt_profile_forward: stage arrays missing or too short");
+  Fwd f;
+  rdt_status st = prepare(h, h0, e, w, T, out, aux, ws, ws_bytes, f);
+  if (st != RDT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  st = check_rho(h, w->A, s);
+  if (st != RDT_OK) return st;
+  Prof prof;
+  st = enqueue(f, s, &prof);
+  HIPCHK(hipStreamSynchronize(s));
+  if (st != RDT_OK) return st;
+  for (int i = 0; i < n_stages; ++i) { stage_ms[i] = 0.f; stage_launches[i] = 0; }
+  for (auto& r : prof.recs) {
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, r.a, r.b));
+    stage_ms[r.stage] += ms;
+    stage_launches[r.stage] += 1;
+  }
+  return RDT_OK;
+}
+
+extern "C" rdt_status rdt_recurrent_forward(rdt_handle* h, const float* h0, const float* e, const rdt_weights* w,
+                                            int32_t T, float* out, const rdt_aux* aux, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  Fwd f;
+  rdt_status st = prepare(h, h0, e, w, T, out, aux, ws, ws_bytes, f);
+  if (st != RDT_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   st = check_rho(h, w->A, s);
   if (st != RDT_OK) return st;

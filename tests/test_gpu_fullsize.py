@@ -1,0 +1,69 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py times
+(graph mode, same shapes). The oracle checks every loop's routing on all rows
+(teacher-forced on the GPU's router input) and, on sampled rows, the loop
+update h_t -> h_{t+1} from the GPU's own state dumps."""
+import numpy as np
+import pytest
+
+from oracle import rdt_oracle as ro
+from rdt_inputs import get_config
+
+from rdt_gpu_run import check_routing_teacher_forced, rms, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _loops_to_check(T):
+    return sorted({0, T // 2, T - 1})
+
+
+@pytest.mark.parametrize("name", ["gqa", "mla", "wide_moe", "act"])
+def test_fullsize(name):
+    cfg = get_config(name)
+    T = cfg["T"]
+    N = cfg["batch"] * cfg["seq"]
+    print(f"[fullsize] {name}: running the GPU forward with dumps", flush=True)
+    res, inp, *_ = run_gpu(cfg, T=T)
+    assert np.all(np.isfinite(res["h"]))
+    mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro)
+    print(f"[fullsize] {name}: routing mismatches={mism} near_ties={near} compared={comp}", flush=True)
+    assert mism == 0
+    rng = np.random.default_rng(123)
+    d_r = cfg["head_dim"] if cfg["attn"] == "gqa" else cfg["qk_rope_head_dim"]
+    tables = ro.rope_tables(cfg["seq"], d_r, cfg["rope_base"])
+    worst = 0.0
+    for t in _loops_to_check(T):
+        active = np.nonzero(res["loops"] > t)[0]
+        if active.size == 0:
+            continue
+        ends = [b * cfg["seq"] + cfg["seq"] - 1 for b in range(cfg["batch"])]
+        pick = np.concatenate([rng.choice(active, size=min(40, active.size), replace=False),
+                               np.intersect1d(ends, active)])
+        rows = np.unique(pick)
+        hn, a, _ = ro.step_rows(cfg, inp, res["h_dump"][t], inp["e"], t, rows, res["route_idx"][t][rows],
+                                tables=tables)
+        err = np.max(np.abs(res["h_dump"][t + 1][rows] - hn))
+        scale = rms(res["h_dump"][t + 1][active])
+        aerr = np.max(np.abs(res["a_dump"][t][rows] - a)) / max(rms(a), 1e-30)
+        worst = max(worst, err / scale)
+        print(f"[fullsize] {name} loop {t}: rows={rows.size} max|dh|/rms={err / scale:.3e} "
+              f"attn-branch rel={aerr:.3e} active={active.size}", flush=True)
+        assert err <= TOL * scale
+    if cfg["act"]:
+        assert res["loops"].min() >= 1 and res["loops"].max() <= T
+        print(f"[fullsize] act: executed token-loops={int(res['loops'].sum())} of {N * T}, "
+              f"mean depth {res['loops'].mean():.2f}", flush=True)
+    if name == "gqa":  # small enough for a full float64 forward with routing forced
+        ref = ro.forward(cfg, inp, T=T, forced_idx=res["route_idx"])
+        err = np.max(np.abs(res["h"] - ref["h"]))
+        print(f"[fullsize] gqa end-to-end max|dh|/rms={err / rms(ref['h']):.3e}", flush=True)
+        assert err <= TOL * rms(ref["h"])

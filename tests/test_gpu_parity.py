@@ -71,6 +71,8 @@ def test_end_to_end_forced(name):
             cum[act_rows] = (cum[act_rows] + (1 / (1 + np.exp(-z))).astype(np.float32)).astype(np.float32)
             halt_o = cum[act_rows] >= thr
             halt_g = res["loops"][act_rows] == t + 1
+            if t == T - 1:  # loops == T also means the token ran out of loops
+                halt_g = halt_g & (res["act_cum"][t][act_rows] >= thr)
             clear = np.abs(cum[act_rows] - thr) >= 1e-3
             bad += int(np.sum((halt_o != halt_g) & clear))
             np.testing.assert_allclose(res["act_cum"][t][act_rows], cum[act_rows], rtol=1e-4, atol=1e-4)

@@ -468,3 +468,23 @@ def test_mla_explicit_equals_absorbed_numpy():
         olat = torch.einsum("hqk,kc->qhc", P, ckv[sl])
         out[sl] = torch.einsum("qhc,hvc->qhv", olat, t(W["Wuv"]).view(H, vd, kvl))
     np.testing.assert_allclose(o, out.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mla_small", "act_small", "wide_small"])
+def test_step_rows_matches_block_step(name):
+    cfg, W = _tiny(name)
+    if cfg["batch"] * cfg["seq"] > 64:
+        cfg.update(batch=2, seq=20)
+        W["e"], W["h0"] = W["e"][:40], W["h0"][:40]
+    N = cfg["batch"] * cfg["seq"]
+    rng = np.random.default_rng(11)
+    h = W["h0"].astype(np.float64) + 0.3 * rng.standard_normal(W["h0"].shape)
+    t = 1
+    full = ro.block_step(cfg, W, h, W["e"], t, np.ones(N, bool))
+    rows = np.unique(np.minimum([0, 3, cfg["seq"] - 1, N - 1, cfg["seq"] + 2], N - 1))
+    hn, a, n2 = ro.step_rows(cfg, W, h, W["e"], t, rows, full["idx"][rows])
+    ref = np.asarray(W["A"], np.float64) * h[rows] + np.asarray(W["B"], np.float64) * W["e"][rows] \
+        + full["a"][rows] + full["m"][rows]
+    np.testing.assert_allclose(a, full["a"][rows], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(n2, full["n2"][rows], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(hn, ref, rtol=1e-11, atol=1e-12)
