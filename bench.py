@@ -144,7 +144,19 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also print the per-stage breakdown to stderr")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (calibrates HBM counters) and exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        x = torch.empty(args.copy_probe // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 3}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
