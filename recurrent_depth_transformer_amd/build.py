@@ -22,6 +22,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # keep hipcc from forming packed fp32 instructions on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs (gfx950 has one unified register file): AGPR
+    # accumulators made the compiler copy them around every loop iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-result",
 ]

@@ -407,7 +407,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     PermuteArgs pa{};
     pa.idx = idx; pa.ndev = ncur; pa.n_static = N; pa.E = E; pa.Se = P.Se; pa.k = k;
     pa.counts = counts; pa.offs = offs; pa.perm = perm; pa.inv = inv;
-    pa.ts_gu = ts_gu; pa.bm_gu = GU_BM; pa.ts_dn = ts_dn; pa.bm_dn = DN_BM;
+    pa.ts_gu = ts_gu; pa.bm_gu = GU_BM; pa.ts_dn = ts_dn; pa.bm_dn = ((long long)N * k / E >= 256 && dt == DT_BF16) ? 128 : 64;
     pa.counts_dump = f.aux.expert_counts ? f.aux.expert_counts + (size_t)t * E : nullptr;
     LAUNCH(RDT_STAGE_PERMUTE, launch_permute(pa, s));
 
@@ -417,12 +417,16 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     gu.perm = perm; gu.offs = offs; gu.counts = counts; gu.tile_start = ts_gu; gu.ndev = ncur; gu.n_static = N;
     gu.E = E; gu.Se = P.Se; gu.k = k; gu.W1 = w.Wg; gu.W2 = w.Wu; gu.S1 = w.Wsg; gu.S2 = w.Wsu;
     gu.N = P.F; gu.K = D; gu.C = hmid; gu.ldc = P.F; gu.max_mtiles = P.gu_max_mtiles;
+    gu.bm = GU_BM; gu.bn = GU_BN; gu.ns = 2;
     LAUNCH(RDT_STAGE_EXPERT_GU, launch_grouped_gemm(gu, s));
     GroupedGemm gd{};
     gd.dtype = dt; gd.kind = 1; gd.A = hmid; gd.lda = P.F;
     gd.perm = perm; gd.offs = offs; gd.counts = counts; gd.tile_start = ts_dn; gd.ndev = ncur; gd.n_static = N;
     gd.E = E; gd.Se = P.Se; gd.k = k; gd.W1 = w.Wd; gd.W2 = nullptr; gd.S1 = w.Wsd; gd.S2 = nullptr;
     gd.N = D; gd.K = P.F; gd.C = ybuf; gd.ldc = D; gd.max_mtiles = P.dn_max_mtiles;
+    // many rows per expert: large tiles; few rows: small tiles, deeper ring
+    if ((long long)N * k / E >= 256 && dt == DT_BF16) { gd.bm = 128; gd.bn = 128; gd.ns = 2; }
+    else { gd.bm = 64; gd.bn = 64; gd.ns = 4; }
     LAUNCH(RDT_STAGE_EXPERT_DOWN, launch_grouped_gemm(gd, s));
 
     // a8: combine + LTI injection (+ ACT)

@@ -1,10 +1,11 @@
 // Causal flash attention for grouped-query and absorbed multi-latent attention.
 //
-// A workgroup owns one sequence b, one tile of QW query rows of that sequence
-// (rows of the compacted active list when ACT is on) and NW query heads that
-// read the same kv head. Key/value tiles of 64 positions are staged once in
-// LDS and shared by the NW waves; each wave keeps its head's queries in
-// registers and runs an online softmax in fp32.
+// A 256-thread workgroup (4 waves) owns one sequence b, NHB query heads that
+// read the same kv head, and 4/NHB consecutive slices of QW query rows (rows of
+// the compacted active list when ACT is on). Wave w handles head w % NHB and
+// slice w / NHB. Key/value tiles of 64 positions are shared by all four waves:
+// they are double-buffered in LDS and the next tile's global loads are in
+// flight while the current tile is multiplied.
 //
 // The scores are formed transposed, S^T = K Q^T, so that a lane holds four
 // consecutive keys of one query: that is exactly the k-slot layout the second
@@ -21,8 +22,8 @@ namespace rdt {
 
 constexpr int KT = 64;  // keys per tile
 
-template <typename T, int DQK, int DV, int QW>
-__global__ __launch_bounds__(512) void k_attention(AttnArgs a) {
+template <typename T, int DQK, int DV, int QW, int NHB>
+__global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   constexpr int DQKP = (DQK + 31) / 32 * 32;
   constexpr int KS = DQKP / 32;
   constexpr int QS = QW / 16;
@@ -30,24 +31,33 @@ __global__ __launch_bounds__(512) void k_attention(AttnArgs a) {
   constexpr int VEC = ST<T>::VEC;
   constexpr int KLD = DQKP + VEC;
   constexpr int VLD = KT + (sizeof(T) == 2 ? 8 : 4);
-  __shared__ __align__(16) T Ks[KT * KLD];
-  __shared__ __align__(16) T Vt[DV * VLD];
+  constexpr int SLICES = 4 / NHB;
+  constexpr int BQ = QW * SLICES;  // query rows per workgroup (per head)
+  // per-thread share of one K tile and one V tile (256 threads)
+  constexpr int KV_VECS = KT * (DQKP / VEC);
+  constexpr int KL = (KV_VECS + 255) / 256;
+  constexpr int VV = sizeof(T) == 2 ? (KT / 2) * (DV / 8) : KT * (DV / 4);
+  constexpr int VL = (VV + 255) / 256;
+  __shared__ __align__(16) T Ks[2][KT * KLD];
+  __shared__ __align__(16) T Vt[2][DV * VLD];
 
-  const int NW = blockDim.x >> 6;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lg = lane >> 4, lc = lane & 15;
   const int b = blockIdx.y;
   const int qt = gridDim.x - 1 - blockIdx.x;  // long (late) query tiles first
-  const int h = blockIdx.z * NW + wave;
+  const int h = blockIdx.z * NHB + (wave % NHB);
+  const int slice = wave / NHB;
   const int kvh = (h * a.KV) / a.H;
   const int S = a.S;
   const int seg0 = a.seg ? a.seg[b] : b * S;
   const int seglen = a.seg ? a.seg[b + 1] - seg0 : S;
-  if (qt * QW >= seglen) return;
-  const int qfirst = seg0 + qt * QW;
-  const int nq = min(QW, seglen - qt * QW);
-  const int last = qfirst + nq - 1;
+  if (qt * BQ >= seglen) return;
+  const int blk_first = seg0 + qt * BQ;
+  const int blk_n = min(BQ, seglen - qt * BQ);
+  const int last = blk_first + blk_n - 1;
   const int kmax = (a.rows ? a.rows[last] : last) - b * S + 1;  // keys 0..kmax-1
+  const int qfirst = blk_first + slice * QW;
+  const int nq = max(0, min(QW, blk_n - slice * QW));  // this wave's query rows
 
   const T* Q = reinterpret_cast<const T*>(a.q);
   const T* Kg = reinterpret_cast<const T*>(a.k);
@@ -82,144 +92,173 @@ __global__ __launch_bounds__(512) void k_attention(AttnArgs a) {
     for (int ds = 0; ds < DS; ++ds) oacc[ds][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sc = a.scale * 1.4426950408889634f;  // exp2 domain
-  const uint4 zero = make_uint4(0, 0, 0, 0);
   const int nkt = (kmax + KT - 1) / KT;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * KT;
-    // K tile [KT][DQKP]
-    for (int v = tid; v < KT * (DQKP / VEC); v += blockDim.x) {
+  // ---- K/V tile: global -> registers -> LDS (V transposed)
+  uint4 rk[KL], rv0[VL], rv1[VL];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < KL; ++u) {
+      const int v = tid + u * 256;
       const int kr = v / (DQKP / VEC), kc = (v % (DQKP / VEC)) * VEC;
       const int key = k0 + kr;
-      uint4 val = zero;
-      if (key < kmax && kc < DQK)
-        val = *reinterpret_cast<const uint4*>(Kg + (tokbase + key) * a.k_ld + (long long)kvh * a.k_hs + kc);
-      *reinterpret_cast<uint4*>(Ks + kr * KLD + kc) = val;
+      rk[u] = (v < KV_VECS && key < kmax && kc < DQK)
+                  ? *reinterpret_cast<const uint4*>(Kg + (tokbase + key) * a.k_ld + (long long)kvh * a.k_hs + kc)
+                  : make_uint4(0, 0, 0, 0);
     }
-    // V tile, transposed into Vt[DV][KT]
-    if constexpr (sizeof(T) == 2) {
-      for (int v = tid; v < (KT / 2) * (DV / 8); v += blockDim.x) {
+#pragma unroll
+    for (int u = 0; u < VL; ++u) {
+      const int v = tid + u * 256;
+      if constexpr (sizeof(T) == 2) {
         const int kp = v / (DV / 8), dc = (v % (DV / 8)) * 8;
         const int key = k0 + 2 * kp;
         const T* src = Vg + (tokbase + key) * a.v_ld + (long long)kvh * a.v_hs + dc;
-        uint4 v0 = zero, v1 = zero;
-        if (key < kmax) v0 = *reinterpret_cast<const uint4*>(src);
-        if (key + 1 < kmax) v1 = *reinterpret_cast<const uint4*>(src + a.v_ld);
-        const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&v0);
-        const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&v1);
+        rv0[u] = (v < VV && key < kmax) ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+        rv1[u] = (v < VV && key + 1 < kmax) ? *reinterpret_cast<const uint4*>(src + a.v_ld) : make_uint4(0, 0, 0, 0);
+      } else {
+        const int kr = v / (DV / 4), dc = (v % (DV / 4)) * 4;
+        const int key = k0 + kr;
+        rv0[u] = (v < VV && key < kmax)
+                     ? *reinterpret_cast<const uint4*>(Vg + (tokbase + key) * a.v_ld + (long long)kvh * a.v_hs + dc)
+                     : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < KL; ++u) {
+      const int v = tid + u * 256;
+      if (v < KV_VECS) {
+        const int kr = v / (DQKP / VEC), kc = (v % (DQKP / VEC)) * VEC;
+        *reinterpret_cast<uint4*>(&Ks[buf][kr * KLD + kc]) = rk[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VL; ++u) {
+      const int v = tid + u * 256;
+      if (v >= VV) continue;
+      if constexpr (sizeof(T) == 2) {
+        const int kp = v / (DV / 8), dc = (v % (DV / 8)) * 8;
+        const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&rv0[u]);
+        const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&rv1[u]);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const uint32_t lo = (p0[x] & 0xffffu) | (p1[x] << 16);
           const uint32_t hi = (p0[x] >> 16) | (p1[x] & 0xffff0000u);
-          *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * x) * VLD + 2 * kp) = lo;
-          *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * x + 1) * VLD + 2 * kp) = hi;
+          *reinterpret_cast<uint32_t*>(&Vt[buf][(dc + 2 * x) * VLD + 2 * kp]) = lo;
+          *reinterpret_cast<uint32_t*>(&Vt[buf][(dc + 2 * x + 1) * VLD + 2 * kp]) = hi;
         }
-      }
-    } else {
-      for (int v = tid; v < KT * (DV / 4); v += blockDim.x) {
+      } else {
         const int kr = v / (DV / 4), dc = (v % (DV / 4)) * 4;
-        const int key = k0 + kr;
-        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (key < kmax)
-          val = *reinterpret_cast<const float4*>(Vg + (tokbase + key) * a.v_ld + (long long)kvh * a.v_hs + dc);
-        Vt[(dc + 0) * VLD + kr] = val.x;
-        Vt[(dc + 1) * VLD + kr] = val.y;
-        Vt[(dc + 2) * VLD + kr] = val.z;
-        Vt[(dc + 3) * VLD + kr] = val.w;
+        const float* f = reinterpret_cast<const float*>(&rv0[u]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) Vt[buf][(dc + x) * VLD + kr] = f[x];
       }
     }
-    __syncthreads();
+  };
 
-    // S^T[key][query] for 4 blocks of 16 keys
-    f32x4 s[4][QS];
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    const int k0 = kt * KT;
+    if (kt + 1 < nkt) gload(k0 + KT);  // next tile in flight during this one
+    if (nq > 0) {
+      const T* Kb = Ks[buf];
+      const T* Vb = Vt[buf];
+      // S^T[key][query] for 4 blocks of 16 keys
+      f32x4 s[4][QS];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-      for (int qs = 0; qs < QS; ++qs) s[kb][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qs = 0; qs < QS; ++qs) s[kb][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const Frag<T> kf = frag_lds<T>(Ks + (kb * 16 + lc) * KLD + ks * 32 + lg * 8);
+        for (int ks = 0; ks < KS; ++ks) {
+          const Frag<T> kf = frag_lds<T>(Kb + (kb * 16 + lc) * KLD + ks * 32 + lg * 8);
 #pragma unroll
-        for (int qs = 0; qs < QS; ++qs) mma(s[kb][qs], kf, qf[qs][ks]);
-      }
-    }
-    // scale, causal mask, online softmax (per query = per lane column)
-#pragma unroll
-    for (int qs = 0; qs < QS; ++qs) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kp = k0 + kb * 16 + lg * 4 + r;
-          float x = s[kb][qs][r] * sc;
-          if (kp > qpos[qs] || kp >= kmax) x = -INFINITY;
-          s[kb][qs][r] = x;
-          mx = fmaxf(mx, x);
+          for (int qs = 0; qs < QS; ++qs) mma(s[kb][qs], kf, qf[qs][ks]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrow[qs], mx);
-      const float base = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(mrow[qs] - base);
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(s[kb][qs][r] - base);
-          s[kb][qs][r] = p;
-          rs += p;
-        }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
-      lrow[qs] = lrow[qs] * alpha + rs;
-      mrow[qs] = mnew;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        oacc[ds][qs][0] *= alpha;
-        oacc[ds][qs][1] *= alpha;
-        oacc[ds][qs][2] *= alpha;
-        oacc[ds][qs][3] *= alpha;
       }
-    }
-    // O^T += V^T P^T, two 32-key chunks; k-slot order: 4 keys of block 2c then 4 of 2c+1
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      Frag<T> pf[QS];
+      // scale, causal mask, online softmax (per query = per lane column)
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) {
-        if constexpr (sizeof(T) == 2) {
-          uint4 u;
-          u.x = (uint32_t)f2bf(s[2 * c][qs][0]) | ((uint32_t)f2bf(s[2 * c][qs][1]) << 16);
-          u.y = (uint32_t)f2bf(s[2 * c][qs][2]) | ((uint32_t)f2bf(s[2 * c][qs][3]) << 16);
-          u.z = (uint32_t)f2bf(s[2 * c + 1][qs][0]) | ((uint32_t)f2bf(s[2 * c + 1][qs][1]) << 16);
-          u.w = (uint32_t)f2bf(s[2 * c + 1][qs][2]) | ((uint32_t)f2bf(s[2 * c + 1][qs][3]) << 16);
-          pf[qs].v[0] = u;
-        } else {
-          pf[qs].v[0] = make_uint4(__float_as_uint(s[2 * c][qs][0]), __float_as_uint(s[2 * c][qs][1]),
-                                   __float_as_uint(s[2 * c][qs][2]), __float_as_uint(s[2 * c][qs][3]));
-          pf[qs].v[sizeof(T) / 2 - 1] =
-              make_uint4(__float_as_uint(s[2 * c + 1][qs][0]), __float_as_uint(s[2 * c + 1][qs][1]),
-                         __float_as_uint(s[2 * c + 1][qs][2]), __float_as_uint(s[2 * c + 1][qs][3]));
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kp = k0 + kb * 16 + lg * 4 + r;
+            float x = s[kb][qs][r] * sc;
+            if (kp > qpos[qs] || kp >= kmax) x = -INFINITY;
+            s[kb][qs][r] = x;
+            mx = fmaxf(mx, x);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(mrow[qs], mx);
+        const float base = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = exp2f(mrow[qs] - base);
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = exp2f(s[kb][qs][r] - base);
+            s[kb][qs][r] = p;
+            rs += p;
+          }
+        rs += __shfl_xor(rs, 16, 64);
+        rs += __shfl_xor(rs, 32, 64);
+        lrow[qs] = lrow[qs] * alpha + rs;
+        mrow[qs] = mnew;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          oacc[ds][qs][0] *= alpha;
+          oacc[ds][qs][1] *= alpha;
+          oacc[ds][qs][2] *= alpha;
+          oacc[ds][qs][3] *= alpha;
         }
       }
+      // O^T += V^T P^T, two 32-key chunks; k-slot order: 4 keys of block 2c then 4 of 2c+1
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const T* vrow = Vt + (ds * 16 + lc) * VLD + 32 * c + lg * 4;
-        Frag<T> vf;
-        if constexpr (sizeof(T) == 2) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-          vf.v[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        } else {
-          vf.v[0] = *reinterpret_cast<const uint4*>(vrow);
-          vf.v[sizeof(T) / 2 - 1] = *reinterpret_cast<const uint4*>(vrow + 16);
+      for (int c = 0; c < 2; ++c) {
+        Frag<T> pf[QS];
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) {
+          if constexpr (sizeof(T) == 2) {
+            uint4 u;
+            u.x = (uint32_t)f2bf(s[2 * c][qs][0]) | ((uint32_t)f2bf(s[2 * c][qs][1]) << 16);
+            u.y = (uint32_t)f2bf(s[2 * c][qs][2]) | ((uint32_t)f2bf(s[2 * c][qs][3]) << 16);
+            u.z = (uint32_t)f2bf(s[2 * c + 1][qs][0]) | ((uint32_t)f2bf(s[2 * c + 1][qs][1]) << 16);
+            u.w = (uint32_t)f2bf(s[2 * c + 1][qs][2]) | ((uint32_t)f2bf(s[2 * c + 1][qs][3]) << 16);
+            pf[qs].v[0] = u;
+          } else {
+            pf[qs].v[0] = make_uint4(__float_as_uint(s[2 * c][qs][0]), __float_as_uint(s[2 * c][qs][1]),
+                                     __float_as_uint(s[2 * c][qs][2]), __float_as_uint(s[2 * c][qs][3]));
+            pf[qs].v[sizeof(T) / 2 - 1] =
+                make_uint4(__float_as_uint(s[2 * c + 1][qs][0]), __float_as_uint(s[2 * c + 1][qs][1]),
+                           __float_as_uint(s[2 * c + 1][qs][2]), __float_as_uint(s[2 * c + 1][qs][3]));
+          }
         }
 #pragma unroll
-        for (int qs = 0; qs < QS; ++qs) mma(oacc[ds][qs], vf, pf[qs]);
+        for (int ds = 0; ds < DS; ++ds) {
+          const T* vrow = Vb + (ds * 16 + lc) * VLD + 32 * c + lg * 4;
+          Frag<T> vf;
+          if constexpr (sizeof(T) == 2) {
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+            vf.v[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          } else {
+            vf.v[0] = *reinterpret_cast<const uint4*>(vrow);
+            vf.v[sizeof(T) / 2 - 1] = *reinterpret_cast<const uint4*>(vrow + 16);
+          }
+#pragma unroll
+          for (int qs = 0; qs < QS; ++qs) mma(oacc[ds][qs], vf, pf[qs]);
+        }
       }
     }
+    if (kt + 1 < nkt) sstore(buf ^ 1);  // the other buffer was last read before the previous barrier
     __syncthreads();
   }
 
@@ -239,49 +278,41 @@ __global__ __launch_bounds__(512) void k_attention(AttnArgs a) {
   }
 }
 
-template <typename T, int DQK, int DV>
-static hipError_t attn_launch_q(const AttnArgs& a, int QW, int NW, hipStream_t s) {
-  const int nqt = (a.S + QW - 1) / QW;
-  dim3 grid(nqt, a.B, a.H / NW);
-  dim3 block(64 * NW);
-  if (QW == 16) {
-    hipLaunchKernelGGL((k_attention<T, DQK, DV, 16>), grid, block, 0, s, a);
-  } else if (QW == 32 || DQK > 64) {  // 64 query rows per wave only fit registers up to width 64
-    hipLaunchKernelGGL((k_attention<T, DQK, DV, 32>), grid, block, 0, s, a);
-  } else {
-    if constexpr (DQK <= 64) hipLaunchKernelGGL((k_attention<T, DQK, DV, 64>), grid, block, 0, s, a);
-  }
+template <typename T, int DQK, int DV, int QW, int NHB>
+static hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
+  constexpr int BQ = QW * (4 / NHB);
+  dim3 grid((a.S + BQ - 1) / BQ, a.B, a.H / NHB);
+  hipLaunchKernelGGL((k_attention<T, DQK, DV, QW, NHB>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-// Picks the query tile and waves per workgroup so the launch fills the chip.
-static void attn_shape(const AttnArgs& a, int& QW, int& NW) {
+// Heads per workgroup: up to 4 heads that share a kv head; 16-row query slices
+// (32 rows when the launch has blocks to spare and the head is narrow).
+template <typename T, int DQK, int DV>
+static hipError_t attn_pick(const AttnArgs& a, hipStream_t s) {
   const int G = a.H / a.KV;
-  NW = G;
-  while (NW > 8) NW >>= 1;
-  while (NW > 1 && (G % NW)) NW >>= 1;
-  const int d = a.dqk > a.dv ? a.dqk : a.dv;
-  QW = d > 64 ? 32 : 64;
-  auto blocks = [&](int qw, int nw) { return (long long)((a.S + qw - 1) / qw) * a.B * (a.H / nw); };
-  while (blocks(QW, NW) < 512 && QW > 16) QW >>= 1;
-  while (blocks(QW, NW) < 512 && NW > 1) NW >>= 1;
+  const int nhb = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+  const long long blocks16 = (long long)((a.S + 63) / 64) * a.B * a.H;  // 64 rows per block per head
+  const bool wide = DQK <= 64 && blocks16 * 2 >= 1024;
+  if (nhb == 4) return wide ? attn_launch<T, DQK, DV, 32, 4>(a, s) : attn_launch<T, DQK, DV, 16, 4>(a, s);
+  if (nhb == 2) return wide ? attn_launch<T, DQK, DV, 32, 2>(a, s) : attn_launch<T, DQK, DV, 16, 2>(a, s);
+  return wide ? attn_launch<T, DQK, DV, 32, 1>(a, s) : attn_launch<T, DQK, DV, 16, 1>(a, s);
 }
 
 template <typename T>
 static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
-  int QW, NW;
-  attn_shape(a, QW, NW);
   const int dq = a.dqk, dv = a.dv;
-  if (dq == 16 && dv == 16) return attn_launch_q<T, 16, 16>(a, QW, NW, s);
-  if (dq == 32 && dv == 32) return attn_launch_q<T, 32, 32>(a, QW, NW, s);
-  if (dq == 64 && dv == 64) return attn_launch_q<T, 64, 64>(a, QW, NW, s);
-  if (dq == 128 && dv == 128) return attn_launch_q<T, 128, 128>(a, QW, NW, s);
-  if (dq == 160 && dv == 128) return attn_launch_q<T, 160, 128>(a, QW, NW, s);
-  if (dq == 96 && dv == 64) return attn_launch_q<T, 96, 64>(a, QW, NW, s);
+  if (dq == 16 && dv == 16) return attn_pick<T, 16, 16>(a, s);
+  if (dq == 32 && dv == 32) return attn_pick<T, 32, 32>(a, s);
+  if (dq == 64 && dv == 64) return attn_pick<T, 64, 64>(a, s);
+  if (dq == 128 && dv == 128) return attn_pick<T, 128, 128>(a, s);
+  if (dq == 160 && dv == 128) return attn_pick<T, 160, 128>(a, s);
+  if (dq == 96 && dv == 64) return attn_pick<T, 96, 64>(a, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.H % a.KV) return hipErrorInvalidValue;
   return a.dtype == DT_F32 ? attn_dispatch<float>(a, s) : attn_dispatch<bf16_t>(a, s);
 }
 

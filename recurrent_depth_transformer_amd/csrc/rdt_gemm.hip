@@ -29,7 +29,7 @@ struct GemmShape {
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr int KSUB = BK / 32;
-  static constexpr int CR = 64;         // epilogue rows per LDS chunk
+  static constexpr int CR = 32;         // epilogue rows per LDS chunk
   static constexpr int EPI_LD = BN + 4;
   static constexpr int SMEM_AB = (BM + BN) * LDK * (int)sizeof(T);
   static constexpr int SMEM_EPI = CR * EPI_LD * 4;
@@ -118,28 +118,222 @@ __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[S::FM][S::FN], char* 
 #undef RDT_SSTORE
 }
 
+// ---------------------------------------------------------------------------
+// bf16 main loop: an NS-stage ring of direct global->LDS loads.
+//
+// Each stage holds 64 k-values (128 bytes) of BM A-rows and BN B-rows. A wave
+// load instruction moves 64 lanes x 16 bytes into 1 KB of LDS in lane order
+// (8 rows x 128 bytes), so the row layout cannot be padded; instead lane l of a
+// row r fetches the 16-byte k-chunk (l % 8) ^ (r % 8), which makes the 16-row
+// fragment reads of the MFMA operands conflict-free. Loads for stage kt+NS-1
+// are issued while stage kt is multiplied, one barrier per stage. Lanes whose
+// row has no data load a valid dummy row (their products only reach discarded
+// outputs); k-chunks past the end of K are zeroed in LDS after they land.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int NS>
+struct LdsRing {
+  static constexpr int AL = BM / 32, BL = BN / 32;  // load rounds (32 rows each) per stage
+  static constexpr int LPS = AL + BL;               // load instructions per thread per stage
+  static constexpr int STAGE = (BM + BN) * 128;     // bytes per stage (>= the fp32 epilogue chunk)
+  static constexpr int FM = BM / 32, FN = BN / 32;  // 16x16 fragments per wave
+};
+
+// Waits until at most n vector-memory operations of this wave are in flight.
+// Written as asm with a memory clobber so that no LDS access moves across it.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define RDT_W(N) case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
+    RDT_W(2) RDT_W(4) RDT_W(6) RDT_W(8) RDT_W(10) RDT_W(12) RDT_W(16) RDT_W(20) RDT_W(24)
+#undef RDT_W
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// One wave-wide direct load: every lane moves 16 bytes from src into LDS at
+// lds + 16 * lane. Issued through asm so that the compiler does not insert
+// conservative waits for the LDS write; the ring waits explicitly (wait_vmcnt).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Stage buffers are distinct __shared__ objects and the loop is unrolled by NS,
+// so every LDS access names its stage statically: the compiler can then tell the
+// DMA writes of one stage from the reads of another and does not serialise them.
+template <int BM, int BN, int NS, bool TWO>
+__device__ __forceinline__ void gemm_mainloop_ring(f32x4 (&acc)[BM / 32][BN / 32], char* const (&L)[NS],
+                                                   const bf16_t* (&ap)[BM / 32], const bf16_t* (&bp)[BN / 32],
+                                                   int K, const bf16_t* (&ap2)[BM / 32],
+                                                   const bf16_t* (&bp2)[BN / 32], int K2, const bf16_t* adummy,
+                                                   const bf16_t* bdummy, const bf16_t* adummy2,
+                                                   const bf16_t* bdummy2) {
+  using R = LdsRing<BM, BN, NS>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int prow = tid >> 3;                        // row within a 32-row round
+  const int kchunk = ((tid & 7) ^ ((prow >> 1) & 7)) * 8;  // logical k offset this lane loads
+  const int nk1 = (K + 63) >> 6;
+  const int nk = nk1 + (TWO ? (K2 + 63) >> 6 : 0);
+
+#pragma unroll
+  for (int i = 0; i < R::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < R::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto issue = [&](int kt, char* buf) {
+    const bool ph2 = TWO && kt >= nk1;
+    const int k = (ph2 ? kt - nk1 : kt) * 64 + kchunk;
+    const int Kp = ph2 ? K2 : K;
+    const uint32_t st = (uint32_t)(uintptr_t)(lds_char*)buf + __builtin_amdgcn_readfirstlane(wave) * 1024;
+#pragma unroll
+    for (int i = 0; i < R::AL; ++i) {
+      const bf16_t* p = ph2 ? ap2[i] : ap[i];
+      const bf16_t* src = (p != nullptr && k < Kp) ? p + k : (ph2 ? adummy2 : adummy);
+      dma16(src, st + i * 4096);
+    }
+#pragma unroll
+    for (int i = 0; i < R::BL; ++i) {
+      const bf16_t* p = ph2 ? bp2[i] : bp[i];
+      const bf16_t* src = (p != nullptr && k < Kp) ? p + k : (ph2 ? bdummy2 : bdummy);
+      dma16(src, st + BM * 128 + i * 4096);
+    }
+  };
+  // one of the LPS load instructions of a stage (idx < AL: A rows, else B rows)
+  auto issue_one = [&](int kt, char* buf, int idx) {
+    const bool ph2 = TWO && kt >= nk1;
+    const int k = (ph2 ? kt - nk1 : kt) * 64 + kchunk;
+    const int Kp = ph2 ? K2 : K;
+    const uint32_t st = (uint32_t)(uintptr_t)(lds_char*)buf + __builtin_amdgcn_readfirstlane(wave) * 1024;
+    if (idx < R::AL) {
+      const bf16_t* p = ph2 ? ap2[idx] : ap[idx];
+      dma16((p != nullptr && k < Kp) ? p + k : (ph2 ? adummy2 : adummy), st + idx * 4096);
+    } else {
+      const bf16_t* p = ph2 ? bp2[idx - R::AL] : bp[idx - R::AL];
+      dma16((p != nullptr && k < Kp) ? p + k : (ph2 ? bdummy2 : bdummy), st + BM * 128 + (idx - R::AL) * 4096);
+    }
+  };
+  // zero this lane's k-chunks that lie past the end of K (after they landed)
+  auto zero_tail = [&](int kt, char* buf) {
+    const bool ph2 = TWO && kt >= nk1;
+    const int k = (ph2 ? kt - nk1 : kt) * 64 + kchunk;
+    const int Kp = ph2 ? K2 : K;
+    if (k < Kp) return;
+    char* st = buf + tid * 16;
+#pragma unroll
+    for (int i = 0; i < R::AL; ++i) *reinterpret_cast<uint4*>(st + i * 4096) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < R::BL; ++i) *reinterpret_cast<uint4*>(st + BM * 128 + i * 4096) = make_uint4(0, 0, 0, 0);
+  };
+  // Fragments of one 32-wide k-step (ks) of a stage, read from LDS into registers.
+  auto read_frags = [&](const char* st, int ks, Frag<bf16_t> (&fa)[R::FM], Frag<bf16_t> (&fb)[R::FN]) {
+    const int kc = ks * 4 + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < R::FM; ++i) {
+      const int row = wm * (BM / 2) + i * 16 + (lane & 15);
+      fa[i].v[0] = *reinterpret_cast<const uint4*>(st + row * 128 + ((kc ^ ((row >> 1) & 7)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < R::FN; ++j) {
+      const int row = wn * (BN / 2) + j * 16 + (lane & 15);
+      fb[j].v[0] = *reinterpret_cast<const uint4*>(st + BM * 128 + row * 128 + ((kc ^ ((row >> 1) & 7)) << 4));
+    }
+  };
+  auto mfmas = [&](const Frag<bf16_t> (&fa)[R::FM], const Frag<bf16_t> (&fb)[R::FN]) {
+#pragma unroll
+    for (int i = 0; i < R::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < R::FN; ++j) mma(acc[i][j], fa[i], fb[j]);
+  };
+  // The same MFMAs with the LPS load instructions of stage `kt` spread between
+  // them: a wave issuing its loads back to back stalls on the CU's shared load
+  // path, while between MFMAs the issue hides under MFMA execution.
+  constexpr int NM = R::FM * R::FN;
+  constexpr int EVERY = NM / R::LPS > 0 ? NM / R::LPS : 1;
+  auto mfmas_issue = [&](const Frag<bf16_t> (&fa)[R::FM], const Frag<bf16_t> (&fb)[R::FN], bool do_issue, int kt,
+                         char* buf) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      mma(acc[m / R::FN][m % R::FN], fa[m / R::FN], fb[m % R::FN]);
+      if (do_issue && (m + 1) % EVERY == 0 && (m + 1) / EVERY <= R::LPS) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_one(kt, buf, (m + 1) / EVERY - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (do_issue)
+#pragma unroll
+      for (int idx = NM / EVERY; idx < R::LPS; ++idx) issue_one(kt, buf, idx);
+  };
+  // Stage kt's data is in LDS for every wave, and every wave has finished
+  // reading the buffer that the next issue refills. A plain barrier:
+  // __syncthreads() would also wait for the loads in flight for later stages.
+  auto stage_ready = [&](int kt, char* buf) {
+    wait_vmcnt(min(NS - 2, nk - 1 - kt) * R::LPS);  // this wave's loads of stage kt landed
+    zero_tail(kt, buf);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  // Software pipeline: the barrier of stage kt+1 sits between the two k-steps
+  // of stage kt, so the first fragments of stage kt+1 stream out of LDS while
+  // the second k-step of stage kt runs on the MFMA units.
+  Frag<bf16_t> fa0[R::FM], fb0[R::FN], fa1[R::FM], fb1[R::FN];
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, L[s]);
+  stage_ready(0, L[0]);
+  if (NS - 1 < nk) issue(NS - 1, L[NS - 1]);
+  read_frags(L[0], 0, fa0, fb0);
+  for (int kt0 = 0; kt0 < nk; kt0 += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int kt = kt0 + s;
+      if (kt >= nk) break;
+      read_frags(L[s], 1, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+      bool refill = false;
+      if (kt + 1 < nk) {
+        stage_ready(kt + 1, L[(s + 1) % NS]);
+        refill = kt + NS < nk;  // stage kt+NS goes into the buffer stage kt just left
+        read_frags(L[(s + 1) % NS], 0, fa0, fb0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas_issue(fa1, fb1, refill, kt + NS, L[s]);
+    }
+  }
+  __syncthreads();
+}
+
 // Writes the accumulators of rows [c*CR, c*CR+CR) into the fp32 LDS tile.
 template <typename T, int BM, int BN, typename S = GemmShape<T, BM, BN>>
 __device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[S::FM][S::FN], float* Cs, int c) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  if ((wm * S::WM) / S::CR != c) return;
-  const int rb = wm * S::WM - c * S::CR;
 #pragma unroll
-  for (int i = 0; i < S::FM; ++i)
+  for (int i = 0; i < S::FM; ++i) {
+    const int r0 = wm * S::WM + i * 16;  // first row of this fragment
+    if (r0 / S::CR != c) continue;
+    const int rb = r0 - c * S::CR;
 #pragma unroll
     for (int j = 0; j < S::FN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        Cs[(rb + i * 16 + (lane >> 4) * 4 + r) * S::EPI_LD + wn * S::WN + j * 16 + (lane & 15)] =
-            acc[i][j][r];
+        Cs[(rb + (lane >> 4) * 4 + r) * S::EPI_LD + wn * S::WN + j * 16 + (lane & 15)] = acc[i][j][r];
+  }
 }
 
 // ============================================================== dense GEMM
-template <typename T, int BM, int BN, bool TWO>
+template <typename T, int BM, int BN, bool TWO, int NS>
 __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
   using S = GemmShape<T, BM, BN>;
-  __shared__ __align__(16) char smem[S::SMEM];
+  constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS>::STAGE : S::SMEM;
+  __shared__ __align__(16) char L0[ST];
+  __shared__ __align__(16) char L1[sizeof(T) == 2 ? ST : 16];
+  __shared__ __align__(16) char L2[sizeof(T) == 2 && NS > 2 ? ST : 16];
+  __shared__ __align__(16) char L3[sizeof(T) == 2 && NS > 3 ? ST : 16];
+  char* smem = L0;
   const int Mact = g.Mdev ? *g.Mdev : g.M;
   int ntot = 0;
   for (int s = 0; s < g.nseg; ++s) ntot += g.seg[s].ncols;
@@ -184,15 +378,23 @@ __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
   }
 
   f32x4 acc[S::FM][S::FN];
-  gemm_mainloop<T, BM, BN, TWO>(acc, smem, ap, bp, g.K, ap2, bp2, g.K2);
+  if constexpr (sizeof(T) == 2) {
+    const T* bd = reinterpret_cast<const T*>(g.seg[0].B) + (long long)z * g.b_bstride;
+    char* const Ls[4] = {L0, L1, L2, L3};
+    char* const (&Lr)[NS] = *reinterpret_cast<char* const(*)[NS]>(Ls);
+    gemm_mainloop_ring<BM, BN, NS, TWO>(acc, Lr, ap, bp, g.K, ap2, bp2, g.K2, A, bd,
+                                        reinterpret_cast<const T*>(g.A2), reinterpret_cast<const T*>(g.B2));
+  } else {
+    gemm_mainloop<T, BM, BN, TWO>(acc, smem, ap, bp, g.K, ap2, bp2, g.K2);
+  }
 
   float* Cs = reinterpret_cast<float*>(smem);
 #pragma unroll 1
-  for (int c = 0; c < BM / S::CR + (BM < S::CR ? 1 : 0); ++c) {
+  for (int c = 0; c < BM / S::CR; ++c) {
     acc_to_lds<T, BM, BN>(acc, Cs, c);
     __syncthreads();
     const int rbase = m0 + c * S::CR;
-    const int nrows = BM < S::CR ? BM : S::CR;
+    const int nrows = S::CR;
     if (g.epi == EPI_STORE) {
       for (int idx = tid; idx < nrows * (BN / 8); idx += 256) {
         const int r = idx / (BN / 8), c8 = (idx % (BN / 8)) * 8;
@@ -277,26 +479,36 @@ __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
   }
 }
 
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, int NS>
 static hipError_t dense_launch(const DenseGemm& g, hipStream_t s) {
   int ntot = 0;
   for (int i = 0; i < g.nseg; ++i) ntot += g.seg[i].ncols;
   const int ntn = (ntot + BN - 1) / BN, ntm = (g.M + BM - 1) / BM;
   dim3 grid(ntn * ntm, 1, g.batch > 0 ? g.batch : 1);
   if (g.A2) {
-    hipLaunchKernelGGL((k_dense_gemm<T, BM, BN, true>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_dense_gemm<T, BM, BN, true, NS>), grid, dim3(256), 0, s, g);
   } else {
-    hipLaunchKernelGGL((k_dense_gemm<T, BM, BN, false>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_dense_gemm<T, BM, BN, false, NS>), grid, dim3(256), 0, s, g);
   }
   return hipGetLastError();
 }
 
+template <typename T, int BM, int BN>
+static hipError_t dense_ns(const DenseGemm& g, hipStream_t s) {
+  if (sizeof(T) == 4) return dense_launch<T, BM, BN, 2>(g, s);  // fp32 ignores the stage count
+  switch (g.ns) {
+    case 3: return dense_launch<T, BM, BN, 3>(g, s);
+    case 4: return dense_launch<T, BM, BN, 4>(g, s);
+    default: return dense_launch<T, BM, BN, 2>(g, s);
+  }
+}
+
 template <typename T>
 static hipError_t dense_dispatch(const DenseGemm& g, hipStream_t s) {
-  if (g.bm == 64 && g.bn == 64) return dense_launch<T, 64, 64>(g, s);
-  if (g.bm == 64 && g.bn == 128) return dense_launch<T, 64, 128>(g, s);
-  if (g.bm == 128 && g.bn == 64) return dense_launch<T, 128, 64>(g, s);
-  return dense_launch<T, 128, 128>(g, s);
+  if (g.bm == 64 && g.bn == 64) return dense_ns<T, 64, 64>(g, s);
+  if (g.bm == 64 && g.bn == 128) return dense_ns<T, 64, 128>(g, s);
+  if (g.bm == 128 && g.bn == 64) return dense_ns<T, 128, 64>(g, s);
+  return dense_ns<T, 128, 128>(g, s);
 }
 
 hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s) {
@@ -305,10 +517,15 @@ hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s) {
 }
 
 // ============================================================ grouped GEMM
-template <typename T, int BM, int BN, int KIND>
+template <typename T, int BM, int BN, int KIND, int NS>
 __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
   using S = GemmShape<T, BM, BN>;
-  __shared__ __align__(16) char smem[S::SMEM];
+  constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS>::STAGE : S::SMEM;
+  __shared__ __align__(16) char L0[ST];
+  __shared__ __align__(16) char L1[sizeof(T) == 2 ? ST : 16];
+  __shared__ __align__(16) char L2[sizeof(T) == 2 && NS > 2 ? ST : 16];
+  __shared__ __align__(16) char L3[sizeof(T) == 2 && NS > 3 ? ST : 16];
+  char* smem = L0;
   const int G = g.E + g.Se;
   const int n = g.ndev ? *g.ndev : g.n_static;
   // KIND 0 produces BN/2 SwiGLU outputs per tile from BN/2 gate + BN/2 up rows
@@ -318,8 +535,16 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
   const int mt = L / ntn, nt = L % ntn;  // consecutive tiles share the A rows
   const int total_mt = g.tile_start[G];
   if (mt >= total_mt) return;
+  // group of this tile: number of groups that end at or before it (one ballot per 64 groups)
   int grp = 0;
-  while (grp + 1 < G && mt >= g.tile_start[grp + 1]) ++grp;
+  {
+    const int lane = threadIdx.x & 63;
+    for (int b0 = 0; b0 < G; b0 += 64) {
+      const bool ended = (b0 + lane < G) && g.tile_start[b0 + lane + 1] <= mt;
+      grp += __popcll(__ballot(ended));
+    }
+    grp = __builtin_amdgcn_readfirstlane(grp);
+  }
   const bool routed = grp < g.E;
   const int rows_g = routed ? g.counts[grp] : n;
   const int pbase = routed ? g.offs[grp] : n * g.k + (grp - g.E) * n;
@@ -361,15 +586,22 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
   }
 
   f32x4 acc[S::FM][S::FN];
-  gemm_mainloop<T, BM, BN, false>(acc, smem, ap, bp, g.K, ap, bp, 0);
+  if constexpr (sizeof(T) == 2) {
+    const T* bd = bp[0] ? bp[0] : reinterpret_cast<const T*>(routed ? g.W1 : g.S1);
+    char* const Ls[4] = {L0, L1, L2, L3};
+    char* const (&Lr)[NS] = *reinterpret_cast<char* const(*)[NS]>(Ls);
+    gemm_mainloop_ring<BM, BN, NS, false>(acc, Lr, ap, bp, g.K, ap, bp, 0, A, bd, A, bd);
+  } else {
+    gemm_mainloop<T, BM, BN, false>(acc, smem, ap, bp, g.K, ap, bp, 0);
+  }
 
   float* Cs = reinterpret_cast<float*>(smem);
   T* C = reinterpret_cast<T*>(g.C);
 #pragma unroll 1
-  for (int c = 0; c < BM / S::CR + (BM < S::CR ? 1 : 0); ++c) {
+  for (int c = 0; c < BM / S::CR; ++c) {
     acc_to_lds<T, BM, BN>(acc, Cs, c);
     __syncthreads();
-    const int nrows = BM < S::CR ? BM : S::CR;
+    const int nrows = S::CR;
     for (int idx = tid; idx < nrows * (OUTW / 8); idx += 256) {
       const int r = idx / (OUTW / 8), c8 = (idx % (OUTW / 8)) * 8;
       const int m = ml0 + c * S::CR + r;
@@ -393,18 +625,29 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
   }
 }
 
+template <typename T, int BM, int BN, int KIND, int NS>
+static hipError_t grouped_launch(const GroupedGemm& g, hipStream_t s) {
+  const int outw = KIND == 0 ? BN / 2 : BN;
+  const int ntn = (g.N + outw - 1) / outw;
+  dim3 grid(g.max_mtiles * ntn);
+  hipLaunchKernelGGL((k_grouped_gemm<T, BM, BN, KIND, NS>), grid, dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t grouped_dispatch(const GroupedGemm& g, hipStream_t s) {
-  if (g.kind == 0) {
-    const int ntn = (g.N + GU_BN / 2 - 1) / (GU_BN / 2);
-    dim3 grid(g.max_mtiles * ntn);
-    hipLaunchKernelGGL((k_grouped_gemm<T, GU_BM, GU_BN, 0>), grid, dim3(256), 0, s, g);
+  if constexpr (sizeof(T) == 4) {
+    return g.kind == 0 ? grouped_launch<T, GU_BM, GU_BN, 0, 2>(g, s) : grouped_launch<T, DN_BM, DN_BN, 1, 2>(g, s);
   } else {
-    const int ntn = (g.N + DN_BN - 1) / DN_BN;
-    dim3 grid(g.max_mtiles * ntn);
-    hipLaunchKernelGGL((k_grouped_gemm<T, DN_BM, DN_BN, 1>), grid, dim3(256), 0, s, g);
+#define RDT_G(K, BM, BN, NS) \
+    if (g.kind == K && g.bm == BM && g.bn == BN && g.ns == NS) return grouped_launch<T, BM, BN, K, NS>(g, s);
+    RDT_G(0, 128, 128, 3) RDT_G(0, 128, 128, 2) RDT_G(0, 64, 128, 3) RDT_G(0, 64, 128, 4)
+    RDT_G(0, 128, 256, 3) RDT_G(0, 64, 256, 3) RDT_G(0, 128, 256, 2)
+    RDT_G(1, 64, 128, 3) RDT_G(1, 64, 128, 4) RDT_G(1, 64, 64, 4) RDT_G(1, 128, 128, 3)
+    RDT_G(1, 128, 64, 3) RDT_G(1, 64, 256, 3) RDT_G(1, 128, 256, 3) RDT_G(1, 128, 128, 2)
+#undef RDT_G
+    return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s) {

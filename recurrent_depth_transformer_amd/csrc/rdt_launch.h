@@ -9,9 +9,11 @@ namespace rdt {
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
 // Tile shapes the host must know to plan grids and the expert tile schedule.
-constexpr int GU_BM = 128;   // grouped gate/up GEMM rows per tile
-constexpr int GU_BN = 128;   // columns of [gate | up] per tile (64 outputs)
-constexpr int DN_BM = 64;    // grouped down GEMM rows per tile
+// Default tiles of the grouped expert GEMMs (rows per tile feed the schedule
+// computed by the permutation kernel; gate/up columns hold gate and up halves).
+constexpr int GU_BM = 128;
+constexpr int GU_BN = 128;
+constexpr int DN_BM = 64;
 constexpr int DN_BN = 128;
 constexpr int ROUTER_BM = 64;
 constexpr int MAX_EXPERTS = 64;
@@ -57,6 +59,7 @@ struct DenseGemm {
   int epi;
   RouterEpi router;
   int bm, bn;            // tile shape (64 or 128 each)
+  int ns;                // bf16 pipeline stages (2..4; 0 = default)
 };
 hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s);
 
@@ -76,6 +79,7 @@ struct GroupedGemm {
   int N, K;
   void* C; int ldc;
   int max_mtiles;
+  int bm, bn, ns;        // tile rows (must match the tile_start schedule), columns, stages
 };
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s);
 

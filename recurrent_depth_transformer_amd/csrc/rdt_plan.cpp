@@ -8,7 +8,7 @@ namespace rdt {
 // Tile heights of the grouped expert GEMMs (kept in step with rdt_launch.h,
 // which this file does not include so that it builds without HIP).
 static constexpr int kGuBM = 128;
-static constexpr int kDnBM = 64;
+static constexpr int kDnBM = 64;  // smallest down-projection tile height (planning bound)
 
 static rdt_status fail(std::string* why, rdt_status st, const char* msg) {
   if (why) *why = msg;
