@@ -244,6 +244,13 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   int* inv = at<int>(ws, P.inv);
   char* hmid = at<char>(ws, P.hmid);
   char* ybuf = at<char>(ws, P.y);
+  unsigned int* done = at<unsigned int>(ws, P.done);
+  LAUNCH(RDT_STAGE_OTHER, launch_fill_i32(reinterpret_cast<int*>(done), 0, 1, s));
+  // down-projection tile height: large tiles when experts see many rows
+  const int dn_bm = ((long long)N * k / E >= 256 && dt == DT_BF16) ? 128 : 64;
+  // gate/up tile height: 192-row tiles stream each weight tile with more rows
+  // per byte and keep two workgroups per CU (measured best for every shape)
+  const int gu_bm = dt == DT_BF16 ? 192 : GU_BM;
 
   for (int t = 0; t < f.T; ++t) {
     const int* cur = act ? lists + (size_t)t * N : nullptr;
@@ -254,10 +261,13 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     const int* seg = act ? segs + (size_t)t * (P.B + 1) : nullptr;
 
     // a1: u = h + e, n1 = RMSNorm(u) * g1 (tokens whose state changed last loop)
-    NormArgs n1a{};
-    n1a.dtype = dt; n1a.h = f.out; n1a.e = f.e; n1a.a = nullptr; n1a.g = w.g1; n1a.eps = c.norm_eps; n1a.D = D;
-    n1a.rows = prev; n1a.ndev = nprev; n1a.n = N; n1a.out = n1; n1a.out_scatter = 1; n1a.dump = nullptr;
-    LAUNCH(RDT_STAGE_NORM1, launch_norm(n1a, s));
+    //     (after the first loop the combine kernel of the previous loop wrote it)
+    if (t == 0) {
+      NormArgs n1a{};
+      n1a.dtype = dt; n1a.h = f.out; n1a.e = f.e; n1a.a = nullptr; n1a.g = w.g1; n1a.eps = c.norm_eps; n1a.D = D;
+      n1a.rows = prev; n1a.ndev = nprev; n1a.n = N; n1a.out = n1; n1a.out_scatter = 1; n1a.dump = nullptr;
+      LAUNCH(RDT_STAGE_NORM1, launch_norm(n1a, s));
+    }
 
     // a2-a4: attention
     if (!P.mla) {
@@ -383,33 +393,27 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     pick_tile(N, D, 16, &go.bm, &go.bn);
     LAUNCH(RDT_STAGE_OPROJ, launch_dense_gemm(go, s));
 
-    // a5: x = u + a, n2 = RMSNorm(x) * g2 (compacted rows)
-    NormArgs n2a{};
+    // a5-a6: x = u + a, n2 = RMSNorm(x) * g2 (compacted rows), router softmax /
+    // top-k, and the stable expert permutation, in one kernel
+    NormRouteArgs nr{};
+    NormArgs& n2a = nr.norm;
     n2a.dtype = dt; n2a.h = f.out; n2a.e = f.e; n2a.a = abuf; n2a.g = w.g2; n2a.eps = c.norm_eps; n2a.D = D;
     n2a.rows = cur; n2a.ndev = ncur; n2a.n = N; n2a.out = n2; n2a.out_scatter = 0;
     n2a.dump = f.aux.n2_dump ? (void*)elt_ptr(f.aux.n2_dump, (long long)t * N * D, elt) : nullptr;
-    LAUNCH(RDT_STAGE_NORM2, launch_norm(n2a, s));
-
-    // a6: router GEMM with softmax / top-k epilogue, then the stable permutation
-    DenseGemm gr{};
-    gr.dtype = dt; gr.A = n2; gr.lda = D; gr.K = D; gr.batch = 1; gr.epi = EPI_ROUTER;
-    gr.rows = cur; gr.gather = 0; gr.M = N; gr.Mdev = ncur;
-    gr.nseg = 1; gr.seg[0] = GemmSeg{w.Wr, E, nullptr, 0, 0, 0, 0};
-    gr.bm = ROUTER_BM; gr.bn = 64;
-    gr.router.bias = w.router_bias && c.n_bias_rows > 0
-                         ? w.router_bias + (size_t)(t < c.n_bias_rows - 1 ? t : c.n_bias_rows - 1) * E
-                         : nullptr;
-    gr.router.E = E; gr.router.k = k; gr.router.idx = idx; gr.router.gates = gates; gr.router.gap = gap;
-    gr.router.dump_idx = f.aux.route_idx ? f.aux.route_idx + (size_t)t * N * k : nullptr;
-    gr.router.dump_gap = f.aux.route_gap ? f.aux.route_gap + (size_t)t * N : nullptr;
-    LAUNCH(RDT_STAGE_ROUTER, launch_dense_gemm(gr, s));
-
-    PermuteArgs pa{};
+    nr.Wr = w.Wr; nr.E = E; nr.k = k;
+    nr.bias = w.router_bias && c.n_bias_rows > 0
+                  ? w.router_bias + (size_t)(t < c.n_bias_rows - 1 ? t : c.n_bias_rows - 1) * E
+                  : nullptr;
+    nr.idx = idx; nr.gates = gates; nr.gap = gap;
+    nr.dump_idx = f.aux.route_idx ? f.aux.route_idx + (size_t)t * N * k : nullptr;
+    nr.dump_gap = f.aux.route_gap ? f.aux.route_gap + (size_t)t * N : nullptr;
+    PermuteArgs& pa = nr.perm;
     pa.idx = idx; pa.ndev = ncur; pa.n_static = N; pa.E = E; pa.Se = P.Se; pa.k = k;
     pa.counts = counts; pa.offs = offs; pa.perm = perm; pa.inv = inv;
-    pa.ts_gu = ts_gu; pa.bm_gu = GU_BM; pa.ts_dn = ts_dn; pa.bm_dn = ((long long)N * k / E >= 256 && dt == DT_BF16) ? 128 : 64;
+    pa.ts_gu = ts_gu; pa.bm_gu = gu_bm; pa.ts_dn = ts_dn; pa.bm_dn = dn_bm;
     pa.counts_dump = f.aux.expert_counts ? f.aux.expert_counts + (size_t)t * E : nullptr;
-    LAUNCH(RDT_STAGE_PERMUTE, launch_permute(pa, s));
+    nr.done = done;
+    LAUNCH(RDT_STAGE_ROUTER, launch_norm_route(nr, s));
 
     // a7: grouped SwiGLU experts
     GroupedGemm gu{};
@@ -417,7 +421,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     gu.perm = perm; gu.offs = offs; gu.counts = counts; gu.tile_start = ts_gu; gu.ndev = ncur; gu.n_static = N;
     gu.E = E; gu.Se = P.Se; gu.k = k; gu.W1 = w.Wg; gu.W2 = w.Wu; gu.S1 = w.Wsg; gu.S2 = w.Wsu;
     gu.N = P.F; gu.K = D; gu.C = hmid; gu.ldc = P.F; gu.max_mtiles = P.gu_max_mtiles;
-    gu.bm = GU_BM; gu.bn = GU_BN; gu.ns = 2;
+    gu.bm = gu_bm; gu.bn = GU_BN; gu.ns = 2;
     LAUNCH(RDT_STAGE_EXPERT_GU, launch_grouped_gemm(gu, s));
     GroupedGemm gd{};
     gd.dtype = dt; gd.kind = 1; gd.A = hmid; gd.lda = P.F;
@@ -425,7 +429,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     gd.E = E; gd.Se = P.Se; gd.k = k; gd.W1 = w.Wd; gd.W2 = nullptr; gd.S1 = w.Wsd; gd.S2 = nullptr;
     gd.N = D; gd.K = P.F; gd.C = ybuf; gd.ldc = D; gd.max_mtiles = P.dn_max_mtiles;
     // many rows per expert: large tiles; few rows: small tiles, deeper ring
-    if ((long long)N * k / E >= 256 && dt == DT_BF16) { gd.bm = 128; gd.bn = 128; gd.ns = 2; }
+    if (dn_bm == 128) { gd.bm = 128; gd.bn = 128; gd.ns = 2; }
     else { gd.bm = 64; gd.bn = 64; gd.ns = 4; }
     LAUNCH(RDT_STAGE_EXPERT_DOWN, launch_grouped_gemm(gd, s));
 
@@ -437,6 +441,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     ca.act = act; ca.w_halt = w.w_halt; ca.thr = c.act_threshold; ca.cum = cum; ca.loops = f.aux.loops; ca.t = t;
     ca.cum_dump = f.aux.act_cum ? f.aux.act_cum + (size_t)t * N : nullptr;
     ca.a_dump = f.aux.a_dump ? f.aux.a_dump + (size_t)t * N * D : nullptr;
+    ca.n1_out = t + 1 < f.T ? n1 : nullptr; ca.g1 = w.g1; ca.eps = c.norm_eps;
     LAUNCH(RDT_STAGE_COMBINE, launch_combine(ca, s));
     if (act) {
       CompactArgs cp{};

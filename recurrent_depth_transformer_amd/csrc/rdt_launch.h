@@ -80,7 +80,12 @@ struct GroupedGemm {
   void* C; int ldc;
   int max_mtiles;
   int bm, bn, ns;        // tile rows (must match the tile_start schedule), columns, stages
+  // register-direct variant (bf16, K % 64 == 0, bm == RD_BM): operands stream
+  // from global memory into registers; ks waves share one output tile along K,
+  // rd_p stages of loads are kept in flight per wave
+  int rd, ks, rd_p;
 };
+constexpr int RD_BM = 64;
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s);
 
 // ------------------------------------------------------------------ attention
@@ -119,6 +124,8 @@ struct CombineArgs {
   int act; const float* w_halt; float thr; float* cum; int* loops; int t;
   float* cum_dump;       // [N] by token, may be null
   float* a_dump;         // [N, D] by token, may be null
+  void* n1_out;          // optional: next loop's RMSNorm(h' + e) * g1 by token
+  const float* g1; float eps;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
@@ -130,6 +137,16 @@ struct PermuteArgs {
   int* counts_dump;      // [E] may be null
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+// Second RMSNorm + router + top-k; the last workgroup builds the permutation.
+struct NormRouteArgs {
+  NormArgs norm;         // x = h + e + a[i]; out = n2 (compacted rows), dump by token
+  const void* Wr; int E, k; const float* bias;
+  int* idx; float* gates; float* gap; int* dump_idx; float* dump_gap;
+  PermuteArgs perm;
+  unsigned int* done;    // completion counter, zero between launches
+};
+hipError_t launch_norm_route(const NormRouteArgs& a, hipStream_t s);
 
 struct CompactArgs {
   const int* rows_in; const int* n_in; const float* cum; float thr;

@@ -5,10 +5,11 @@
 
 namespace rdt {
 
-// Tile heights of the grouped expert GEMMs (kept in step with rdt_launch.h,
-// which this file does not include so that it builds without HIP).
-static constexpr int kGuBM = 128;
-static constexpr int kDnBM = 64;  // smallest down-projection tile height (planning bound)
+// Smallest tile heights the grouped expert GEMMs use (kept in step with the
+// host orchestration; this file does not include the HIP headers). Taller
+// tiles need fewer tiles, so these bound the grid from above.
+static constexpr int kGuBM = 128;  // gate/up
+static constexpr int kDnBM = 64;   // down projection
 
 static rdt_status fail(std::string* why, rdt_status st, const char* msg) {
   if (why) *why = msg;
@@ -120,6 +121,7 @@ Plan make_plan(const rdt_config& c, int T) {
   p.ncount = take(Tp * 4);
   p.seg = take(Tp * (p.B + 1) * 4);
   p.cum = take(N * 4);
+  p.done = take(4);
   p.total = off;
   return p;
 }

@@ -25,6 +25,7 @@ struct Plan {
   size_t idx, gates, gap, counts, offs, ts_gu, ts_dn, perm, inv;
   size_t hmid, y;
   size_t lists, ncount, seg, cum;
+  size_t done;              // completion counter of the fused router kernel
   size_t total;
 };
 

@@ -111,6 +111,31 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       z += wv.x * hn.x + wv.y * hn.y + wv.z * hn.z + wv.w * hn.w;
     }
   }
+  if (a.n1_out) {
+    // next loop's first RMSNorm of u = h' + e, for the rows just updated
+    float ss = 0.f;
+    for (int c = 0; c < MAXV; ++c) {
+      const int col = (c * 64 + lane) * 4;
+      if (col >= D) break;
+      const float4 hv = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + col);
+      const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
+      const float u0 = hv.x + ev.x, u1 = hv.y + ev.y, u2 = hv.z + ev.z, u3 = hv.w + ev.w;
+      ss += u0 * u0 + u1 * u1 + u2 * u2 + u3 * u3;
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.f / sqrtf(ss / (float)D + a.eps);
+    T* dst = reinterpret_cast<T*>(a.n1_out) + (long long)tok * D;
+    for (int c = 0; c < MAXV; ++c) {
+      const int col = (c * 64 + lane) * 4;
+      if (col >= D) break;
+      const float4 hv = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + col);
+      const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
+      const float4 gv = *reinterpret_cast<const float4*>(a.g1 + col);
+      float y[4] = {(hv.x + ev.x) * inv * gv.x, (hv.y + ev.y) * inv * gv.y, (hv.z + ev.z) * inv * gv.z,
+                    (hv.w + ev.w) * inv * gv.w};
+      store4<T>(dst + col, y);
+    }
+  }
   if (a.act) {
     z = wave_sum(z);
     if (lane == 0) {
@@ -136,7 +161,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
 // expert ranks the rows of one wave that chose it, wave totals are scanned per
 // expert, and a running count carries across chunks. Positions inside an
 // expert therefore follow row order (a stable counting sort, no atomics).
-__global__ __launch_bounds__(1024) void k_permute(PermuteArgs a) {
+__device__ void permute_block(const PermuteArgs& a) {
   __shared__ unsigned long long wmask[16][MAX_EXPERTS];
   __shared__ int wbase[16][MAX_EXPERTS];
   __shared__ int run[MAX_EXPERTS];
@@ -206,6 +231,169 @@ __global__ __launch_bounds__(1024) void k_permute(PermuteArgs a) {
       a.inv[q] = p;
       a.perm[p] = i;
     }
+}
+
+__global__ __launch_bounds__(1024) void k_permute(PermuteArgs a) { permute_block(a); }
+
+// ----------------------------------------- second RMSNorm + router + permute
+// A workgroup of 16 waves takes 16 compacted rows. Each wave forms one row
+// x = h + e + a, n2 = RMSNorm(x) * g2 (stored in the storage type, and staged
+// in LDS in column chunks). The router logits n2 . Wr^T of the 16 rows come
+// from 16x16x32 MFMAs: wave w takes expert tile (w % NT) and every (16/NT)-th
+// k-step, partial tiles are summed through LDS. Then one wave per row: softmax
+// gates over all experts, top-k on logit + bias by k rounds of a wave argmax
+// (equal scores go to the lower expert). The last workgroup to finish (an
+// atomic completion count) builds the stable expert permutation.
+template <typename T, int NV>
+__global__ __launch_bounds__(1024) void k_norm_route(NormRouteArgs a) {
+  constexpr int KC = 4096 / (int)sizeof(T);        // columns per LDS chunk
+  constexpr int LDA = KC + 16 / (int)sizeof(T);    // padded row stride
+  __shared__ __align__(16) T As[16 * LDA];
+  __shared__ int s_idx[16][MAX_EXPERTS];         // chosen experts of the 16 rows
+  __shared__ int is_last;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const NormArgs& na = a.norm;
+  const int i = blockIdx.x * 16 + wave;
+  const int n = na.ndev ? *na.ndev : na.n;
+  const int D = na.D, E = a.E, k = a.k;
+  const bool live = i < n;
+  const int tok = live ? (na.rows ? na.rows[i] : i) : 0;
+  float x[NV][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    const int col = (c * 64 + lane) * 4;
+    x[c][0] = x[c][1] = x[c][2] = x[c][3] = 0.f;
+    if (live && col < D) {
+      const float4 hv = *reinterpret_cast<const float4*>(na.h + (long long)tok * D + col);
+      const float4 ev = *reinterpret_cast<const float4*>(na.e + (long long)tok * D + col);
+      const float4 av = *reinterpret_cast<const float4*>(na.a + (long long)i * D + col);
+      x[c][0] = hv.x + ev.x + av.x; x[c][1] = hv.y + ev.y + av.y;
+      x[c][2] = hv.z + ev.z + av.z; x[c][3] = hv.w + ev.w + av.w;
+      ss += x[c][0] * x[c][0] + x[c][1] * x[c][1] + x[c][2] * x[c][2] + x[c][3] * x[c][3];
+    }
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.f / sqrtf(ss / (float)D + na.eps);
+  T* out = reinterpret_cast<T*>(na.out) + (long long)i * D;
+  T* dump = na.dump && live ? reinterpret_cast<T*>(na.dump) + (long long)tok * D : nullptr;
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    const int col = (c * 64 + lane) * 4;
+    if (live && col < D) {
+      const float4 gv = *reinterpret_cast<const float4*>(na.g + col);
+      x[c][0] *= inv * gv.x; x[c][1] *= inv * gv.y; x[c][2] *= inv * gv.z; x[c][3] *= inv * gv.w;
+      store4<T>(out + col, x[c]);
+      if (dump) store4<T>(dump + col, x[c]);
+    }
+  }
+  // router logits on the stored (rounded) values
+  const int NT = E <= 16 ? 1 : E <= 32 ? 2 : 4;   // expert tiles of 16
+  const int KS = 16 / NT;                          // waves sharing one expert tile
+  const int nt = wave % NT, ks = wave / NT;
+  const int en = nt * 16 + (lane & 15);            // expert of this lane's B row
+  const T* Wr = reinterpret_cast<const T*>(a.Wr);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kc0 = 0; kc0 < D; kc0 += KC) {
+    const int ck = D - kc0 < KC ? D - kc0 : KC;
+    const int ck32 = (ck + 31) & ~31;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      const int col = (c * 64 + lane) * 4;        // global column
+      const int lc = col - kc0;                   // column inside the chunk
+      if (lc >= 0 && lc < ck32) store4<T>(As + wave * LDA + lc, x[c]);   // zero beyond D
+    }
+    __syncthreads();
+    const int nstep = ck32 / 32;
+    for (int st = ks; st < nstep; st += KS) {
+      const int kk = st * 32 + (lane >> 4) * 8;
+      const Frag<T> af = frag_lds<T>(As + (lane & 15) * LDA + kk);
+      Frag<T> bf = frag_zero<T>();
+      if (en < E && kc0 + kk < D) {
+        const uint4* q = reinterpret_cast<const uint4*>(Wr + (long long)en * D + kc0 + kk);
+#pragma unroll
+        for (int v = 0; v < (int)(sizeof(T) / 2); ++v) bf.v[v] = q[v];
+      }
+      mma(acc, af, bf);
+    }
+    __syncthreads();
+  }
+  // partial tiles -> LDS (reusing the staging buffer), summed per row below
+  float* red = reinterpret_cast<float*>(As);      // [KS][16][64]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(ks * 16 + (lane >> 4) * 4 + r) * 64 + nt * 16 + (lane & 15)] = acc[r];
+  __syncthreads();
+  if (live) {
+    const bool own = lane < E;                     // lane e holds expert e
+    float logit = 0.f;
+    for (int q = 0; q < KS; ++q) logit += red[(q * 16 + wave) * 64 + lane];
+    const float mx = wave_max(own ? logit : -INFINITY);
+    const float pe = own ? expf(logit - mx) : 0.f;
+    const float den = wave_sum(pe);
+    const float gate = pe / den;
+    float sel = own ? logit + (a.bias ? a.bias[lane] : 0.f) : -INFINITY;
+    bool avail = own;                              // not chosen yet
+    float kth = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const float best = wave_max(avail ? sel : -INFINITY);
+      unsigned long long m = __ballot(avail && sel == best);
+      if (m == 0ull) m = __ballot(avail);          // NaN scores: first free expert (k <= E)
+      const int win = __ffsll((long long)m) - 1;   // lowest expert among equal scores
+      const float g = __shfl(gate, win, 64);
+      if (lane == 0) {
+        s_idx[wave][j] = win;
+        a.gates[(long long)i * k + j] = g;
+        if (a.dump_idx) a.dump_idx[(long long)tok * k + j] = win;
+      }
+      if (lane == win) avail = false;
+      kth = best;
+    }
+    const float nxt = wave_max(avail ? sel : -INFINITY);
+    if (lane == 0) {
+      const float gp = k < E ? kth - nxt : INFINITY;
+      a.gap[i] = gp;
+      if (a.dump_gap) a.dump_gap[tok] = gp;
+    }
+  }
+  // Wave 0 publishes the block's expert choices (the only data the permutation
+  // reads) and releases them with one device-scope fence; the last workgroup
+  // to count in acquires and builds the permutation. A fence per wave would
+  // write back the XCD's L2 once per wave.
+  __syncthreads();
+  if (wave == 0) {
+    for (int q = lane; q < 16 * k; q += 64) {
+      const int r = q / k, row = blockIdx.x * 16 + r;
+      if (row < n) a.idx[(long long)row * k + (q - r * k)] = s_idx[r][q - r * k];
+    }
+    __threadfence();
+    if (lane == 0) {
+      const bool last = atomicAdd(a.done, 1u) == gridDim.x - 1;
+      if (last) __threadfence();
+      is_last = last;
+    }
+  }
+  __syncthreads();
+  if (is_last) {
+    permute_block(a.perm);
+    if (threadIdx.x == 0) atomicExch(a.done, 0u);  // ready for the next launch
+  }
+}
+
+template <typename T>
+static hipError_t norm_route_t(const NormRouteArgs& a, hipStream_t s) {
+  dim3 grid((a.norm.n + 15) / 16);
+  const int nv = (a.norm.D + 255) / 256;
+  if (nv <= 1) hipLaunchKernelGGL((k_norm_route<T, 1>), grid, dim3(1024), 0, s, a);
+  else if (nv <= 2) hipLaunchKernelGGL((k_norm_route<T, 2>), grid, dim3(1024), 0, s, a);
+  else if (nv <= 4) hipLaunchKernelGGL((k_norm_route<T, 4>), grid, dim3(1024), 0, s, a);
+  else if (nv <= 8) hipLaunchKernelGGL((k_norm_route<T, 8>), grid, dim3(1024), 0, s, a);
+  else hipLaunchKernelGGL((k_norm_route<T, 16>), grid, dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_route(const NormRouteArgs& a, hipStream_t s) {
+  if (a.norm.n <= 0 || a.E > MAX_EXPERTS || a.E < 1 || a.k > a.E || a.norm.D % 8) return hipErrorInvalidValue;
+  return a.norm.dtype == DT_F32 ? norm_route_t<float>(a, s) : norm_route_t<bf16_t>(a, s);
 }
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
