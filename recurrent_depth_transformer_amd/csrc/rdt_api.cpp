@@ -1,13 +1,14 @@
 // librdt C-ABI: argument checks, the rho(A) guard, the per-loop launch plan and
 // the cache of captured HIP graphs.
 //
-// One forward enqueues, per loop t (techbriefly: h_{t+1} = A h_t + B e +
-// Transformer(h_t, e)):
-//   RMSNorm(h + e) -> Q/K/V (GQA, RoPE in the epilogue) or the MLA latent
-//   chain -> causal flash attention -> output projection (+ depth-wise LoRA as
-//   a second K phase) -> RMSNorm -> router GEMM with softmax/top-k epilogue ->
-//   stable expert permutation -> grouped SwiGLU gate/up -> grouped down ->
-//   combine + injection (+ ACT) -> (ACT) active-list compaction.
+// One forward enqueues, per loop t (h_{t+1} = A h_t + B e + Block(h_t, e)):
+//   RMSNorm(h + e) (first loop only; later loops get it from the combine
+//   kernel) -> Q/K/V (GQA, RoPE in the epilogue) or the MLA latent chain ->
+//   causal flash attention -> output projection (+ depth-wise LoRA as a second
+//   K phase) -> one kernel for RMSNorm, router softmax/top-k and the stable
+//   expert permutation -> grouped SwiGLU gate/up -> grouped down -> combine +
+//   injection (+ ACT, + the next loop's first RMSNorm) -> (ACT) active-list
+//   compaction.
 // Data-dependent sizes (active tokens, rows per expert) stay on the device;
 // grids are sized for the worst case and idle workgroups exit at once, so the
 // whole T-loop is a static graph.
@@ -247,10 +248,14 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   unsigned int* done = at<unsigned int>(ws, P.done);
   LAUNCH(RDT_STAGE_OTHER, launch_fill_i32(reinterpret_cast<int*>(done), 0, 1, s));
   // down-projection tile height: large tiles when experts see many rows
-  const int dn_bm = ((long long)N * k / E >= 256 && dt == DT_BF16) ? 128 : 64;
-  // gate/up tile height: 192-row tiles stream each weight tile with more rows
-  // per byte and keep two workgroups per CU (measured best for every shape)
-  const int gu_bm = dt == DT_BF16 ? 192 : GU_BM;
+  // Expert GEMM tiles (measured on MI355X): gate/up 192x128 with a two-stage
+  // ring (two workgroups per CU) for every shape; down 128x128 when experts
+  // see many rows, else 64x64 with a three-stage ring.
+  const long long rows_per_expert = (long long)N * k / E;
+  const bool bf = dt == DT_BF16;
+  const int gu_bm = bf ? 192 : GU_BM;
+  const int gu_bn = GU_BN;
+  const int dn_bm = (rows_per_expert >= 256 && bf) ? 128 : 64;
 
   for (int t = 0; t < f.T; ++t) {
     const int* cur = act ? lists + (size_t)t * N : nullptr;
@@ -421,7 +426,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     gu.perm = perm; gu.offs = offs; gu.counts = counts; gu.tile_start = ts_gu; gu.ndev = ncur; gu.n_static = N;
     gu.E = E; gu.Se = P.Se; gu.k = k; gu.W1 = w.Wg; gu.W2 = w.Wu; gu.S1 = w.Wsg; gu.S2 = w.Wsu;
     gu.N = P.F; gu.K = D; gu.C = hmid; gu.ldc = P.F; gu.max_mtiles = P.gu_max_mtiles;
-    gu.bm = gu_bm; gu.bn = GU_BN; gu.ns = 2;
+    gu.bm = gu_bm; gu.bn = gu_bn; gu.ns = 2;
     LAUNCH(RDT_STAGE_EXPERT_GU, launch_grouped_gemm(gu, s));
     GroupedGemm gd{};
     gd.dtype = dt; gd.kind = 1; gd.A = hmid; gd.lda = P.F;
@@ -430,7 +435,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     gd.N = D; gd.K = P.F; gd.C = ybuf; gd.ldc = D; gd.max_mtiles = P.dn_max_mtiles;
     // many rows per expert: large tiles; few rows: small tiles, deeper ring
     if (dn_bm == 128) { gd.bm = 128; gd.bn = 128; gd.ns = 2; }
-    else { gd.bm = 64; gd.bn = 64; gd.ns = 4; }
+    else { gd.bm = 64; gd.bn = 64; gd.ns = 3; }
     LAUNCH(RDT_STAGE_EXPERT_DOWN, launch_grouped_gemm(gd, s));
 
     // a8: combine + LTI injection (+ ACT)

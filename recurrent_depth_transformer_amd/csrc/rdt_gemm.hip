@@ -629,213 +629,6 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
   }
 }
 
-// ============================================== register-direct grouped GEMM
-// When experts see few rows the expert GEMMs are bound by streaming weights
-// from HBM, and an LDS ring holds too few bytes in flight to cover the memory
-// latency. Here every wave loads its MFMA operands straight from global memory
-// into a P-stage register ring: no LDS staging and no barrier in the main
-// loop. A block has 4 waves; wave w takes column slice (w % WNC) and every
-// KS-th 64-wide k-stage starting at stage (w / WNC). The KS partial tiles are
-// summed through LDS in a fixed order, so results do not depend on timing.
-//
-// Inside a 64-wide stage, lane l (row l % 16, group q = l / 16) loads the 16
-// consecutive k values [16q, 16q + 16) of its row as two 16-byte vectors; the
-// first feeds k-step 0 and the second k-step 1. A and B use the same mapping
-// of k to (k-step, lane group), so every product pairs equal k; only the
-// order of the k summation differs from a plain sweep.
-constexpr int RD_WN = 64;   // B rows per wave (gate/up: 32 gate + 32 up rows)
-
-template <int KIND, int KS, int P>
-__global__ __launch_bounds__(256) void k_grouped_rd(GroupedGemm g) {
-  constexpr int WNC = 4 / KS;
-  constexpr int FM = RD_BM / 16, FN = RD_WN / 16;
-  constexpr int OUTW_W = KIND == 0 ? RD_WN / 2 : RD_WN;  // outputs per wave
-  constexpr int OUTW = WNC * OUTW_W;                      // outputs per block
-  constexpr int ELD = OUTW_W + 4;                         // epilogue row stride (floats)
-  constexpr int RED = (KS - 1) * WNC * FM * FN * 4 * 64;  // partial tiles (floats)
-  constexpr int EPI = WNC * RD_BM * ELD;
-  __shared__ __align__(16) float sm[RED > EPI ? RED : EPI];
-  const int G = g.E + g.Se;
-  const int n = g.ndev ? *g.ndev : g.n_static;
-  const int ntn = (g.N + OUTW - 1) / OUTW;
-  const int total_mt = g.tile_start[G];
-  const int nb = total_mt * ntn;
-  if ((int)blockIdx.x >= nb) return;
-  // m-tiles of one column tile are adjacent, so tiles that stream the same
-  // weights land on one XCD and can share them through its L2
-  const int L = xcd_remap(blockIdx.x, nb);
-  const int mt = L % total_mt, nt = L / total_mt;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int gi = 0;
-  for (int b0 = 0; b0 < G; b0 += 64) {
-    const bool ended = (b0 + lane < G) && g.tile_start[b0 + lane + 1] <= mt;
-    gi += __popcll(__ballot(ended));
-  }
-  gi = __builtin_amdgcn_readfirstlane(gi);
-  const bool routed = gi < g.E;
-  const int rows_g = routed ? g.counts[gi] : n;
-  const int pbase = routed ? g.offs[gi] : n * g.k + (gi - g.E) * n;
-  const int ml0 = (mt - g.tile_start[gi]) * RD_BM;
-  const int n0 = nt * OUTW;
-  const int wn = wave % WNC, wk = wave / WNC;
-  const int r16 = lane & 15, q16 = (lane >> 4) * 16;
-  const int K = g.K;
-
-  // operand rows of this lane; rows past the end repeat a valid row (their
-  // products only reach outputs that are not stored)
-  const bf16_t* A = reinterpret_cast<const bf16_t*>(g.A);
-  const bf16_t* ap[FM];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = ml0 + i * 16 + r16;
-    const int mm = m < rows_g ? m : ml0;
-    const int src = KIND == 0 ? (routed ? g.perm[pbase + mm] : mm) : pbase + mm;
-    ap[i] = A + (long long)src * g.lda + q16;
-  }
-  const long long wsz = (long long)g.N * K;
-  const bf16_t* bp[FN];
-  if (KIND == 0) {
-    const bf16_t* wg = reinterpret_cast<const bf16_t*>(routed ? g.W1 : g.S1) + (routed ? gi : gi - g.E) * wsz;
-    const bf16_t* wu = reinterpret_cast<const bf16_t*>(routed ? g.W2 : g.S2) + (routed ? gi : gi - g.E) * wsz;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int f = n0 + wn * OUTW_W + (j % (FN / 2)) * 16 + r16;
-      bp[j] = (j < FN / 2 ? wg : wu) + (long long)(f < g.N ? f : g.N - 1) * K + q16;
-    }
-  } else {
-    const bf16_t* wd = reinterpret_cast<const bf16_t*>(routed ? g.W1 : g.S1) + (routed ? gi : gi - g.E) * wsz;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int c = n0 + wn * RD_WN + j * 16 + r16;
-      bp[j] = wd + (long long)(c < g.N ? c : g.N - 1) * K + q16;
-    }
-  }
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nk = K / 64;
-  const int nq = nk > wk ? (nk - wk + KS - 1) / KS : 0;  // stages of this wave
-  uint4 ra[P][FM][2], rb[P][FN][2];
-  auto load = [&](int q, uint4 (&a)[FM][2], uint4 (&b)[FN][2]) {
-    const int k = (wk + KS * q) * 64;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      a[i][0] = *reinterpret_cast<const uint4*>(ap[i] + k);
-      a[i][1] = *reinterpret_cast<const uint4*>(ap[i] + k + 8);
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      b[j][0] = *reinterpret_cast<const uint4*>(bp[j] + k);
-      b[j][1] = *reinterpret_cast<const uint4*>(bp[j] + k + 8);
-    }
-  };
-  auto compute = [&](const uint4 (&a)[FM][2], const uint4 (&b)[FN][2]) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[i][h]),
-                                                              __builtin_bit_cast(bf16x8_t, b[j][h]), acc[i][j], 0, 0, 0);
-  };
-#pragma unroll
-  for (int s = 0; s < P; ++s)
-    if (s < nq) load(s, ra[s], rb[s]);
-  for (int q0 = 0; q0 < nq; q0 += P) {
-#pragma unroll
-    for (int s = 0; s < P; ++s) {
-      const int q = q0 + s;
-      if (q < nq) {
-        compute(ra[s], rb[s]);
-        if (q + P < nq) load(q + P, ra[s], rb[s]);
-      }
-    }
-  }
-
-  // sum the KS partial tiles in a fixed order (lane-major: conflict-free)
-  if constexpr (KS > 1) {
-    constexpr int TILE = FM * FN * 4 * 64;
-    if (wk > 0) {
-      float* dst = sm + ((wk - 1) * WNC + wn) * TILE;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[((i * FN + j) * 4 + r) * 64 + lane] = acc[i][j][r];
-    }
-    __syncthreads();
-    if (wk == 0) {
-      for (int w2 = 1; w2 < KS; ++w2) {
-        const float* src = sm + ((w2 - 1) * WNC + wn) * TILE;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] += src[((i * FN + j) * 4 + r) * 64 + lane];
-      }
-    }
-    __syncthreads();
-  }
-  // results -> LDS as [row][col] per column slice, then 16-byte row stores
-  if (wk == 0) {
-    float* et = sm + wn * RD_BM * ELD;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = i * 16 + (lane >> 4) * 4 + r;
-        if (KIND == 0) {
-#pragma unroll
-          for (int j = 0; j < FN / 2; ++j) {
-            const float gt = acc[i][j][r], up = acc[i][j + FN / 2][r];
-            et[row * ELD + j * 16 + r16] = gt / (1.f + expf(-gt)) * up;
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) et[row * ELD + j * 16 + r16] = acc[i][j][r];
-        }
-      }
-  }
-  __syncthreads();
-  bf16_t* C = reinterpret_cast<bf16_t*>(g.C);
-  for (int idx = threadIdx.x; idx < RD_BM * (OUTW / 8); idx += 256) {
-    const int r = idx / (OUTW / 8), c8 = (idx % (OUTW / 8)) * 8;
-    const int m = ml0 + r, col = n0 + c8;
-    if (m >= rows_g || col >= g.N) continue;
-    const float* src = sm + (c8 / OUTW_W) * RD_BM * ELD + r * ELD + (c8 % OUTW_W);
-    float v[8];
-    const float4 x0 = *reinterpret_cast<const float4*>(src);
-    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-    v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w; v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-    store8<bf16_t>(C + (long long)(pbase + m) * g.ldc + col, v);
-  }
-}
-
-template <int KIND, int KS, int P>
-static hipError_t grouped_rd_launch(const GroupedGemm& g, hipStream_t s) {
-  constexpr int OUTW = (4 / KS) * (KIND == 0 ? RD_WN / 2 : RD_WN);
-  const int ntn = (g.N + OUTW - 1) / OUTW;
-  dim3 grid(g.max_mtiles * ntn);
-  hipLaunchKernelGGL((k_grouped_rd<KIND, KS, P>), grid, dim3(256), 0, s, g);
-  return hipGetLastError();
-}
-
-static hipError_t grouped_rd_dispatch(const GroupedGemm& g, hipStream_t s) {
-  if (g.dtype != DT_BF16 || g.K % 64 || g.bm != RD_BM) return hipErrorInvalidValue;
-#define RDT_R(K, KS, P) \
-  if (g.kind == K && g.ks == KS && g.rd_p == P) return grouped_rd_launch<K, KS, P>(g, s);
-  RDT_R(0, 1, 2) RDT_R(0, 2, 2) RDT_R(0, 1, 3) RDT_R(0, 2, 3) RDT_R(0, 4, 2)
-  RDT_R(1, 1, 2) RDT_R(1, 2, 2) RDT_R(1, 4, 2) RDT_R(1, 2, 3) RDT_R(1, 4, 3)
-#undef RDT_R
-  return hipErrorInvalidValue;
-}
-
 template <typename T, int BM, int BN, int KIND, int NS>
 static hipError_t grouped_launch(const GroupedGemm& g, hipStream_t s) {
   const int outw = KIND == 0 ? BN / 2 : BN;
@@ -852,12 +645,8 @@ static hipError_t grouped_dispatch(const GroupedGemm& g, hipStream_t s) {
   } else {
 #define RDT_G(K, BM, BN, NS) \
     if (g.kind == K && g.bm == BM && g.bn == BN && g.ns == NS) return grouped_launch<T, BM, BN, K, NS>(g, s);
-    RDT_G(0, 128, 128, 3) RDT_G(0, 128, 128, 2) RDT_G(0, 64, 128, 3) RDT_G(0, 64, 128, 4)
-    RDT_G(0, 128, 256, 3) RDT_G(0, 64, 256, 3) RDT_G(0, 128, 256, 2)
-    RDT_G(0, 192, 128, 2) RDT_G(0, 256, 64, 2) RDT_G(0, 256, 64, 3) RDT_G(0, 192, 64, 3) RDT_G(0, 128, 64, 4)
-    RDT_G(1, 64, 128, 3) RDT_G(1, 64, 128, 4) RDT_G(1, 64, 64, 4) RDT_G(1, 128, 128, 3)
-    RDT_G(1, 128, 64, 3) RDT_G(1, 64, 256, 3) RDT_G(1, 128, 256, 3) RDT_G(1, 128, 128, 2)
-    RDT_G(1, 192, 64, 3) RDT_G(1, 128, 64, 4) RDT_G(1, 64, 64, 3) RDT_G(1, 64, 64, 2)
+    RDT_G(0, 128, 128, 2) RDT_G(0, 192, 128, 2)
+    RDT_G(1, 64, 64, 3) RDT_G(1, 64, 64, 4) RDT_G(1, 128, 128, 2)
 #undef RDT_G
     return hipErrorInvalidValue;
   }
@@ -865,7 +654,6 @@ static hipError_t grouped_dispatch(const GroupedGemm& g, hipStream_t s) {
 
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s) {
   if (g.max_mtiles <= 0) return hipSuccess;
-  if (g.rd) return grouped_rd_dispatch(g, s);
   return g.dtype == DT_F32 ? grouped_dispatch<float>(g, s) : grouped_dispatch<bf16_t>(g, s);
 }
 

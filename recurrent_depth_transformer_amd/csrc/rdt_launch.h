@@ -80,12 +80,7 @@ struct GroupedGemm {
   void* C; int ldc;
   int max_mtiles;
   int bm, bn, ns;        // tile rows (must match the tile_start schedule), columns, stages
-  // register-direct variant (bf16, K % 64 == 0, bm == RD_BM): operands stream
-  // from global memory into registers; ks waves share one output tile along K,
-  // rd_p stages of loads are kept in flight per wave
-  int rd, ks, rd_p;
 };
-constexpr int RD_BM = 64;
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s);
 
 // ------------------------------------------------------------------ attention
