@@ -221,6 +221,63 @@ rdt_status rdt_recurrent_forward(rdt_handle* h, const float* h0, const float* e,
                                  const rdt_aux* aux, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/*
+ * Per-loop key/value cache for incremental decoding. Generation keeps one cache
+ * per loop iteration, and MLA caches the compressed kv latent instead of full
+ * keys and values (openclawapi Passo 4 and troubleshooting item 1; bigsaas,
+ * MLA vs GQA). Device memory owned by the caller, in the storage type of
+ * cfg.dtype:
+ *   GQA  for each loop t < T: K[t] then V[t], each [batch * max_seq,
+ *        n_kv_heads * head_dim]; row b * max_seq + p holds the key (after RoPE)
+ *        and the value of position p of sequence b as loop t computed them.
+ *   MLA  for each loop t < T: L[t] [batch * max_seq, kv_lora_rank +
+ *        qk_rope_head_dim]: the RMS-normalised kv latent, then the rotated
+ *        shared rope key.
+ * Rows of positions not yet written are never read. Returns the byte size for
+ * T loops and max_seq positions per sequence (0 on a null or invalid config,
+ * T < 1, T > max_T or max_seq < 1).
+ */
+size_t rdt_cache_size(const rdt_config* cfg, int32_t T, int32_t max_seq);
+
+/*
+ * rdt_recurrent_forward over the cfg.seq prompt tokens of every sequence that
+ * also writes each loop's keys and values (MLA: latents) of positions
+ * 0..seq-1 into `cache` (rdt_cache_size(cfg, T, max_seq) bytes, 256-byte
+ * aligned, max_seq >= seq, T >= 1). Other arguments, workspace and errors are
+ * those of rdt_recurrent_forward.
+ */
+rdt_status rdt_prefill(rdt_handle* h, const float* h0, const float* e, const rdt_weights* w,
+                       int32_t T, float* out, const rdt_aux* aux, void* cache, int32_t max_seq,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of rdt_decode_step for T loops and caches of max_seq
+ * positions (0 on a null handle, T > max_T or max_seq < 1). */
+size_t rdt_decode_workspace_size(const rdt_handle* h, int32_t T, int32_t max_seq);
+
+/*
+ * One decoding step: one new token per sequence, at position pos, runs T loops
+ * (openclawapi Passo 4: generation with a per-loop cache). In loop t the
+ * token's key and value (MLA: latent) go to row b * max_seq + pos of the loop-t
+ * cache and the token attends to rows b * max_seq + 0..pos of it. A prefill of
+ * positions 0..pos-1 (or earlier steps) followed by this step therefore gives
+ * the state rdt_recurrent_forward computes for that position on the whole
+ * sequence (causal attention).
+ *   h0, e, out  float [batch, dim] device, 16-byte aligned: the new token of
+ *               each sequence; out may alias h0 exactly.
+ *   T           loops, 1 <= T <= max_T, the T the cache was filled with.
+ *   pos         0 <= pos < max_seq; positions below pos must already be cached.
+ *   cache       as for rdt_prefill (same T and max_seq).
+ *   aux         optional dumps as for rdt_recurrent_forward, batch rows.
+ *   ws          at least rdt_decode_workspace_size(h, T, max_seq) bytes.
+ * With ACT a token that halts keeps its frozen key and value in the caches of
+ * the remaining loops, so later tokens still see it. Errors as for
+ * rdt_recurrent_forward, plus RDT_E_INVALID for pos or max_seq out of range or
+ * a null or misaligned cache.
+ */
+rdt_status rdt_decode_step(rdt_handle* h, const float* h0, const float* e, const rdt_weights* w,
+                           int32_t T, int32_t pos, void* cache, int32_t max_seq, float* out,
+                           const rdt_aux* aux, void* ws, size_t ws_bytes, void* stream);
+
 /* Stages of one loop iteration, for rdt_profile_forward. */
 typedef enum rdt_stage {
   RDT_STAGE_NORM1 = 0,    /* u = h + e, RMSNorm */

@@ -23,6 +23,7 @@ EXPORTED_SYMBOLS = [
     "rdt_config_default", "rdt_config_validate", "rdt_create", "rdt_destroy",
     "rdt_workspace_size", "rdt_spectral_radius", "rdt_set_graph_mode",
     "rdt_recurrent_forward", "rdt_profile_forward", "rdt_stage_name", "rdt_last_error", "rdt_version",
+    "rdt_cache_size", "rdt_prefill", "rdt_decode_workspace_size", "rdt_decode_step",
 ]
 N_STAGES = 12
 
@@ -90,12 +91,21 @@ def load_library(path: str = LIB_PATH):
     lib.rdt_profile_forward.argtypes = [_vp, _vp, _vp, ctypes.POINTER(RdtWeights), _i32, _vp,
                                         ctypes.POINTER(RdtAux), _vp, ctypes.c_size_t, _vp,
                                         ctypes.POINTER(_f32), ctypes.POINTER(_i32), _i32]
+    lib.rdt_cache_size.argtypes = [ctypes.POINTER(RdtConfig), _i32, _i32]
+    lib.rdt_cache_size.restype = ctypes.c_size_t
+    lib.rdt_prefill.argtypes = [_vp, _vp, _vp, ctypes.POINTER(RdtWeights), _i32, _vp, ctypes.POINTER(RdtAux),
+                                _vp, _i32, _vp, ctypes.c_size_t, _vp]
+    lib.rdt_decode_workspace_size.argtypes = [_vp, _i32, _i32]
+    lib.rdt_decode_workspace_size.restype = ctypes.c_size_t
+    lib.rdt_decode_step.argtypes = [_vp, _vp, _vp, ctypes.POINTER(RdtWeights), _i32, _i32, _vp, _i32, _vp,
+                                    ctypes.POINTER(RdtAux), _vp, ctypes.c_size_t, _vp]
     lib.rdt_stage_name.argtypes = [_i32]
     lib.rdt_stage_name.restype = ctypes.c_char_p
     lib.rdt_last_error.restype = ctypes.c_char_p
     lib.rdt_version.restype = ctypes.c_char_p
     for name in ["rdt_config_default", "rdt_config_validate", "rdt_create", "rdt_spectral_radius",
-                 "rdt_set_graph_mode", "rdt_recurrent_forward", "rdt_profile_forward"]:
+                 "rdt_set_graph_mode", "rdt_recurrent_forward", "rdt_profile_forward", "rdt_prefill",
+                 "rdt_decode_step"]:
         getattr(lib, name).restype = _i32
     _lib = lib
     return lib
@@ -205,6 +215,61 @@ class RecurrentBlock:
         """Kernel-by-kernel forward with HIP events around every launch.
         Returns (out, {stage name: (device ms, launches)}); waits for the GPU."""
         return self._run(True, h0, e, weights, T, out, aux, workspace, stream)
+
+    # ---------------------------------------------------------------- decode
+    def cache_size(self, T: int, max_seq: int) -> int:
+        """Bytes of the per-loop K/V (MLA: latent) cache."""
+        return int(self.lib.rdt_cache_size(ctypes.byref(self.c), int(T), int(max_seq)))
+
+    def new_cache(self, T: int, max_seq: int, device="cuda"):
+        import torch
+        n = self.cache_size(T, max_seq)
+        if n == 0:
+            raise RdtError(RDT_E_INVALID, "invalid cache shape")
+        return torch.empty(n, dtype=torch.uint8, device=device)
+
+    def prefill(self, h0, e, weights: dict, T: int, cache, max_seq: int, out=None, aux: dict | None = None,
+                workspace=None, stream=None):
+        """Forward over the prompt that also fills the per-loop cache."""
+        import torch
+        if out is None:
+            out = torch.empty_like(h0)
+        w, a = self._structs(weights, aux)
+        ws = self.workspace(T, h0.device) if workspace is None else workspace
+        stream = torch.cuda.current_stream(h0.device).cuda_stream if stream is None else stream
+        _check(self.lib.rdt_prefill(self.h, _ptr(h0), _ptr(e), ctypes.byref(w), int(T), _ptr(out), ctypes.byref(a),
+                                    _ptr(cache), int(max_seq), _ptr(ws), ws.numel(), stream))
+        return out
+
+    def decode_workspace_size(self, T: int, max_seq: int) -> int:
+        return int(self.lib.rdt_decode_workspace_size(self.h, int(T), int(max_seq)))
+
+    def decode_step(self, h0, e, weights: dict, T: int, pos: int, cache, max_seq: int, out=None,
+                    aux: dict | None = None, workspace=None, stream=None):
+        """One new token per sequence ([batch, dim] state) at position pos."""
+        import torch
+        if out is None:
+            out = torch.empty_like(h0)
+        w, a = self._structs(weights, aux)
+        if workspace is None:
+            need = self.decode_workspace_size(T, max_seq)
+            if getattr(self, "_dws", None) is None or self._dws.numel() < need:
+                self._dws = torch.empty(max(need, 256), dtype=torch.uint8, device=h0.device)
+            workspace = self._dws
+        stream = torch.cuda.current_stream(h0.device).cuda_stream if stream is None else stream
+        _check(self.lib.rdt_decode_step(self.h, _ptr(h0), _ptr(e), ctypes.byref(w), int(T), int(pos), _ptr(cache),
+                                        int(max_seq), _ptr(out), ctypes.byref(a), _ptr(workspace),
+                                        workspace.numel(), stream))
+        return out
+
+    def _structs(self, weights, aux):
+        w = RdtWeights()
+        for name in WEIGHT_FIELDS:
+            setattr(w, name, _ptr(weights.get(name)))
+        a = RdtAux()
+        for name in AUX_FIELDS:
+            setattr(a, name, _ptr((aux or {}).get(name)))
+        return w, a
 
     def _run(self, profile, h0, e, weights, T, out, aux, workspace, stream):
         import torch

@@ -41,8 +41,10 @@ static rdt_status set_err(rdt_status st, const std::string& msg) {
 
 struct GraphKey {
   const void* ptrs[48];
-  int T;
-  bool operator==(const GraphKey& o) const { return T == o.T && memcmp(ptrs, o.ptrs, sizeof(ptrs)) == 0; }
+  int T, max_seq, decode;
+  bool operator==(const GraphKey& o) const {
+    return T == o.T && max_seq == o.max_seq && decode == o.decode && memcmp(ptrs, o.ptrs, sizeof(ptrs)) == 0;
+  }
 };
 
 struct GraphEntry {
@@ -145,6 +147,11 @@ struct Fwd {
   float* out;
   rdt_aux aux;
   char* ws;
+  // per-loop cache: prefill writes positions 0..S-1, a decode step (decode = 1,
+  // one token per sequence, position read from the workspace) appends one row
+  char* cache = nullptr;
+  int max_seq = 0;
+  int decode = 0;
 };
 
 // Event pairs around launches (rdt_profile_forward only).
@@ -207,7 +214,19 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   }
   float* cosb = at<float>(ws, P.cosb);
   float* sinb = at<float>(ws, P.sinb);
-  LAUNCH(RDT_STAGE_OTHER, launch_rope_tables(cosb, sinb, P.S, P.dr, c.rope_base, s));
+  LAUNCH(RDT_STAGE_OTHER, launch_rope_tables(cosb, sinb, P.rope_len, P.dr, c.rope_base, s));
+  int* pos_dev = f.decode ? at<int>(ws, P.pos) : nullptr;
+  // loop t's cache: GQA keys then values, or MLA latents (rows b*max_seq + p)
+  const size_t crow = P.mla ? (size_t)(P.kvl + P.nr) : (size_t)P.KV * P.d;  // elements per row
+  const size_t cplane = (size_t)P.B * f.max_seq * crow * elt;                 // bytes per array per loop
+  auto cache_at = [&](int t, int which) { return f.cache + ((size_t)t * (P.mla ? 1 : 2) + which) * cplane; };
+  // rows of this call's K/V (or latent) buffer -> cache rows
+  auto append = [&](int t, int which, const char* src) -> hipError_t {
+    if (!f.cache) return hipSuccess;
+    const int s_in = f.decode ? 1 : P.S;
+    return launch_rows_scatter(cache_at(t, which), (long long)crow * elt, src, (long long)crow * elt,
+                               (int)(crow * elt), N, s_in, f.max_seq, pos_dev, s);
+  };
   if (P.mla) LAUNCH(RDT_STAGE_OTHER, launch_head_transpose(dt, at<char>(ws, P.wukT), w.Wuk, P.H, P.nope, P.kvl, s));
 
   int* lists = at<int>(ws, P.lists);
@@ -285,7 +304,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       GemmSeg sv{w.Wv, KVd, vb, KVd, 1, 0, 0};
       DenseGemm g{};
       g.dtype = dt; g.A = n1; g.lda = D; g.K = D; g.batch = 1;
-      g.cosb = cosb; g.sinb = sinb; g.rope_dim = P.d; g.seq = P.S; g.epi = EPI_STORE;
+      g.cosb = cosb; g.sinb = sinb; g.rope_dim = P.d; g.seq = P.S; g.epi = EPI_STORE; g.pos_dev = pos_dev;
       g.M = N;
       if (!act) {
         g.rows = nullptr; g.gather = 0; g.Mdev = nullptr;
@@ -302,13 +321,16 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
         pick_tile(N, 2 * KVd, P.d, &gkv.bm, &gkv.bn);
         LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(gkv, s));
       }
+      LAUNCH(RDT_STAGE_QKV, append(t, 0, kb));
+      LAUNCH(RDT_STAGE_QKV, append(t, 1, vb));
       AttnArgs aa{};
       aa.dtype = dt; aa.dqk = P.d; aa.dv = P.d;
       aa.q = q; aa.q_ld = Hd; aa.q_hs = P.d;
-      aa.k = kb; aa.k_ld = KVd; aa.k_hs = P.d;
-      aa.v = vb; aa.v_ld = KVd; aa.v_hs = P.d;
+      aa.k = f.decode ? cache_at(t, 0) : kb; aa.k_ld = KVd; aa.k_hs = P.d;
+      aa.v = f.decode ? cache_at(t, 1) : vb; aa.v_ld = KVd; aa.v_hs = P.d;
       aa.o = o; aa.o_ld = Hd; aa.o_hs = P.d;
-      aa.H = P.H; aa.KV = P.KV; aa.rows = cur; aa.seg = seg; aa.B = P.B; aa.S = P.S;
+      aa.H = P.H; aa.KV = P.KV; aa.rows = cur; aa.seg = seg; aa.B = P.B;
+      aa.S = f.decode ? f.max_seq : P.S; aa.dec = f.decode; aa.dec_pos = pos_dev;
       aa.scale = 1.f / sqrtf((float)P.d);
       LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, s));
     } else {
@@ -334,8 +356,9 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       mn.dtype = dt; mn.cq_raw = (const float*)cq_raw; mn.ql = P.ql; mn.lat_raw = (const float*)lat_raw;
       mn.kvl = P.kvl; mn.nr = P.nr; mn.gq = w.gq; mn.gkv = w.gkv; mn.eps = c.norm_eps;
       mn.rows = prev; mn.ndev = nprev; mn.n = N; mn.cqn = cqn; mn.latent = latent;
-      mn.cosb = cosb; mn.sinb = sinb; mn.S = P.S;
+      mn.cosb = cosb; mn.sinb = sinb; mn.S = P.S; mn.pos_dev = pos_dev;
       LAUNCH(RDT_STAGE_QKV, launch_mla_norm(mn, s));
+      LAUNCH(RDT_STAGE_QKV, append(t, 0, latent));
       // query up-projection (compacted rows)
       DenseGemm g2{};
       g2.dtype = dt; g2.A = cqn; g2.lda = P.ql; g2.K = P.ql; g2.batch = 1; g2.epi = EPI_STORE;
@@ -355,15 +378,17 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       qr.dtype = dt; qr.src = qfull; qr.src_ld = P.H * qw; qr.src_hs = qw; qr.src_off = P.nope;
       qr.dst = qattn; qr.dst_ld = P.H * W; qr.dst_hs = W; qr.dst_off = P.kvl;
       qr.H = P.H; qr.nr = P.nr; qr.rows = cur; qr.ndev = ncur; qr.n = N;
-      qr.cosb = cosb; qr.sinb = sinb; qr.S = P.S;
+      qr.cosb = cosb; qr.sinb = sinb; qr.S = P.S; qr.pos_dev = pos_dev;
       LAUNCH(RDT_STAGE_QKV, launch_qrope(qr, s));
       AttnArgs aa{};
       aa.dtype = dt; aa.dqk = W; aa.dv = P.kvl;
       aa.q = qattn; aa.q_ld = P.H * W; aa.q_hs = W;
-      aa.k = latent; aa.k_ld = W; aa.k_hs = 0;
-      aa.v = latent; aa.v_ld = W; aa.v_hs = 0;
+      const char* lat_src = f.decode ? cache_at(t, 0) : latent;
+      aa.k = lat_src; aa.k_ld = W; aa.k_hs = 0;
+      aa.v = lat_src; aa.v_ld = W; aa.v_hs = 0;
       aa.o = olat; aa.o_ld = P.H * P.kvl; aa.o_hs = P.kvl;
-      aa.H = P.H; aa.KV = 1; aa.rows = cur; aa.seg = seg; aa.B = P.B; aa.S = P.S;
+      aa.H = P.H; aa.KV = 1; aa.rows = cur; aa.seg = seg; aa.B = P.B;
+      aa.S = f.decode ? f.max_seq : P.S; aa.dec = f.decode; aa.dec_pos = pos_dev;
       aa.scale = 1.f / sqrtf((float)(P.nope + P.nr));
       LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, s));
       // value up-projection per head: o[h] = o_lat[h] . Wuv[h]^T
@@ -504,16 +529,18 @@ static rdt_status check_rho(rdt_handle* h, const float* A, hipStream_t s) {
   return RDT_OK;
 }
 
-// Argument checks shared by the forward entry points; fills *f.
+// Argument checks shared by the forward entry points; fills *f. `rows` is the
+// number of state rows (batch*seq for a forward, batch for a decode step).
 static rdt_status prepare(rdt_handle* h, const float* h0, const float* e, const rdt_weights* w, int32_t T,
-                          float* out, const rdt_aux* aux, void* ws, size_t ws_bytes, Fwd& f) {
+                          float* out, const rdt_aux* aux, void* ws, size_t ws_bytes, Fwd& f, bool decode = false,
+                          int max_seq = 0) {
   if (!h) return set_err(RDT_E_INVALID, "null handle");
   const rdt_config& c = h->cfg;
   if (T < 0 || T > c.max_T) return set_err(RDT_E_INVALID, "T must be in [0, max_T]");
   if (!h0 || !e || !out) return set_err(RDT_E_INVALID, "null h0, e or out");
   if (misaligned(h0, 16) || misaligned(e, 16) || misaligned(out, 16))
     return set_err(RDT_E_INVALID, "h0, e and out must be 16-byte aligned");
-  const size_t bytes = (size_t)c.batch * c.seq * c.dim * 4;
+  const size_t bytes = (size_t)c.batch * (decode ? 1 : c.seq) * c.dim * 4;
   auto overlap = [&](const void* a, const void* b) {
     const char* x = (const char*)a;
     const char* y = (const char*)b;
@@ -525,11 +552,66 @@ static rdt_status prepare(rdt_handle* h, const float* h0, const float* e, const 
   if (st != RDT_OK) return st;
   f = Fwd{};
   f.c = &h->cfg;
-  f.P = make_plan(c, T);
+  f.P = decode ? make_decode_plan(c, T, max_seq) : make_plan(c, T);
   if (!ws || ws_bytes < f.P.total) return set_err(RDT_E_WORKSPACE, "workspace missing or too small");
   if (misaligned(ws, 256)) return set_err(RDT_E_INVALID, "workspace must be 256-byte aligned");
   f.h0 = h0; f.e = e; f.w = w; f.T = T; f.out = out; f.ws = (char*)ws;
+  f.decode = decode ? 1 : 0;
+  f.max_seq = max_seq;
   if (aux) f.aux = *aux;
+  return RDT_OK;
+}
+
+// Cache arguments of rdt_prefill / rdt_decode_step.
+static rdt_status check_cache(rdt_handle* h, int32_t T, void* cache, int32_t max_seq, int32_t need_seq) {
+  if (max_seq <= 0 || max_seq < need_seq) return set_err(RDT_E_INVALID, "max_seq too small");
+  if (T < 1) return set_err(RDT_E_INVALID, "a cache needs T >= 1");
+  if (!cache) return set_err(RDT_E_INVALID, "null cache");
+  if (misaligned(cache, 256)) return set_err(RDT_E_INVALID, "cache must be 256-byte aligned");
+  if ((long long)h->cfg.batch * max_seq > (1ll << 30)) return set_err(RDT_E_UNSUPPORTED, "cache too long");
+  return RDT_OK;
+}
+
+// Enqueue f on s: replay (capturing on first use) the HIP graph of this
+// argument set, or launch the kernels one by one when graphs are off.
+static rdt_status launch(rdt_handle* h, const Fwd& f, hipStream_t s) {
+  if (!h->graph_mode || f.T == 0) return enqueue(f, s);
+  GraphKey key{};
+  int nk = 0;
+  const void* const* wv = reinterpret_cast<const void* const*>(f.w);
+  for (size_t i = 0; i < sizeof(rdt_weights) / sizeof(void*); ++i) key.ptrs[nk++] = wv[i];
+  const void* const* av = reinterpret_cast<const void* const*>(&f.aux);
+  for (size_t i = 0; i < sizeof(rdt_aux) / sizeof(void*); ++i) key.ptrs[nk++] = av[i];
+  key.ptrs[nk++] = f.h0; key.ptrs[nk++] = f.e; key.ptrs[nk++] = f.out; key.ptrs[nk++] = f.ws;
+  key.ptrs[nk++] = f.cache;
+  key.T = f.T; key.max_seq = f.max_seq; key.decode = f.decode;
+  for (auto& g : h->graphs)
+    if (g.key == key) {
+      HIPCHK(hipGraphLaunch(g.exec, s));
+      return RDT_OK;
+    }
+  HIPCHK(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
+  rdt_status st = enqueue(f, h->cap);
+  hipGraph_t graph = nullptr;
+  hipError_t ce = hipStreamEndCapture(h->cap, &graph);
+  if (st != RDT_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st;
+  }
+  if (ce != hipSuccess) return set_err(RDT_E_HIP, std::string("graph capture failed: ") + hipGetErrorString(ce));
+  hipGraphExec_t exec = nullptr;
+  ce = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (ce != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return set_err(RDT_E_HIP, std::string("graph instantiate failed: ") + hipGetErrorString(ce));
+  }
+  if (h->graphs.size() >= 16) {
+    (void)hipGraphExecDestroy(h->graphs.front().exec);
+    (void)hipGraphDestroy(h->graphs.front().graph);
+    h->graphs.erase(h->graphs.begin());
+  }
+  h->graphs.push_back(GraphEntry{key, graph, exec});
+  HIPCHK(hipGraphLaunch(exec, s));
   return RDT_OK;
 }
 
@@ -575,44 +657,51 @@ extern "C" rdt_status rdt_recurrent_forward(rdt_handle* h, const float* h0, cons
   hipStream_t s = (hipStream_t)stream;
   st = check_rho(h, w->A, s);
   if (st != RDT_OK) return st;
-  if (!h->graph_mode || T == 0) return enqueue(f, s);
+  return launch(h, f, s);
+}
 
-  GraphKey key{};
-  int nk = 0;
-  const void* wp = w;
-  (void)wp;
-  const void* const* wv = reinterpret_cast<const void* const*>(w);
-  for (size_t i = 0; i < sizeof(rdt_weights) / sizeof(void*); ++i) key.ptrs[nk++] = wv[i];
-  const void* const* av = reinterpret_cast<const void* const*>(&f.aux);
-  for (size_t i = 0; i < sizeof(rdt_aux) / sizeof(void*); ++i) key.ptrs[nk++] = av[i];
-  key.ptrs[nk++] = h0; key.ptrs[nk++] = e; key.ptrs[nk++] = out; key.ptrs[nk++] = ws;
-  key.T = T;
-  for (auto& g : h->graphs)
-    if (g.key == key) {
-      HIPCHK(hipGraphLaunch(g.exec, s));
-      return RDT_OK;
-    }
-  HIPCHK(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
-  st = enqueue(f, h->cap);
-  hipGraph_t graph = nullptr;
-  hipError_t ce = hipStreamEndCapture(h->cap, &graph);
-  if (st != RDT_OK) {
-    if (graph) (void)hipGraphDestroy(graph);
-    return st;
-  }
-  if (ce != hipSuccess) return set_err(RDT_E_HIP, std::string("graph capture failed: ") + hipGetErrorString(ce));
-  hipGraphExec_t exec = nullptr;
-  ce = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-  if (ce != hipSuccess) {
-    (void)hipGraphDestroy(graph);
-    return set_err(RDT_E_HIP, std::string("graph instantiate failed: ") + hipGetErrorString(ce));
-  }
-  if (h->graphs.size() >= 16) {
-    (void)hipGraphExecDestroy(h->graphs.front().exec);
-    (void)hipGraphDestroy(h->graphs.front().graph);
-    h->graphs.erase(h->graphs.begin());
-  }
-  h->graphs.push_back(GraphEntry{key, graph, exec});
-  HIPCHK(hipGraphLaunch(exec, s));
-  return RDT_OK;
+extern "C" size_t rdt_cache_size(const rdt_config* cfg, int32_t T, int32_t max_seq) {
+  if (!cfg || validate_config(*cfg, nullptr) != RDT_OK || T > cfg->max_T) return 0;
+  return cache_bytes(*cfg, T, max_seq);
+}
+
+extern "C" rdt_status rdt_prefill(rdt_handle* h, const float* h0, const float* e, const rdt_weights* w, int32_t T,
+                                  float* out, const rdt_aux* aux, void* cache, int32_t max_seq, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  if (!h) return set_err(RDT_E_INVALID, "null handle");
+  rdt_status st = check_cache(h, T, cache, max_seq, h->cfg.seq);
+  if (st != RDT_OK) return st;
+  Fwd f;
+  st = prepare(h, h0, e, w, T, out, aux, ws, ws_bytes, f);
+  if (st != RDT_OK) return st;
+  f.cache = (char*)cache;
+  f.max_seq = max_seq;
+  hipStream_t s = (hipStream_t)stream;
+  st = check_rho(h, w->A, s);
+  if (st != RDT_OK) return st;
+  return launch(h, f, s);
+}
+
+extern "C" size_t rdt_decode_workspace_size(const rdt_handle* h, int32_t T, int32_t max_seq) {
+  if (!h || T < 0 || T > h->cfg.max_T || max_seq <= 0) return 0;
+  return make_decode_plan(h->cfg, T, max_seq).total;
+}
+
+extern "C" rdt_status rdt_decode_step(rdt_handle* h, const float* h0, const float* e, const rdt_weights* w,
+                                      int32_t T, int32_t pos, void* cache, int32_t max_seq, float* out,
+                                      const rdt_aux* aux, void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return set_err(RDT_E_INVALID, "null handle");
+  rdt_status st = check_cache(h, T, cache, max_seq, 1);
+  if (st != RDT_OK) return st;
+  if (pos < 0 || pos >= max_seq) return set_err(RDT_E_INVALID, "pos must be in [0, max_seq)");
+  Fwd f;
+  st = prepare(h, h0, e, w, T, out, aux, ws, ws_bytes, f, true, max_seq);
+  if (st != RDT_OK) return st;
+  f.cache = (char*)cache;
+  hipStream_t s = (hipStream_t)stream;
+  st = check_rho(h, w->A, s);
+  if (st != RDT_OK) return st;
+  // the position lives in the workspace, so one captured graph serves every step
+  HIPCHK(launch_fill_i32(reinterpret_cast<int*>(f.ws + f.P.pos), pos, 1, s));
+  return launch(h, f, s);
 }

@@ -49,13 +49,16 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   const int slice = wave / NHB;
   const int kvh = (h * a.KV) / a.H;
   const int S = a.S;
-  const int seg0 = a.seg ? a.seg[b] : b * S;
-  const int seglen = a.seg ? a.seg[b + 1] - seg0 : S;
+  // token of query row x: its cache row in decode, else the token itself
+  const int dpos = a.dec ? *a.dec_pos : 0;
+  auto tok = [&](int x) { return a.dec ? (a.rows ? a.rows[x] : x) * S + dpos : (a.rows ? a.rows[x] : x); };
+  const int seg0 = a.seg ? a.seg[b] : (a.dec ? b : b * S);
+  const int seglen = a.seg ? a.seg[b + 1] - seg0 : (a.dec ? 1 : S);
   if (qt * BQ >= seglen) return;
   const int blk_first = seg0 + qt * BQ;
   const int blk_n = min(BQ, seglen - qt * BQ);
   const int last = blk_first + blk_n - 1;
-  const int kmax = (a.rows ? a.rows[last] : last) - b * S + 1;  // keys 0..kmax-1
+  const int kmax = tok(last) - b * S + 1;  // keys 0..kmax-1
   const int qfirst = blk_first + slice * QW;
   const int nq = max(0, min(QW, blk_n - slice * QW));  // this wave's query rows
 
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     const int qq = qs * 16 + lc;
     const bool valid = qq < nq;
     const int i = qfirst + qq;
-    qpos[qs] = valid ? (a.rows ? a.rows[i] : i) - b * S : -1;
+    qpos[qs] = valid ? tok(i) - b * S : -1;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = ks * 32 + lg * 8;
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 template <typename T, int DQK, int DV, int QW, int NHB>
 static hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
   constexpr int BQ = QW * (4 / NHB);
-  dim3 grid((a.S + BQ - 1) / BQ, a.B, a.H / NHB);
+  dim3 grid(a.dec ? 1 : (a.S + BQ - 1) / BQ, a.B, a.H / NHB);
   hipLaunchKernelGGL((k_attention<T, DQK, DV, QW, NHB>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -292,7 +295,7 @@ template <typename T, int DQK, int DV>
 static hipError_t attn_pick(const AttnArgs& a, hipStream_t s) {
   const int G = a.H / a.KV;
   const int nhb = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
-  const long long blocks16 = (long long)((a.S + 63) / 64) * a.B * a.H;  // 64 rows per block per head
+  const long long blocks16 = (long long)(a.dec ? 1 : (a.S + 63) / 64) * a.B * a.H;  // 64 rows per block per head
   const bool wide = DQK <= 64 && blocks16 * 2 >= 1024;
   if (nhb == 4) return wide ? attn_launch<T, DQK, DV, 32, 4>(a, s) : attn_launch<T, DQK, DV, 16, 4>(a, s);
   if (nhb == 2) return wide ? attn_launch<T, DQK, DV, 32, 2>(a, s) : attn_launch<T, DQK, DV, 16, 2>(a, s);

@@ -412,7 +412,7 @@ __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
         for (int x = 0; x < 8; ++x) v[x] = crow[c8 + x];
         if (sg.rope) {
           const int rd = g.rope_dim, half = rd >> 1;
-          const int pos = tok % g.seq;
+          const int pos = g.pos_dev ? *g.pos_dev : tok % g.seq;
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
             const int hd = (lc + x) % rd;

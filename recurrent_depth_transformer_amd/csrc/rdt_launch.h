@@ -58,6 +58,7 @@ struct DenseGemm {
   const float* cosb; const float* sinb; int rope_dim; int seq;
   int epi;
   RouterEpi router;
+  const int* pos_dev;    // RoPE at position *pos_dev for every row (one-token decode), else token % seq
   int bm, bn;            // tile shape (64 or 128 each)
   int ns;                // bf16 pipeline stages (2..4; 0 = default)
 };
@@ -96,6 +97,10 @@ struct AttnArgs {
   const int* seg;        // [B+1] start of each sequence in the query list (null: b*S)
   int B, S;
   float scale;           // softmax scale (multiplies q.k)
+  // one-token decode: query row i is slot s = rows[i] (or i) at position
+  // *dec_pos, its keys are rows s*S .. s*S + *dec_pos of the K/V cache (S is
+  // the cache length), and sequence b of the grid is slot b
+  int dec; const int* dec_pos;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
@@ -158,6 +163,7 @@ struct MlaNormArgs {
   const int* rows; const int* ndev; int n;
   void* cqn; void* latent;            // T [N, ql], T [N, kvl+nr] by token
   const float* cosb; const float* sinb; int S;
+  const int* pos_dev;                 // RoPE at position *pos_dev for every row (decode)
 };
 hipError_t launch_mla_norm(const MlaNormArgs& a, hipStream_t s);
 
@@ -168,6 +174,7 @@ struct QRopeArgs {
   int H, nr;
   const int* rows; const int* ndev; int n;
   const float* cosb; const float* sinb; int S;
+  const int* pos_dev;
 };
 hipError_t launch_qrope(const QRopeArgs& a, hipStream_t s);
 
@@ -178,6 +185,12 @@ hipError_t launch_fill_f32(float* p, float v, long long n, hipStream_t s);
 hipError_t launch_fill_u16(uint16_t* p, uint16_t v, long long n, hipStream_t s);
 hipError_t launch_iota(int* p, int n, int* count, int count_val, int* seg, int B, int S, hipStream_t s);
 hipError_t launch_copy_f32(float* dst, const float* src, long long n, hipStream_t s);
+// dst row (r / s_in) * s_out + r % s_in + pos0 <- src row r, for r < nrows,
+// with pos0 = *pos_dev (or 0 when null): copies rows of `bytes` bytes (a
+// multiple of 16) between strided buffers. Appends per-token K/V or latent
+// rows to a per-loop cache.
+hipError_t launch_rows_scatter(void* dst, long long dst_ld, const void* src, long long src_ld, int bytes, int nrows,
+                               int s_in, int s_out, const int* pos_dev, hipStream_t s);
 // dst[h][c][i] = src[h*rows + i][c]: per-head transpose of an [H*rows, cols] matrix
 hipError_t launch_head_transpose(int dtype, void* dst, const void* src, int H, int rows, int cols,
                                  hipStream_t s);

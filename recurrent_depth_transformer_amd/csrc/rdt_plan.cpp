@@ -122,8 +122,31 @@ Plan make_plan(const rdt_config& c, int T) {
   p.seg = take(Tp * (p.B + 1) * 4);
   p.cum = take(N * 4);
   p.done = take(4);
+  p.pos = take(4);
+  p.rope_len = p.S;
   p.total = off;
   return p;
+}
+
+Plan make_decode_plan(const rdt_config& c, int T, int max_seq) {
+  rdt_config d = c;
+  d.seq = 1;
+  Plan p = make_plan(d, T);
+  size_t off = p.total;
+  auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+  p.cosb = take((size_t)max_seq * (p.dr / 2) * 4);
+  p.sinb = take((size_t)max_seq * (p.dr / 2) * 4);
+  p.rope_len = max_seq;
+  p.total = off;
+  return p;
+}
+
+size_t cache_bytes(const rdt_config& c, int T, int max_seq) {
+  if (T <= 0 || max_seq <= 0) return 0;
+  const size_t elt = c.dtype == RDT_F32 ? 4 : 2;
+  const size_t row = c.attn_type == RDT_ATTN_MLA ? (size_t)(c.kv_lora_rank + c.qk_rope_head_dim)
+                                                 : (size_t)2 * c.n_kv_heads * c.head_dim;
+  return (size_t)T * c.batch * max_seq * row * elt;
 }
 
 }  // namespace rdt

@@ -26,6 +26,8 @@ struct Plan {
   size_t hmid, y;
   size_t lists, ncount, seg, cum;
   size_t done;              // completion counter of the fused router kernel
+  size_t pos;               // decode position (one int, written before each step)
+  int rope_len;             // positions in the RoPE tables
   size_t total;
 };
 
@@ -34,5 +36,10 @@ rdt_status validate_config(const rdt_config& c, std::string* why);
 
 // Layout for loop counts up to T (T >= 0). Requires a validated config.
 Plan make_plan(const rdt_config& c, int T);
+// Plan of one decoding step: batch slots of one token each, RoPE tables for
+// max_seq positions.
+Plan make_decode_plan(const rdt_config& c, int T, int max_seq);
+// Bytes of the per-loop cache for T loops and max_seq positions (0 if invalid).
+size_t cache_bytes(const rdt_config& c, int T, int max_seq);
 
 }  // namespace rdt

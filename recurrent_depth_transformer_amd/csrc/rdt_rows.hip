@@ -486,7 +486,7 @@ __global__ __launch_bounds__(256) void k_mla_norm(MlaNormArgs a) {
     for (int c = lane; c < a.kvl; c += 64) dst[c] = ST<T>::from_f(src[c] * inv * a.gkv[c]);
   }
   const int half = a.nr >> 1;
-  const int pos = tok % a.S;
+  const int pos = a.pos_dev ? *a.pos_dev : tok % a.S;
   for (int j = lane; j < half; j += 64) {
     const float x1 = src[a.kvl + j], x2 = src[a.kvl + j + half];
     const float cs = a.cosb[pos * half + j], sn = a.sinb[pos * half + j];
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(256) void k_qrope(QRopeArgs a) {
   const int rem = (int)(gid % per_row);
   const int h = rem / half, j = rem % half;
   const int tok = a.rows ? a.rows[i] : i;
-  const int pos = tok % a.S;
+  const int pos = a.pos_dev ? *a.pos_dev : tok % a.S;
   const T* s = reinterpret_cast<const T*>(a.src) + (long long)i * a.src_ld + (long long)h * a.src_hs + a.src_off;
   T* d = reinterpret_cast<T*>(a.dst) + (long long)i * a.dst_ld + (long long)h * a.dst_hs + a.dst_off;
   const float x1 = ST<T>::to_f(s[j]), x2 = ST<T>::to_f(s[j + half]);
@@ -601,6 +601,31 @@ hipError_t launch_copy_f32(float* dst, const float* src, long long n, hipStream_
   const long long n4 = n / 4;  // callers pass multiples of 4
   hipLaunchKernelGGL(k_copy_f32, dim3(fill_blocks(n4)), dim3(256), 0, s, reinterpret_cast<float4*>(dst),
                      reinterpret_cast<const float4*>(src), n4);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ row scatter
+__global__ __launch_bounds__(256) void k_rows_scatter(char* dst, long long dst_ld, const char* src, long long src_ld,
+                                                      int vecs, int nrows, int s_in, int s_out, const int* pos_dev) {
+  const int pos0 = pos_dev ? *pos_dev : 0;
+  const long long n = (long long)nrows * vecs;
+  for (long long x = blockIdx.x * 256ll + threadIdx.x; x < n; x += (long long)gridDim.x * 256) {
+    const int r = (int)(x / vecs), v = (int)(x % vecs);
+    const long long dr = (long long)(r / s_in) * s_out + r % s_in + pos0;
+    *reinterpret_cast<uint4*>(dst + dr * dst_ld + v * 16) =
+        *reinterpret_cast<const uint4*>(src + (long long)r * src_ld + v * 16);
+  }
+}
+
+hipError_t launch_rows_scatter(void* dst, long long dst_ld, const void* src, long long src_ld, int bytes, int nrows,
+                               int s_in, int s_out, const int* pos_dev, hipStream_t s) {
+  if (nrows <= 0) return hipSuccess;
+  if (bytes % 16 || s_in <= 0) return hipErrorInvalidValue;
+  const int vecs = bytes / 16;
+  const long long n = (long long)nrows * vecs;
+  const int blocks = (int)(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
+  hipLaunchKernelGGL(k_rows_scatter, dim3(blocks), dim3(256), 0, s, (char*)dst, dst_ld, (const char*)src, src_ld,
+                     vecs, nrows, s_in, s_out, pos_dev);
   return hipGetLastError();
 }
 

@@ -111,3 +111,40 @@ def test_null_handle_paths(lib):
     assert lib.rdt_set_graph_mode(None, 1) == rdt.RDT_E_INVALID
     lib.rdt_destroy(None)
     assert lib.rdt_version().decode().startswith("librdt")
+
+
+@pytest.mark.parametrize("name", ["gqa", "mla", "wide_moe", "act", "tiny", "mla_small"])
+def test_cache_size_matches_oracle_bytes(lib, name):
+    """rdt_cache_size is T x batch x max_seq rows of the per-token cache the
+    oracle states (GQA: K and V of the kv heads; MLA: latent + rope key)."""
+    from oracle import rdt_oracle
+    cfg = get_config(name)
+    c = rdt.make_config(cfg)
+    T, max_seq = cfg["T"], 333
+    elt = 4 if cfg["dtype"] == "f32" else 2
+    per_tok = rdt_oracle.kv_cache_bytes_per_token(cfg, elem_bytes=elt)
+    assert lib.rdt_cache_size(ctypes.byref(c), T, max_seq) == T * cfg["batch"] * max_seq * per_tok
+    assert lib.rdt_cache_size(ctypes.byref(c), 0, max_seq) == 0
+    assert lib.rdt_cache_size(ctypes.byref(c), T, 0) == 0
+    assert lib.rdt_cache_size(None, T, max_seq) == 0
+
+
+def test_mla_cache_saving_measured(lib):
+    """The MLA cache the library allocates is 16x smaller than full per-head
+    keys and values of the same model (the pages claim 10-20x)."""
+    import json
+    facts = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")))
+    lo, hi = facts["mla_kv_saving_range"]["value"]
+    cfg = get_config("mla")
+    c = rdt.make_config(cfg)
+    T, max_seq = cfg["T"], 1024
+    got = lib.rdt_cache_size(ctypes.byref(c), T, max_seq)
+    H = cfg["n_heads"]
+    full = T * cfg["batch"] * max_seq * H * ((cfg["qk_nope_head_dim"] + cfg["qk_rope_head_dim"]) + cfg["v_head_dim"]) * 2
+    assert lo <= full / got <= hi
+
+
+def test_decode_null_paths(lib):
+    assert lib.rdt_decode_workspace_size(None, 3, 64) == 0
+    assert lib.rdt_decode_step(None, None, None, None, 1, 0, None, 8, None, None, None, 0, None) == rdt.RDT_E_INVALID
+    assert lib.rdt_prefill(None, None, None, None, 1, None, None, None, 8, None, 0, None) == rdt.RDT_E_INVALID
