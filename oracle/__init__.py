@@ -24,7 +24,8 @@ Sources (the web pages on OpenMythos and on depth-recurrent attention mixtures):
 Pinned by tests/test_oracle_pins.py (closed form of the injection, T=1 against an
 independent torch block, GQA = MHA, k = E dense MoE, MLA explicit = absorbed,
 float64 scalar brute force, causality, RoPE relativity, router invariants, ACT
-special cases, LoRA merge). Parity unpinned: nothing on the pages prints a value
+special cases, LoRA merge; the router-bias update on hand-worked counts and
+on the dead-expert case of troubleshooting item 5). Parity unpinned: nothing on the pages prints a value
 of a full random-weight block, so beyond those pins the oracle is its own
 reference.
 """
@@ -32,4 +33,5 @@ from .rdt_oracle import (  # noqa: F401
     rmsnorm, rope_tables, apply_rope, attention_causal, gqa_attention,
     mla_attention_explicit, swiglu, route, moe, block_step, forward,
     spectral_radius, kv_cache_bytes_per_token, step_rows,
+    bias_row_counts, router_bias_update, expert_depths,
 )

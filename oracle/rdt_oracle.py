@@ -384,3 +384,41 @@ def step_rows(cfg, W, h, e, t, rows, forced_idx_rows, tables=None):
     m = moe(n2, idx, gates, W, cfg["n_shared_experts"])
     h_new = np.asarray(W["A"], F64) * h[rows] + np.asarray(W["B"], F64) * e[rows] + a + m
     return h_new, a, n2
+
+
+# ----------------------------------------------------------------------------
+# between forwards: router-bias balancing and expert depth usage
+# ----------------------------------------------------------------------------
+def bias_row_counts(counts, rows):
+    """Tokens per expert seen by each router-bias row: loop t selects with row
+    min(t, rows-1), so row r sums the counts of those loops. counts: [T, E]."""
+    counts = np.asarray(counts, np.int64)
+    T, E = counts.shape
+    out = np.zeros((rows, E), np.int64)
+    for t in range(T):
+        out[min(t, rows - 1)] += counts[t]
+    return out
+
+
+def router_bias_update(counts, bias, gamma):
+    """Auxiliary-loss-free load balancing (openclawapi troubleshooting item 5:
+    DeepSeekMoE-style dynamic adjustment of router_bias; Dreamer summary,
+    routing: top-k with a balancing bias vector as in DeepSeek-V3). Reading:
+    every expert below the mean load of its bias row gains gamma, every expert
+    above it loses gamma, an expert at the mean keeps its bias. The load
+    comparison is exact (integers); the bias is stored and updated in float32.
+    counts [T, E] int, bias [rows, E] -> new bias [rows, E] float32."""
+    bias = np.asarray(bias, np.float32)
+    rows, E = bias.shape
+    c = bias_row_counts(counts, rows)
+    total = c.sum(axis=1, keepdims=True)
+    # sign(mean - c_e) with mean = total / E, compared as total vs E * c_e
+    s = np.sign(total - E * c).astype(np.float32)
+    return (bias + np.float32(gamma) * s).astype(np.float32)
+
+
+def expert_depths(counts):
+    """Number of loop iterations (depths) in which each expert received at
+    least one token (Dreamer summary, expert diversity: share of experts used
+    at several depths). counts [T, E] -> [E] int."""
+    return (np.asarray(counts) > 0).sum(axis=0).astype(np.int64)

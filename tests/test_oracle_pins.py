@@ -488,3 +488,57 @@ def test_step_rows_matches_block_step(name):
     np.testing.assert_allclose(a, full["a"][rows], rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(n2, full["n2"][rows], rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(hn, ref, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# router-bias balancing and expert depth usage (between forwards)
+# ---------------------------------------------------------------------------
+def test_bias_update_hand_worked():
+    # loop 0 uses bias row 0, loops 1 and 2 share row 1 (row min(t, rows - 1))
+    counts = np.array([[5, 1, 0, 2],     # row 0: mean 2 -> over, under, under, at
+                       [2, 2, 2, 2],
+                       [0, 4, 4, 0]])    # row 1: [2, 6, 6, 2], mean 4
+    bias = np.array([[0.5, -0.25, 0.0, 1.0], [0.0, 0.0, 0.0, 0.0]], np.float32)
+    got = oracle.router_bias_update(counts, bias, 0.25)
+    want = np.array([[0.25, 0.0, 0.25, 1.0], [0.25, -0.25, -0.25, 0.25]], np.float32)
+    np.testing.assert_array_equal(got, want)
+    assert got.dtype == np.float32
+
+
+def test_bias_update_balanced_and_unused_rows_unchanged():
+    bias = np.random.default_rng(3).standard_normal((4, 6)).astype(np.float32)
+    counts = np.full((2, 6), 7)          # balanced; rows 2 and 3 see no loop
+    np.testing.assert_array_equal(oracle.router_bias_update(counts, bias, 0.1), bias)
+
+
+def test_bias_update_revives_dead_experts():
+    """Troubleshooting item 5: without the bias adjustment the router keeps
+    choosing the first two experts; repeated updates bring every expert into
+    use and flatten the load."""
+    rng = np.random.default_rng(11)
+    E, k, D, n = 8, 2, 32, 512
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    n2 = rng.standard_normal((n, D)) + 2.0 * u
+    Wr = 0.1 * rng.standard_normal((E, D))
+    Wr[:2] += 3.0 * u                     # experts 0 and 1 dominate every token
+    bias = np.zeros((1, E), np.float32)
+
+    def load(b):
+        idx, *_ = oracle.route(n2, Wr, b[0].astype(np.float64), k)
+        return np.bincount(idx.ravel(), minlength=E)
+
+    c0 = load(bias)
+    assert c0[0] + c0[1] >= 0.9 * n * k          # the other six share under 10 %
+    for _ in range(300):
+        bias = oracle.router_bias_update(load(bias)[None, :], bias, 0.05)
+    c = load(bias)
+    assert 0.5 * c.mean() < c.min() <= c.max() < 1.5 * c.mean()
+    assert np.all(bias[0, :2] < 0) and np.all(bias[0, 2:] > 0)
+
+
+def test_expert_depths_counts_loops_with_tokens():
+    rng = np.random.default_rng(5)
+    counts = rng.integers(0, 3, size=(9, 7)) * (rng.random((9, 7)) < 0.6)
+    want = [sum(1 for t in range(9) if counts[t, e] > 0) for e in range(7)]
+    assert oracle.expert_depths(counts).tolist() == want
