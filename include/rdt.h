@@ -278,6 +278,33 @@ rdt_status rdt_decode_step(rdt_handle* h, const float* h0, const float* e, const
                            int32_t T, int32_t pos, void* cache, int32_t max_seq, float* out,
                            const rdt_aux* aux, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Auxiliary-loss-free load balancing between forwards (openclawapi
+ * troubleshooting item 5: the router bias must be adjusted dynamically in the
+ * DeepSeekMoE style or the router settles on a few experts; Dreamer summary,
+ * routing: a balancing bias vector as in DeepSeek-V3). For every bias row r,
+ * c_e is the number of tokens expert e received in the loops that select with
+ * row r (loop t uses row min(t, rows - 1)); an expert below the row's mean
+ * load gains gamma, one above it loses gamma, one at the mean is unchanged.
+ *   expert_counts  int32 [T, E] device, e.g. rdt_aux.expert_counts of a forward
+ *                  (may be null when T = 0: nothing changes)
+ *   router_bias    float [rows, E] device, updated in place
+ *   gamma          step, finite and >= 0
+ * Enqueued on `stream`; deterministic. RDT_E_INVALID on null pointers,
+ * T < 0, E <= 0, rows <= 0 or a bad gamma.
+ */
+rdt_status rdt_router_bias_update(const int32_t* expert_counts, int32_t T, int32_t E,
+                                  float* router_bias, int32_t rows, float gamma, void* stream);
+
+/*
+ * Expert depth usage (Dreamer summary, expert diversity: how many depths use
+ * each expert): depths[e] = number of loops t < T with expert_counts[t][e] > 0.
+ *   expert_counts int32 [T, E] device; depths int32 [E] device (written).
+ * Enqueued on `stream`. RDT_E_INVALID on null pointers, T < 0 or E <= 0.
+ */
+rdt_status rdt_expert_depths(const int32_t* expert_counts, int32_t T, int32_t E, int32_t* depths,
+                             void* stream);
+
 /* Stages of one loop iteration, for rdt_profile_forward. */
 typedef enum rdt_stage {
   RDT_STAGE_NORM1 = 0,    /* u = h + e, RMSNorm */

@@ -15,7 +15,8 @@ import ctypes
 import os
 
 __all__ = ["RdtConfig", "RdtWeights", "RdtAux", "RdtError", "RecurrentBlock", "load_library",
-           "device_weights", "make_config", "EXPORTED_SYMBOLS", "LIB_PATH"]
+           "device_weights", "make_config", "EXPORTED_SYMBOLS", "LIB_PATH", "router_bias_update",
+           "expert_depths"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librdt.so")
 
@@ -24,6 +25,7 @@ EXPORTED_SYMBOLS = [
     "rdt_workspace_size", "rdt_spectral_radius", "rdt_set_graph_mode",
     "rdt_recurrent_forward", "rdt_profile_forward", "rdt_stage_name", "rdt_last_error", "rdt_version",
     "rdt_cache_size", "rdt_prefill", "rdt_decode_workspace_size", "rdt_decode_step",
+    "rdt_router_bias_update", "rdt_expert_depths",
 ]
 N_STAGES = 12
 
@@ -99,13 +101,15 @@ def load_library(path: str = LIB_PATH):
     lib.rdt_decode_workspace_size.restype = ctypes.c_size_t
     lib.rdt_decode_step.argtypes = [_vp, _vp, _vp, ctypes.POINTER(RdtWeights), _i32, _i32, _vp, _i32, _vp,
                                     ctypes.POINTER(RdtAux), _vp, ctypes.c_size_t, _vp]
+    lib.rdt_router_bias_update.argtypes = [_vp, _i32, _i32, _vp, _i32, _f32, _vp]
+    lib.rdt_expert_depths.argtypes = [_vp, _i32, _i32, _vp, _vp]
     lib.rdt_stage_name.argtypes = [_i32]
     lib.rdt_stage_name.restype = ctypes.c_char_p
     lib.rdt_last_error.restype = ctypes.c_char_p
     lib.rdt_version.restype = ctypes.c_char_p
     for name in ["rdt_config_default", "rdt_config_validate", "rdt_create", "rdt_spectral_radius",
                  "rdt_set_graph_mode", "rdt_recurrent_forward", "rdt_profile_forward", "rdt_prefill",
-                 "rdt_decode_step"]:
+                 "rdt_decode_step", "rdt_router_bias_update", "rdt_expert_depths"]:
         getattr(lib, name).restype = _i32
     _lib = lib
     return lib
@@ -296,3 +300,29 @@ class RecurrentBlock:
                                             ctypes.byref(a), _ptr(ws), ws.numel(), stream, ms, cnt, N_STAGES))
         stages = {self.lib.rdt_stage_name(i).decode(): (float(ms[i]), int(cnt[i])) for i in range(N_STAGES)}
         return out, stages
+
+
+def router_bias_update(expert_counts, router_bias, gamma: float, stream=None):
+    """In-place balancing step on device tensors: expert_counts int32 [T, E],
+    router_bias float32 [rows, E]."""
+    import torch
+    lib = load_library()
+    T, E = expert_counts.shape
+    rows = router_bias.shape[0]
+    if router_bias.shape[1] != E or expert_counts.dtype != torch.int32 or router_bias.dtype != torch.float32:
+        raise RdtError(RDT_E_INVALID, "expert_counts int32 [T, E] and router_bias float32 [rows, E] expected")
+    stream = torch.cuda.current_stream(router_bias.device).cuda_stream if stream is None else stream
+    _check(lib.rdt_router_bias_update(_ptr(expert_counts.contiguous()), T, E, _ptr(router_bias), rows,
+                                      float(gamma), stream))
+    return router_bias
+
+
+def expert_depths(expert_counts, stream=None):
+    """Loops in which each expert received tokens: int32 [E] device tensor."""
+    import torch
+    lib = load_library()
+    T, E = expert_counts.shape
+    out = torch.empty(E, dtype=torch.int32, device=expert_counts.device)
+    stream = torch.cuda.current_stream(out.device).cuda_stream if stream is None else stream
+    _check(lib.rdt_expert_depths(_ptr(expert_counts.contiguous()), T, E, _ptr(out), stream))
+    return out

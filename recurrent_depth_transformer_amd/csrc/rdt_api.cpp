@@ -14,6 +14,8 @@
 // whole T-loop is a static graph.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <cmath>
 #include <string.h>
 
 #include <mutex>
@@ -704,4 +706,21 @@ extern "C" rdt_status rdt_decode_step(rdt_handle* h, const float* h0, const floa
   // the position lives in the workspace, so one captured graph serves every step
   HIPCHK(launch_fill_i32(reinterpret_cast<int*>(f.ws + f.P.pos), pos, 1, s));
   return launch(h, f, s);
+}
+
+extern "C" rdt_status rdt_router_bias_update(const int32_t* expert_counts, int32_t T, int32_t E, float* router_bias,
+                                             int32_t rows, float gamma, void* stream) {
+  if ((!expert_counts && T > 0) || !router_bias) return set_err(RDT_E_INVALID, "null counts or bias");
+  if (T < 0 || E <= 0 || rows <= 0) return set_err(RDT_E_INVALID, "T must be >= 0, E and rows positive");
+  if (!(gamma >= 0.f) || !std::isfinite(gamma)) return set_err(RDT_E_INVALID, "gamma must be finite and >= 0");
+  HIPCHK(launch_bias_update(expert_counts, T, E, router_bias, rows, gamma, (hipStream_t)stream));
+  return RDT_OK;
+}
+
+extern "C" rdt_status rdt_expert_depths(const int32_t* expert_counts, int32_t T, int32_t E, int32_t* depths,
+                                        void* stream) {
+  if ((!expert_counts && T > 0) || !depths) return set_err(RDT_E_INVALID, "null counts or depths");
+  if (T < 0 || E <= 0) return set_err(RDT_E_INVALID, "T must be >= 0 and E positive");
+  HIPCHK(launch_expert_depths(expert_counts, T, E, depths, (hipStream_t)stream));
+  return RDT_OK;
 }

@@ -178,6 +178,10 @@ struct QRopeArgs {
 };
 hipError_t launch_qrope(const QRopeArgs& a, hipStream_t s);
 
+// ------------------------------------------------------- between forwards
+hipError_t launch_bias_update(const int* counts, int T, int E, float* bias, int rows, float gamma, hipStream_t s);
+hipError_t launch_expert_depths(const int* counts, int T, int E, int* depths, hipStream_t s);
+
 // ------------------------------------------------------------------ utilities
 hipError_t launch_rope_tables(float* cosb, float* sinb, int S, int dr, float base, hipStream_t s);
 hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t s);

@@ -604,6 +604,58 @@ hipError_t launch_copy_f32(float* dst, const float* src, long long n, hipStream_
   return hipGetLastError();
 }
 
+// --------------------------------------------- router-bias balancing update
+// One workgroup per bias row r. c_e = tokens expert e received in the loops
+// that select with row r (loop t uses row min(t, rows - 1)); every expert
+// below the row's mean load gains gamma, every expert above it loses gamma.
+// The comparison is exact: total vs E * c_e in 64-bit integers.
+__global__ __launch_bounds__(256) void k_bias_update(const int* counts, int T, int E, float* bias, int rows,
+                                                     float gamma) {
+  __shared__ long long part[256];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  auto load = [&](int e) {
+    long long c = 0;
+    for (int t = 0; t < T; ++t)
+      if ((t < rows - 1 ? t : rows - 1) == r) c += counts[(long long)t * E + e];
+    return c;
+  };
+  long long acc = 0;
+  for (int e = tid; e < E; e += 256) acc += load(e);
+  part[tid] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) part[tid] += part[tid + o];
+    __syncthreads();
+  }
+  const long long total = part[0];
+  for (int e = tid; e < E; e += 256) {
+    const long long d = total - (long long)E * load(e);
+    const float sg = d > 0 ? 1.f : (d < 0 ? -1.f : 0.f);
+    bias[(long long)r * E + e] += gamma * sg;
+  }
+}
+
+hipError_t launch_bias_update(const int* counts, int T, int E, float* bias, int rows, float gamma, hipStream_t s) {
+  if (rows <= 0 || E <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bias_update, dim3(rows), dim3(256), 0, s, counts, T, E, bias, rows, gamma);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------- expert depth usage
+__global__ __launch_bounds__(256) void k_expert_depths(const int* counts, int T, int E, int* depths) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  int d = 0;
+  for (int t = 0; t < T; ++t) d += counts[(long long)t * E + e] > 0;
+  depths[e] = d;
+}
+
+hipError_t launch_expert_depths(const int* counts, int T, int E, int* depths, hipStream_t s) {
+  if (E <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_expert_depths, dim3((E + 255) / 256), dim3(256), 0, s, counts, T, E, depths);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ row scatter
 __global__ __launch_bounds__(256) void k_rows_scatter(char* dst, long long dst_ld, const char* src, long long src_ld,
                                                       int vecs, int nrows, int s_in, int s_out, const int* pos_dev) {
