@@ -33,5 +33,5 @@ from .rdt_oracle import (  # noqa: F401
     rmsnorm, rope_tables, apply_rope, attention_causal, gqa_attention,
     mla_attention_explicit, swiglu, route, moe, block_step, forward,
     spectral_radius, kv_cache_bytes_per_token, step_rows,
-    bias_row_counts, router_bias_update, expert_depths,
+    bias_row_counts, router_bias_update, expert_depths, depth_rope, depth_attention,
 )

@@ -60,6 +60,24 @@ def apply_rope(x, pos, cos, sin):
     return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
 
 
+def depth_rope(x, pos, pos_rev, base):
+    """Depth RoPE (Dreamer summary, depth attention: rotary encoding of the
+    depth, with one half reversed to carry the distance to the maximum depth).
+    Reading: half-split pairs (i, i + d/2) as in R4; pairs i < d/4 rotate by
+    the depth pos, pairs d/4 <= i < d/2 by the reversed depth pos_rev =
+    T - 1 - pos. x [n, heads, d]."""
+    x = np.asarray(x, F64)
+    d = x.shape[-1]
+    half = d // 2
+    i = np.arange(half, dtype=F64)
+    inv_freq = np.power(F64(base), -2.0 * i / d)
+    p = np.where(np.arange(half) < half // 2, F64(pos), F64(pos_rev))
+    ang = p * inv_freq
+    c, sn = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * sn, x1 * sn + x2 * c], axis=-1)
+
+
 def softmax(z, axis=-1):
     z = np.asarray(z, F64)
     z = z - np.max(z, axis=axis, keepdims=True)
@@ -151,10 +169,11 @@ def route(n2, Wr, bias_row, k):
     return idx, gates, gap.astype(np.float32), sel
 
 
-def moe(n2, idx, gates, W, n_shared):
+def moe(n2, idx, gates, W, n_shared, shared_w=None):
     """Sparse MoE output: sum over a token's selected experts of gate * expert(x),
     plus every always-on shared expert at weight 1 (openclawapi Passo 2,
-    n_shared_experts; reading R7)."""
+    n_shared_experts; reading R7) or, with shared_w [n], at that per-token weight
+    (Dreamer summary, routing: the shared expert scaled by the maximum score)."""
     n2 = np.asarray(n2, F64)
     m = np.zeros_like(n2)
     E = W["Wg"].shape[0]
@@ -165,8 +184,38 @@ def moe(n2, idx, gates, W, n_shared):
         y = swiglu(n2[rows], W["Wg"][e], W["Wu"][e], W["Wd"][e])
         m[rows] += gates[rows, slot][:, None] * y
     for s in range(n_shared):
-        m += swiglu(n2, W["Wsg"][s], W["Wsu"][s], W["Wsd"][s])
+        y = swiglu(n2, W["Wsg"][s], W["Wsu"][s], W["Wsd"][s])
+        m += y if shared_w is None else np.asarray(shared_w, F64)[:, None] * y
     return m
+
+
+def depth_attention(cfg, W, nd, t, T, hist):
+    """Dreamer depth attention at loop t (Dreamer summary, Metodologia: the
+    sequence dimension is the batch and depth is the sequence; the depth KV can
+    be dropped after each token). Every token attends over its own loop states
+    0..t: q from loop t, keys and values of loops 0..t (kept in hist, to which
+    this loop's are appended). GQA head map and 1/sqrt(d) scale as R5; depth
+    RoPE as depth_rope with T the loop count of the forward. nd [N, D] is
+    RMSNorm(u) * g_da. Returns the sublayer output [N, D] (after Wo_da)."""
+    N = nd.shape[0]
+    Hd, KVd, dd = cfg["da_heads"], cfg["da_kv_heads"], cfg["da_head_dim"]
+    base = cfg["rope_base"]
+    q = (nd @ W["Wq_da"].astype(F64).T).reshape(N, Hd, dd)
+    k = (nd @ W["Wk_da"].astype(F64).T).reshape(N, KVd, dd)
+    v = (nd @ W["Wv_da"].astype(F64).T).reshape(N, KVd, dd)
+    q = depth_rope(q, t, T - 1 - t, base)
+    k = depth_rope(k, t, T - 1 - t, base)
+    hist["k"].append(k)
+    hist["v"].append(v)
+    K = np.stack(hist["k"], axis=2)              # [N, KVd, t+1, dd]
+    V = np.stack(hist["v"], axis=2)
+    o = np.empty((N, Hd, dd))
+    for i in range(Hd):
+        j = (i * KVd) // Hd
+        sc = np.einsum("nd,ntd->nt", q[:, i], K[:, j]) / np.sqrt(dd)
+        p = softmax(sc, axis=1)
+        o[:, i] = np.einsum("nt,ntd->nd", p, V[:, j])
+    return o.reshape(N, Hd * dd) @ W["Wo_da"].astype(F64).T
 
 
 def spectral_radius(A):
@@ -202,23 +251,41 @@ def _attn_out(cfg, W, n1, pos, cos, sin):
     return o.reshape(N, -1)
 
 
-def block_step(cfg, W, h, e, t, active, forced_idx=None, tables=None):
+def block_step(cfg, W, h, e, t, active, forced_idx=None, tables=None, depth=None, T=None):
     """Residual branch of one recurrent-block iteration (reading R1/R2):
     u = h + e; a = attention-out-projection(RMSNorm(u)) [+ depth-wise LoRA];
     x = u + a; n2 = RMSNorm(x); m = MoE(n2). Attention runs on every token (keys
     of halted tokens use their frozen state); the router and experts run on the
-    active rows only. Returns a dict with a, n2, m [N, D] (rows of inactive
-    tokens of m are zero), idx [N, k] (-1 when inactive), gates, gap, counts."""
+    active rows only.
+
+    Dreamer variants (Dreamer summary, Metodologia): with depth attention
+    (cfg da_heads > 0; needs depth = {"k": [], "v": []} carried across loops
+    and T) the sublayers run DA -> SA -> EA, each on RMSNorm of the running
+    residual: d = DA(RMSNorm(u) g_da), a = SA(RMSNorm(u + d) g1), m =
+    MoE(RMSNorm(u + d + a) g2), branch d + a + m. With cfg parallel every
+    sublayer reads RMSNorm(u) (own gains). With cfg shared_scale the shared
+    expert is weighted by the token's maximum router probability.
+
+    Returns a dict with a (the whole residual branch except m: d + a), d, n2,
+    m [N, D] (rows of inactive tokens of m are zero), idx [N, k] (-1 when
+    inactive), gates, gap, counts."""
     N, D = h.shape
     S = cfg["seq"]
     eps = cfg["norm_eps"]
+    par = bool(cfg.get("parallel", 0))
     pos = np.arange(N) % S
     if tables is None:
         d_r = cfg["head_dim"] if cfg["attn"] == "gqa" else cfg["qk_rope_head_dim"]
         tables = rope_tables(S, d_r, cfg["rope_base"])
     cos, sin = tables
     u = np.asarray(h, F64) + np.asarray(e, F64)
-    n1 = rmsnorm(u, W["g1"], eps)
+    d = np.zeros((N, D), F64)
+    if cfg.get("da_heads", 0):
+        if depth is None or T is None:
+            raise ValueError("depth attention needs the depth history and T")
+        d = depth_attention(cfg, W, rmsnorm(u, W["g_da"], eps), t, T, depth)
+    u1 = u if par else u + d
+    n1 = rmsnorm(u1, W["g1"], eps)
     o = _attn_out(cfg, W, n1, pos, cos, sin)
     a = o @ W["Wo"].astype(F64).T
     if cfg["lora_rank"]:
@@ -226,7 +293,7 @@ def block_step(cfg, W, h, e, t, active, forced_idx=None, tables=None):
         # lora_rank and advanced direction 1); reading R8
         tl = min(t, cfg["n_lora"] - 1)
         a = a + (o @ W["lora_down"][tl].astype(F64).T) @ W["lora_up"][tl].astype(F64).T
-    x = u + a
+    x = u if par else u1 + a
     n2 = rmsnorm(x, W["g2"], eps)
 
     k = cfg["top_k"]
@@ -234,12 +301,13 @@ def block_step(cfg, W, h, e, t, active, forced_idx=None, tables=None):
     act_rows = np.nonzero(active)[0]
     bias_row = W["router_bias"][min(t, cfg["n_bias_rows"] - 1)]
     idx_a, gates_a, gap_a, _ = route(n2[act_rows], W["Wr"], bias_row, k)
+    logits = n2[act_rows] @ W["Wr"].astype(F64).T
+    p_all = softmax(logits, axis=1)
     if forced_idx is not None:
         idx_a = np.asarray(forced_idx, np.int64)[act_rows]
-        logits = n2[act_rows] @ W["Wr"].astype(F64).T
-        p = softmax(logits, axis=1)
-        gates_a = p[np.arange(act_rows.size)[:, None], idx_a]
-    m_a = moe(n2[act_rows], idx_a, gates_a, W, cfg["n_shared_experts"])
+        gates_a = p_all[np.arange(act_rows.size)[:, None], idx_a]
+    sw = p_all.max(axis=1) if cfg.get("shared_scale", 0) else None
+    m_a = moe(n2[act_rows], idx_a, gates_a, W, cfg["n_shared_experts"], sw)
     m = np.zeros((N, D), F64)
     m[act_rows] = m_a
     idx = np.full((N, k), -1, np.int64)
@@ -249,7 +317,7 @@ def block_step(cfg, W, h, e, t, active, forced_idx=None, tables=None):
     gap = np.full(N, np.nan, np.float32)
     gap[act_rows] = gap_a
     counts = np.bincount(idx_a.reshape(-1), minlength=E)[:E].astype(np.int64)
-    return dict(a=a, n2=n2, m=m, idx=idx, gates=gates, gap=gap, counts=counts)
+    return dict(a=d + a, d=d, n2=n2, m=m, idx=idx, gates=gates, gap=gap, counts=counts)
 
 
 def forward(cfg, W, h0=None, e=None, T=None, forced_idx=None, forced_loops=None,
@@ -273,6 +341,9 @@ def forward(cfg, W, h0=None, e=None, T=None, forced_idx=None, forced_loops=None,
         raise ValueError("T must be >= 0")
     if spectral_radius(W["A"]) >= 1.0:
         raise ValueError("unstable injection: rho(A) >= 1")
+    if cfg.get("da_heads", 0) and cfg["act"]:
+        raise ValueError("depth attention with ACT halting is not defined here")
+    depth = {"k": [], "v": []}
     A = np.asarray(W["A"], F64)[None, :]
     Bv = np.asarray(W["B"], F64)[None, :]
     N = h.shape[0]
@@ -297,7 +368,7 @@ def forward(cfg, W, h0=None, e=None, T=None, forced_idx=None, forced_loops=None,
                 rec["h"].append(h.copy())
             continue
         fi = None if forced_idx is None else forced_idx[t]
-        st = block_step(cfg, W, h, e, t, active, fi, tables)
+        st = block_step(cfg, W, h, e, t, active, fi, tables, depth, T)
         rows = np.nonzero(active)[0]
         # LTI injection plus the block's residual branch (techbriefly loop update)
         h[rows] = A * h[rows] + Bv * e[rows] + st["a"][rows] + st["m"][rows]
@@ -328,7 +399,10 @@ def step_rows(cfg, W, h, e, t, rows, forced_idx_rows, tables=None):
     state h of every token (same definitions as block_step and forward; keys
     and values come from every token of the sequence, queries only from the
     sampled rows). forced_idx_rows: [len(rows), k] expert indices. Returns
-    (h_new_rows, a_rows, n2_rows)."""
+    (h_new_rows, a_rows, n2_rows). Not defined for the Dreamer variants (depth
+    attention needs every earlier loop's state of the token)."""
+    if cfg.get("da_heads", 0) or cfg.get("parallel", 0) or cfg.get("shared_scale", 0):
+        raise NotImplementedError("step_rows covers the sequential block without depth attention")
     h = np.asarray(h, F64)
     e = np.asarray(e, F64)
     rows = np.asarray(rows)

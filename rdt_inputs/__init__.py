@@ -23,7 +23,8 @@ The ``*_small`` workloads keep each family's structure at sizes a CPU reference
 finishes in seconds, with sequence lengths and widths that leave ragged tiles.
 
 Draw order is fixed: A, B, e, then the weights in struct field order, then the
-router bias, then the LoRA factors, then the halting vector. bf16 workloads round
+router bias, then the LoRA factors, then the halting vector, then the depth
+attention weights (Wq_da, Wk_da, Wv_da, Wo_da). bf16 workloads round
 every drawn weight once to bfloat16 (round to nearest even) and hand both sides
 those exact values as float32 arrays.
 """
@@ -41,6 +42,7 @@ _BASE = dict(
     v_head_dim=0, rope_base=10000.0, norm_eps=1e-6,
     n_experts=4, n_shared_experts=0, top_k=2, expert_dim=128,
     n_bias_rows=1, lora_rank=0, n_lora=0, act=False, act_threshold=0.99,
+    parallel=0, shared_scale=0, da_heads=0, da_kv_heads=0, da_head_dim=0,
     dtype="f32", T=4, seed=0,
     # distributions
     a_range=(0.5, 0.95), b_range=(0.0, 0.5), w_std=0.02, router_std=None,
@@ -93,6 +95,20 @@ WORKLOADS = {
     "act_small": _cfg(batch=3, seq=70, dim=256, n_heads=4, n_kv_heads=2, head_dim=64,
                       n_experts=8, top_k=2, expert_dim=192, T=8, dtype="bf16",
                       lora_rank=8, n_lora=4, act=True),
+    # ---- Dreamer block variants (depth attention, parallel sublayers,
+    # shared expert scaled by the max router score) ----
+    "dreamer_small": _cfg(batch=2, seq=72, dim=256, n_heads=4, n_kv_heads=2, head_dim=64,
+                          da_heads=4, da_kv_heads=2, da_head_dim=32, n_experts=8,
+                          n_shared_experts=1, shared_scale=1, top_k=2, expert_dim=192,
+                          T=6, dtype="bf16"),
+    "parallel_small": _cfg(batch=2, seq=68, dim=256, n_heads=8, n_kv_heads=2, head_dim=32,
+                           da_heads=4, da_kv_heads=4, da_head_dim=64, parallel=1,
+                           n_experts=16, n_shared_experts=1, shared_scale=1, top_k=4,
+                           expert_dim=160, T=4, dtype="bf16"),
+    "dreamer_tiny": _cfg(batch=1, seq=32, dim=64, n_heads=4, n_kv_heads=2, head_dim=16,
+                         da_heads=2, da_kv_heads=1, da_head_dim=16, n_experts=4,
+                         n_shared_experts=1, shared_scale=1, top_k=2, expert_dim=128, T=5,
+                         dtype="f32", a_range=(0.5, 0.9)),
 }
 
 
@@ -201,4 +217,11 @@ def make_inputs(cfg: dict) -> dict:
     if cfg["act"]:
         out["w_halt"] = (rng.standard_normal(D, dtype=np.float32)
                          * np.float32(cfg["halt_std"])).astype(np.float32)
+    if cfg["da_heads"]:
+        Hd, KVd, dd = cfg["da_heads"], cfg["da_kv_heads"], cfg["da_head_dim"]
+        out["g_da"] = np.ones(D, np.float32)
+        for name, shape in [("Wq_da", (Hd * dd, D)), ("Wk_da", (KVd * dd, D)),
+                            ("Wv_da", (KVd * dd, D)), ("Wo_da", (D, Hd * dd))]:
+            w = rng.standard_normal(shape, dtype=np.float32) * np.float32(cfg["w_std"])
+            out[name] = rnd(w)
     return out

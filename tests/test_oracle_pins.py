@@ -542,3 +542,122 @@ def test_expert_depths_counts_loops_with_tokens():
     counts = rng.integers(0, 3, size=(9, 7)) * (rng.random((9, 7)) < 0.6)
     want = [sum(1 for t in range(9) if counts[t, e] > 0) for e in range(7)]
     assert oracle.expert_depths(counts).tolist() == want
+
+
+# ---------------------------------------------------------------------------
+# Dreamer variants: depth attention, parallel sublayers, max-score shared expert
+# ---------------------------------------------------------------------------
+def _complex_depth_rope(x, pos, pos_rev, base):
+    """Independent form: pair (x_i, x_{i+d/2}) as the complex number
+    x_i + 1j x_{i+d/2}, multiplied by exp(1j p_i theta_i)."""
+    d = x.shape[-1]
+    h = d // 2
+    z = x[..., :h] + 1j * x[..., h:]
+    th = base ** (-2.0 * np.arange(h) / d)
+    p = np.array([pos if i < h // 2 else pos_rev for i in range(h)], dtype=np.float64)
+    z = z * np.exp(1j * p * th)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def test_depth_rope_matches_complex_rotation():
+    x = np.random.default_rng(1).standard_normal((5, 3, 16))
+    for pos, rev in [(0, 7), (3, 4), (7, 0)]:
+        np.testing.assert_allclose(oracle.depth_rope(x, pos, rev, 10000.0),
+                                   _complex_depth_rope(x, pos, rev, 10000.0), rtol=1e-12, atol=1e-12)
+
+
+def _depth_setup(seed=2, N=3, D=16, Hd=4, KVd=2, dd=8):
+    rng = np.random.default_rng(seed)
+    cfg = dict(da_heads=Hd, da_kv_heads=KVd, da_head_dim=dd, rope_base=10000.0)
+    W = {"Wq_da": rng.standard_normal((Hd * dd, D)) * 0.3, "Wk_da": rng.standard_normal((KVd * dd, D)) * 0.3,
+         "Wv_da": rng.standard_normal((KVd * dd, D)) * 0.3, "Wo_da": rng.standard_normal((D, Hd * dd)) * 0.3}
+    states = rng.standard_normal((6, N, D))          # RMSNorm outputs of loops 0..5
+    return cfg, W, states
+
+
+def test_depth_attention_brute_force():
+    """Scalar loops over tokens, heads and depths, complex-number rotations."""
+    cfg, W, states = _depth_setup()
+    T, N = 5, states.shape[1]
+    Hd, KVd, dd = cfg["da_heads"], cfg["da_kv_heads"], cfg["da_head_dim"]
+    hist = {"k": [], "v": []}
+    for t in range(T):
+        got = oracle.depth_attention(cfg, W, states[t], t, T, hist)
+        want = np.zeros_like(got)
+        for n in range(N):
+            o = np.zeros(Hd * dd)
+            for i in range(Hd):
+                j = i * KVd // Hd
+                q = _complex_depth_rope((states[t, n] @ W["Wq_da"].T)[i * dd:(i + 1) * dd], t, T - 1 - t, 1e4)
+                sc, vs = [], []
+                for tau in range(t + 1):
+                    kk = _complex_depth_rope((states[tau, n] @ W["Wk_da"].T)[j * dd:(j + 1) * dd], tau,
+                                             T - 1 - tau, 1e4)
+                    sc.append(float(q @ kk) / np.sqrt(dd))
+                    vs.append((states[tau, n] @ W["Wv_da"].T)[j * dd:(j + 1) * dd])
+                w = np.exp(np.array(sc) - max(sc))
+                w /= w.sum()
+                o[i * dd:(i + 1) * dd] = sum(wi * vi for wi, vi in zip(w, vs))
+            want[n] = W["Wo_da"] @ o
+        np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+def test_depth_attention_first_loop_passes_values():
+    """At loop 0 a token has one depth state: attention returns its value."""
+    cfg, W, states = _depth_setup()
+    got = oracle.depth_attention(cfg, W, states[0], 0, 4, {"k": [], "v": []})
+    Hd, KVd, dd = cfg["da_heads"], cfg["da_kv_heads"], cfg["da_head_dim"]
+    v = (states[0] @ W["Wv_da"].T).reshape(-1, KVd, dd)
+    o = np.concatenate([v[:, i * KVd // Hd] for i in range(Hd)], axis=1)
+    np.testing.assert_allclose(got, o @ W["Wo_da"].T, rtol=1e-12, atol=1e-12)
+
+
+def test_depth_attention_relative_in_both_halves():
+    """Scores depend on depth offsets only (the reversed half on the negated
+    offset), so the output does not depend on the loop count T."""
+    cfg, W, states = _depth_setup()
+    outs = []
+    for T in (5, 9):
+        hist = {"k": [], "v": []}
+        outs.append([oracle.depth_attention(cfg, W, states[t], t, T, hist) for t in range(5)])
+    np.testing.assert_allclose(np.array(outs[0]), np.array(outs[1]), rtol=1e-10, atol=1e-12)
+
+
+def test_parallel_equals_sequential_without_attention_output():
+    base = get_config("parallel_small", T=2)
+    W = make_inputs(base)
+    W["Wo"] = np.zeros_like(W["Wo"])
+    W["Wo_da"] = np.zeros_like(W["Wo_da"])
+    seq = oracle.forward(dict(base, parallel=0), W)["h"]
+    par = oracle.forward(base, W)["h"]
+    np.testing.assert_allclose(par, seq, rtol=1e-13, atol=1e-13)
+    W2 = make_inputs(base)
+    assert not np.allclose(oracle.forward(dict(base, parallel=0), W2)["h"], oracle.forward(base, W2)["h"])
+
+
+def test_shared_expert_scaled_by_max_score_dense():
+    """k = E: the MoE is the dense softmax mixture plus max(p) times the
+    shared expert (einsum over all experts, written independently)."""
+    cfg = get_config("dreamer_tiny", top_k=4, T=1)
+    W = make_inputs(cfg)
+    rng = np.random.default_rng(4)
+    n2 = rng.standard_normal((10, cfg["dim"]))
+    p = np.exp(n2 @ W["Wr"].astype(np.float64).T)
+    p /= p.sum(1, keepdims=True)
+
+    def ffn(x, g, u, dn):
+        a = x @ g.T
+        return (a / (1 + np.exp(-a)) * (x @ u.T)) @ dn.T
+    ys = np.stack([ffn(n2, W["Wg"][e], W["Wu"][e], W["Wd"][e]) for e in range(4)], 1)
+    want = np.einsum("ne,ned->nd", p, ys) + p.max(1)[:, None] * ffn(n2, W["Wsg"][0], W["Wsu"][0], W["Wsd"][0])
+    idx = np.tile(np.arange(4), (10, 1))
+    got = oracle.moe(n2, idx, p, W, 1, p.max(1))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_depth_attention_rejected_with_act():
+    cfg = get_config("dreamer_tiny", act=True)
+    W = make_inputs(cfg)
+    W["w_halt"] = np.zeros(cfg["dim"], np.float32)
+    with pytest.raises(ValueError):
+        oracle.forward(cfg, W)
