@@ -61,7 +61,7 @@ typedef enum rdt_dtype { RDT_F32 = 0, RDT_BF16 = 1 } rdt_dtype;
  *   rope_base             RoPE base (half-split rotation, positions 0..seq-1)
  *   norm_eps              RMSNorm epsilon
  *   n_experts, top_k      routed experts and experts per token (top_k <= n_experts <= 64)
- *   n_shared_experts      always-on experts (weight 1)
+ *   n_shared_experts      always-on experts (weight 1, or see shared_scale)
  *   expert_dim            SwiGLU hidden width of every expert
  *   n_bias_rows           rows of the router selection bias; loop t uses row min(t, rows-1)
  *   lora_rank, n_lora     depth-wise LoRA on the attention output projection;
@@ -72,6 +72,18 @@ typedef enum rdt_dtype { RDT_F32 = 0, RDT_BF16 = 1 } rdt_dtype;
  *                         sum reaches the threshold; a halted token keeps its state
  *   dtype                 RDT_F32 or RDT_BF16 storage of weights and activations
  *   max_T                 largest loop count a workspace is planned for
+ * Dreamer block variants (Dreamer summary, Metodologia), all 0 by default:
+ *   parallel_block        1: attention and the MoE both read RMSNorm(h + e) (own
+ *                         gains) instead of running one after the other
+ *   shared_scale          1: shared experts weighted by the token's maximum router
+ *                         probability instead of 1
+ *   da_heads, da_kv_heads, da_head_dim
+ *                         depth attention before sequence attention: every token
+ *                         attends over its own states of loops 0..t (depth as the
+ *                         sequence), with depth RoPE whose second half of rotary
+ *                         pairs uses the reversed depth T-1-t; da_heads = 0 turns
+ *                         it off. da_head_dim 16, 32, 64 or 128; not combinable with
+ *                         ACT; max_T <= 64
  */
 typedef struct rdt_config {
   int32_t batch, seq, dim;
@@ -86,6 +98,9 @@ typedef struct rdt_config {
   float act_threshold;
   int32_t dtype;
   int32_t max_T;
+  int32_t parallel_block;
+  int32_t shared_scale;
+  int32_t da_heads, da_kv_heads, da_head_dim;
 } rdt_config;
 
 /*
@@ -109,6 +124,9 @@ typedef struct rdt_config {
  *   lora_down [L, r, Hv]; lora_up [L, D, r]  T-type (null when r = 0)
  *   w_halt float [D]  ACT halting vector (null unless ACT)
  *   A, B float [D]    injection diagonals; rho(A) = max |A_i| must be < 1
+ *   depth attention (null unless da_heads > 0; Hd = da_heads, KVd = da_kv_heads,
+ *   dd = da_head_dim): Wq_da [Hd*dd, D], Wk_da [KVd*dd, D], Wv_da [KVd*dd, D],
+ *   Wo_da [D, Hd*dd] T-type; g_da float [D] its RMSNorm gain
  */
 typedef struct rdt_weights {
   const float* g1;
@@ -137,6 +155,11 @@ typedef struct rdt_weights {
   const float* w_halt;
   const float* A;
   const float* B;
+  const void* Wq_da;
+  const void* Wk_da;
+  const void* Wv_da;
+  const void* Wo_da;
+  const float* g_da;
 } rdt_weights;
 
 /*

@@ -44,12 +44,14 @@ class RdtConfig(ctypes.Structure):
                 ("rope_base", _f32), ("norm_eps", _f32),
                 ("n_experts", _i32), ("n_shared_experts", _i32), ("top_k", _i32), ("expert_dim", _i32),
                 ("n_bias_rows", _i32), ("lora_rank", _i32), ("n_lora", _i32),
-                ("act_enabled", _i32), ("act_threshold", _f32), ("dtype", _i32), ("max_T", _i32)]
+                ("act_enabled", _i32), ("act_threshold", _f32), ("dtype", _i32), ("max_T", _i32),
+                ("parallel_block", _i32), ("shared_scale", _i32),
+                ("da_heads", _i32), ("da_kv_heads", _i32), ("da_head_dim", _i32)]
 
 
 WEIGHT_FIELDS = ["g1", "g2", "Wq", "Wk", "Wv", "Wdq", "gq", "Wuq", "Wdkv", "gkv", "Wuk", "Wuv",
                  "Wo", "Wr", "router_bias", "Wg", "Wu", "Wd", "Wsg", "Wsu", "Wsd",
-                 "lora_down", "lora_up", "w_halt", "A", "B"]
+                 "lora_down", "lora_up", "w_halt", "A", "B", "Wq_da", "Wk_da", "Wv_da", "Wo_da", "g_da"]
 AUX_FIELDS = ["loops", "route_idx", "route_gap", "expert_counts", "act_cum", "n2_dump", "a_dump", "h_dump"]
 
 
@@ -143,6 +145,11 @@ def make_config(cfg: dict) -> RdtConfig:
     c.act_threshold = float(cfg.get("act_threshold", 0.99))
     c.dtype = 0 if cfg.get("dtype", "bf16") == "f32" else 1
     c.max_T = int(cfg.get("max_T", max(16, int(cfg.get("T", 16)))))
+    c.parallel_block = int(cfg.get("parallel", 0))
+    c.shared_scale = int(cfg.get("shared_scale", 0))
+    c.da_heads = int(cfg.get("da_heads", 0))
+    c.da_kv_heads = int(cfg.get("da_kv_heads", 0))
+    c.da_head_dim = int(cfg.get("da_head_dim", 0))
     return c
 
 
@@ -154,7 +161,7 @@ def device_weights(inputs: dict, cfg: dict, device="cuda") -> dict:
     router bias, halting vector, h0 and e stay float32.
     """
     import torch
-    f32_names = {"g1", "g2", "gq", "gkv", "router_bias", "w_halt", "A", "B", "e", "h0"}
+    f32_names = {"g1", "g2", "gq", "gkv", "router_bias", "w_halt", "A", "B", "e", "h0", "g_da"}
     store = torch.float32 if cfg.get("dtype", "bf16") == "f32" else torch.bfloat16
     out = {}
     for k, v in inputs.items():

@@ -251,6 +251,18 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   if (act && f.aux.a_dump) LAUNCH(RDT_STAGE_OTHER, launch_fill_f32(f.aux.a_dump, 0.f, (long long)f.T * N * D, s));
 
   char* n1 = at<char>(ws, P.n1);
+  // Dreamer variants: depth attention buffers, parallel sublayers, shared scale
+  const bool par = c.parallel_block != 0;
+  float* smax = (c.shared_scale && P.Se > 0) ? at<float>(ws, P.smax) : nullptr;
+  char* nd = P.da ? at<char>(ws, P.da_nd) : nullptr;
+  char* dq = P.da ? at<char>(ws, P.da_q) : nullptr;
+  char* dk = P.da ? at<char>(ws, P.da_k) : nullptr;
+  char* dvb = P.da ? at<char>(ws, P.da_v) : nullptr;
+  char* dout = P.da ? at<char>(ws, P.da_out) : nullptr;
+  float* dbuf = P.da ? at<float>(ws, P.da_buf) : nullptr;
+  float* dcos = P.da ? at<float>(ws, P.da_cos) : nullptr;
+  float* dsin = P.da ? at<float>(ws, P.da_sin) : nullptr;
+  if (P.da) LAUNCH(RDT_STAGE_OTHER, launch_rope_tables(dcos, dsin, f.T, P.dd, c.rope_base, s));
   char* o = at<char>(ws, P.o);
   char* z = at<char>(ws, P.z);
   float* abuf = at<float>(ws, P.a);
@@ -288,10 +300,46 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
 
     // a1: u = h + e, n1 = RMSNorm(u) * g1 (tokens whose state changed last loop)
     //     (after the first loop the combine kernel of the previous loop wrote it)
+    //     With depth attention the first norm feeds it (gain g_da) and the
+    //     attention input is normalised after it.
     if (t == 0) {
       NormArgs n1a{};
-      n1a.dtype = dt; n1a.h = f.out; n1a.e = f.e; n1a.a = nullptr; n1a.g = w.g1; n1a.eps = c.norm_eps; n1a.D = D;
-      n1a.rows = prev; n1a.ndev = nprev; n1a.n = N; n1a.out = n1; n1a.out_scatter = 1; n1a.dump = nullptr;
+      n1a.dtype = dt; n1a.h = f.out; n1a.e = f.e; n1a.a = nullptr; n1a.g = P.da ? w.g_da : w.g1;
+      n1a.eps = c.norm_eps; n1a.D = D;
+      n1a.rows = prev; n1a.ndev = nprev; n1a.n = N; n1a.out = P.da ? nd : n1; n1a.out_scatter = 1; n1a.dump = nullptr;
+      LAUNCH(RDT_STAGE_NORM1, launch_norm(n1a, s));
+    }
+    if (P.da) {
+      // Dreamer depth attention: q, k, v of this loop (depth RoPE at t and at
+      // the reversed depth T-1-t), keys/values kept per loop, attention over
+      // loops 0..t of the same token, output projection into dbuf (float)
+      const int qw = P.Hd * P.dd, kw = P.KVd * P.dd;
+      const size_t lpl = (size_t)N * kw;  // elements per loop in dk / dv
+      DenseGemm g{};
+      g.dtype = dt; g.A = nd; g.lda = D; g.K = D; g.batch = 1; g.epi = EPI_STORE;
+      g.rows = nullptr; g.gather = 0; g.M = N; g.Mdev = nullptr;
+      g.nseg = 3;
+      g.seg[0] = GemmSeg{w.Wq_da, qw, dq, qw, 0, 1, 0};
+      g.seg[1] = GemmSeg{w.Wk_da, kw, dk + (size_t)t * lpl * elt, kw, 1, 1, 0};
+      g.seg[2] = GemmSeg{w.Wv_da, kw, dvb + (size_t)t * lpl * elt, kw, 1, 0, 0};
+      g.cosb = dcos; g.sinb = dsin; g.rope_dim = P.dd; g.seq = 1;
+      g.drope = 1; g.dpos0 = t; g.dpos1 = f.T - 1 - t;
+      pick_tile(N, qw + 2 * kw, P.dd, &g.bm, &g.bn);
+      LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g, s));
+      DepthAttnArgs da{};
+      da.dtype = dt; da.q = dq; da.k = dk; da.v = dvb; da.o = dout; da.lstride = (long long)lpl;
+      da.n = N; da.H = P.Hd; da.KV = P.KVd; da.dd = P.dd; da.t = t; da.scale = 1.f / sqrtf((float)P.dd);
+      LAUNCH(RDT_STAGE_ATTN, launch_depth_attention(da, s));
+      DenseGemm gdo{};
+      gdo.dtype = dt; gdo.A = dout; gdo.lda = qw; gdo.K = qw; gdo.batch = 1; gdo.epi = EPI_STORE;
+      gdo.rows = nullptr; gdo.gather = 0; gdo.M = N; gdo.Mdev = nullptr;
+      gdo.nseg = 1; gdo.seg[0] = GemmSeg{w.Wo_da, D, dbuf, D, 0, 0, 1};
+      pick_tile(N, D, 16, &gdo.bm, &gdo.bn);
+      LAUNCH(RDT_STAGE_OPROJ, launch_dense_gemm(gdo, s));
+      // sequence-attention input: RMSNorm(u + d) (sequential) or RMSNorm(u) (parallel)
+      NormArgs n1a{};
+      n1a.dtype = dt; n1a.h = f.out; n1a.e = f.e; n1a.a = par ? nullptr : dbuf; n1a.g = w.g1; n1a.eps = c.norm_eps;
+      n1a.D = D; n1a.rows = nullptr; n1a.ndev = nullptr; n1a.n = N; n1a.out = n1; n1a.out_scatter = 1;
       LAUNCH(RDT_STAGE_NORM1, launch_norm(n1a, s));
     }
 
@@ -429,10 +477,12 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     // top-k, and the stable expert permutation, in one kernel
     NormRouteArgs nr{};
     NormArgs& n2a = nr.norm;
-    n2a.dtype = dt; n2a.h = f.out; n2a.e = f.e; n2a.a = abuf; n2a.g = w.g2; n2a.eps = c.norm_eps; n2a.D = D;
+    // parallel block: the MoE reads RMSNorm(u); sequential: RMSNorm(u [+ d] + a)
+    n2a.dtype = dt; n2a.h = f.out; n2a.e = f.e; n2a.a = par ? nullptr : abuf; n2a.a2 = (P.da && !par) ? dbuf : nullptr;
+    n2a.g = w.g2; n2a.eps = c.norm_eps; n2a.D = D;
     n2a.rows = cur; n2a.ndev = ncur; n2a.n = N; n2a.out = n2; n2a.out_scatter = 0;
     n2a.dump = f.aux.n2_dump ? (void*)elt_ptr(f.aux.n2_dump, (long long)t * N * D, elt) : nullptr;
-    nr.Wr = w.Wr; nr.E = E; nr.k = k;
+    nr.Wr = w.Wr; nr.E = E; nr.k = k; nr.smax = smax;
     nr.bias = w.router_bias && c.n_bias_rows > 0
                   ? w.router_bias + (size_t)(t < c.n_bias_rows - 1 ? t : c.n_bias_rows - 1) * E
                   : nullptr;
@@ -473,7 +523,8 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     ca.act = act; ca.w_halt = w.w_halt; ca.thr = c.act_threshold; ca.cum = cum; ca.loops = f.aux.loops; ca.t = t;
     ca.cum_dump = f.aux.act_cum ? f.aux.act_cum + (size_t)t * N : nullptr;
     ca.a_dump = f.aux.a_dump ? f.aux.a_dump + (size_t)t * N * D : nullptr;
-    ca.n1_out = t + 1 < f.T ? n1 : nullptr; ca.g1 = w.g1; ca.eps = c.norm_eps;
+    ca.n1_out = t + 1 < f.T ? (P.da ? nd : n1) : nullptr; ca.g1 = P.da ? w.g_da : w.g1; ca.eps = c.norm_eps;
+    ca.d = P.da ? dbuf : nullptr; ca.smax = smax;
     LAUNCH(RDT_STAGE_COMBINE, launch_combine(ca, s));
     if (act) {
       CompactArgs cp{};
@@ -506,6 +557,10 @@ static rdt_status check_weights(const rdt_config& c, const rdt_weights* w) {
   if (c.n_shared_experts > 0) { req(w->Wsg, "Wsg"); req(w->Wsu, "Wsu"); req(w->Wsd, "Wsd"); }
   if (c.lora_rank > 0) { req(w->lora_down, "lora_down"); req(w->lora_up, "lora_up"); }
   if (c.act_enabled) req(w->w_halt, "w_halt");
+  if (c.da_heads > 0) {
+    req(w->Wq_da, "Wq_da"); req(w->Wk_da, "Wk_da"); req(w->Wv_da, "Wv_da"); req(w->Wo_da, "Wo_da");
+    req(w->g_da, "g_da");
+  }
   for (int i = 0; i < n; ++i) {
     if (!need[i]) return set_err(RDT_E_INVALID, std::string("null weight pointer: ") + names[i]);
     if (misaligned(need[i], 16)) return set_err(RDT_E_INVALID, std::string("weight not 16-byte aligned: ") + names[i]);

@@ -417,7 +417,8 @@ __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
           for (int x = 0; x < 8; ++x) {
             const int hd = (lc + x) % rd;
             const int jj = hd % half;
-            const float cs = g.cosb[pos * half + jj], sn = g.sinb[pos * half + jj];
+            const int pp = g.drope ? (jj < (half >> 1) ? g.dpos0 : g.dpos1) : pos;
+            const float cs = g.cosb[pp * half + jj], sn = g.sinb[pp * half + jj];
             if (hd < half) {
               v[x] = crow[c8 + x] * cs - crow[c8 + x + half] * sn;
             } else {

@@ -59,6 +59,7 @@ struct DenseGemm {
   int epi;
   RouterEpi router;
   const int* pos_dev;    // RoPE at position *pos_dev for every row (one-token decode), else token % seq
+  int drope, dpos0, dpos1; // depth RoPE: pairs below rope_dim/4 at dpos0, the rest at dpos1
   int bm, bn;            // tile shape (64 or 128 each)
   int ns;                // bf16 pipeline stages (2..4; 0 = default)
 };
@@ -108,6 +109,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 struct NormArgs {
   int dtype;
   const float* h; const float* e; const float* a;  // a optional: x = h + e + a[i]
+  const float* a2;       // optional second addend (row i), used by the router kernel
   const float* g; float eps; int D;
   const int* rows; const int* ndev; int n;
   void* out; int out_scatter;
@@ -126,6 +128,8 @@ struct CombineArgs {
   float* a_dump;         // [N, D] by token, may be null
   void* n1_out;          // optional: next loop's RMSNorm(h' + e) * g1 by token
   const float* g1; float eps;
+  const float* d;        // optional depth-attention output (row i), added to h'
+  const float* smax;     // optional: shared experts weighted by smax[i] (else 1)
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
@@ -143,6 +147,7 @@ struct NormRouteArgs {
   NormArgs norm;         // x = h + e + a[i]; out = n2 (compacted rows), dump by token
   const void* Wr; int E, k; const float* bias;
   int* idx; float* gates; float* gap; int* dump_idx; float* dump_gap;
+  float* smax;           // optional [n]: maximum router probability of row i
   PermuteArgs perm;
   unsigned int* done;    // completion counter, zero between launches
 };
@@ -153,6 +158,19 @@ struct CompactArgs {
   int* rows_out; int* n_out; int* seg_out; int B, S;
 };
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+
+// -------------------------------------------------------- depth attention
+// Row i (token tok = i) and query head h attend over the token's own keys and
+// values of loops 0..t: k[tau][tok], v[tau][tok] with loop stride `lstride`
+// elements; online softmax in loop order.
+struct DepthAttnArgs {
+  int dtype;
+  const void* q; const void* k; const void* v; void* o;
+  long long lstride;     // elements between loops in k and v
+  int n, H, KV, dd, t;
+  float scale;
+};
+hipError_t launch_depth_attention(const DepthAttnArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- MLA helpers
 struct MlaNormArgs {

@@ -57,6 +57,17 @@ rdt_status validate_config(const rdt_config& c, std::string* why) {
   if (c.lora_rank % 8) return fail(why, RDT_E_UNSUPPORTED, "lora_rank must be a multiple of 8");
   const long long N = (long long)c.batch * c.seq;
   if (N * (c.top_k + c.n_shared_experts) > (1ll << 30)) return fail(why, RDT_E_UNSUPPORTED, "too many token rows");
+  if (c.parallel_block != 0 && c.parallel_block != 1) return fail(why, RDT_E_INVALID, "parallel_block must be 0 or 1");
+  if (c.shared_scale != 0 && c.shared_scale != 1) return fail(why, RDT_E_INVALID, "shared_scale must be 0 or 1");
+  if (c.da_heads < 0) return fail(why, RDT_E_INVALID, "da_heads is negative");
+  if (c.da_heads > 0) {
+    if (c.da_kv_heads <= 0 || c.da_heads % c.da_kv_heads)
+      return fail(why, RDT_E_INVALID, "da_heads must be a positive multiple of da_kv_heads");
+    if (c.da_head_dim != 16 && c.da_head_dim != 32 && c.da_head_dim != 64 && c.da_head_dim != 128)
+      return fail(why, RDT_E_UNSUPPORTED, "da_head_dim must be 16, 32, 64 or 128");
+    if (c.act_enabled) return fail(why, RDT_E_UNSUPPORTED, "depth attention with ACT halting");
+    if (c.max_T > 64) return fail(why, RDT_E_UNSUPPORTED, "depth attention needs max_T <= 64");
+  }
   return RDT_OK;
 }
 
@@ -123,6 +134,19 @@ Plan make_plan(const rdt_config& c, int T) {
   p.cum = take(N * 4);
   p.done = take(4);
   p.pos = take(4);
+  p.smax = take(N * 4);
+  p.da = c.da_heads > 0;
+  if (p.da) {
+    p.Hd = c.da_heads; p.KVd = c.da_kv_heads; p.dd = c.da_head_dim;
+    p.da_nd = take(N * D * e);
+    p.da_q = take(N * p.Hd * p.dd * e);
+    p.da_k = take(Tp * N * p.KVd * p.dd * e);
+    p.da_v = take(Tp * N * p.KVd * p.dd * e);
+    p.da_out = take(N * p.Hd * p.dd * e);
+    p.da_buf = take(N * D * 4);
+    p.da_cos = take(Tp * (p.dd / 2) * 4);
+    p.da_sin = take(Tp * (p.dd / 2) * 4);
+  }
   p.rope_len = p.S;
   p.total = off;
   return p;

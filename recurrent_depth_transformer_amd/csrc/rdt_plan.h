@@ -28,6 +28,11 @@ struct Plan {
   size_t done;              // completion counter of the fused router kernel
   size_t pos;               // decode position (one int, written before each step)
   int rope_len;             // positions in the RoPE tables
+  size_t smax;              // [N] float: maximum router probability per row
+  // depth attention (Dreamer): norm output, queries, per-loop keys/values
+  // [T+1][N][KVd*dd], attention output, projected output (float), depth RoPE
+  int da, Hd, KVd, dd;
+  size_t da_nd, da_q, da_k, da_v, da_out, da_buf, da_cos, da_sin;
   size_t total;
 };
 

@@ -87,11 +87,16 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       load4f<T>(Y + (long long)p * D + col, y);
       m[0] += gt * y[0]; m[1] += gt * y[1]; m[2] += gt * y[2]; m[3] += gt * y[3];
     }
+    const float sw = a.smax ? a.smax[i] : 1.f;   // shared-expert weight
     for (int s = 0; s < a.Se; ++s) {
       const long long p = (long long)n * k + (long long)s * n + i;
       float y[4];
       load4f<T>(Y + p * D + col, y);
-      m[0] += y[0]; m[1] += y[1]; m[2] += y[2]; m[3] += y[3];
+      m[0] += sw * y[0]; m[1] += sw * y[1]; m[2] += sw * y[2]; m[3] += sw * y[3];
+    }
+    if (a.d) {
+      const float4 dv = *reinterpret_cast<const float4*>(a.d + (long long)i * D + col);
+      m[0] += dv.x; m[1] += dv.y; m[2] += dv.z; m[3] += dv.w;
     }
     float* hp = a.h + (long long)tok * D + col;
     const float4 hv = *reinterpret_cast<const float4*>(hp);
@@ -267,9 +272,15 @@ __global__ __launch_bounds__(1024) void k_norm_route(NormRouteArgs a) {
     if (live && col < D) {
       const float4 hv = *reinterpret_cast<const float4*>(na.h + (long long)tok * D + col);
       const float4 ev = *reinterpret_cast<const float4*>(na.e + (long long)tok * D + col);
-      const float4 av = *reinterpret_cast<const float4*>(na.a + (long long)i * D + col);
-      x[c][0] = hv.x + ev.x + av.x; x[c][1] = hv.y + ev.y + av.y;
-      x[c][2] = hv.z + ev.z + av.z; x[c][3] = hv.w + ev.w + av.w;
+      x[c][0] = hv.x + ev.x; x[c][1] = hv.y + ev.y; x[c][2] = hv.z + ev.z; x[c][3] = hv.w + ev.w;
+      if (na.a2) {  // depth-attention output (Dreamer sequential block)
+        const float4 dv = *reinterpret_cast<const float4*>(na.a2 + (long long)i * D + col);
+        x[c][0] += dv.x; x[c][1] += dv.y; x[c][2] += dv.z; x[c][3] += dv.w;
+      }
+      if (na.a) {   // attention output (absent in the parallel block)
+        const float4 av = *reinterpret_cast<const float4*>(na.a + (long long)i * D + col);
+        x[c][0] += av.x; x[c][1] += av.y; x[c][2] += av.z; x[c][3] += av.w;
+      }
       ss += x[c][0] * x[c][0] + x[c][1] * x[c][1] + x[c][2] * x[c][2] + x[c][3] * x[c][3];
     }
   }
@@ -331,6 +342,7 @@ __global__ __launch_bounds__(1024) void k_norm_route(NormRouteArgs a) {
     const float pe = own ? expf(logit - mx) : 0.f;
     const float den = wave_sum(pe);
     const float gate = pe / den;
+    if (lane == 0 && a.smax) a.smax[i] = 1.f / den;  // the largest probability: exp(0) / den
     float sel = own ? logit + (a.bias ? a.bias[lane] : 0.f) : -INFINITY;
     bool avail = own;                              // not chosen yet
     float kth = 0.f;
@@ -601,6 +613,66 @@ hipError_t launch_copy_f32(float* dst, const float* src, long long n, hipStream_
   const long long n4 = n / 4;  // callers pass multiples of 4
   hipLaunchKernelGGL(k_copy_f32, dim3(fill_blocks(n4)), dim3(256), 0, s, reinterpret_cast<float4*>(dst),
                      reinterpret_cast<const float4*>(src), n4);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------- depth attention
+// One wave per (row, query head): the row's token attends over its own keys
+// and values of loops 0..t (at most 64 loops), online softmax in loop order.
+// Lane l holds elements [l*EPL, l*EPL + EPL) of the head (dd = 64 * EPL, or
+// dd < 64 with lanes >= dd idle).
+template <typename T, int EPL>
+__global__ __launch_bounds__(256) void k_depth_attention(DepthAttnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long job = (long long)blockIdx.x * 4 + wave;
+  if (job >= (long long)a.n * a.H) return;
+  const int i = (int)(job / a.H), h = (int)(job % a.H);
+  const int kvh = (h * a.KV) / a.H;
+  const int dd = a.dd;
+  const bool on = lane * EPL < dd;
+  const T* Q = reinterpret_cast<const T*>(a.q) + (long long)i * a.H * dd + (long long)h * dd + lane * EPL;
+  const long long kvoff = (long long)i * a.KV * dd + (long long)kvh * dd + lane * EPL;
+  float q[EPL], o[EPL];
+#pragma unroll
+  for (int x = 0; x < EPL; ++x) {
+    q[x] = on ? ST<T>::to_f(Q[x]) : 0.f;
+    o[x] = 0.f;
+  }
+  float mrun = -INFINITY, lrun = 0.f;
+  for (int tau = 0; tau <= a.t; ++tau) {
+    const T* K = reinterpret_cast<const T*>(a.k) + tau * a.lstride + kvoff;
+    const T* V = reinterpret_cast<const T*>(a.v) + tau * a.lstride + kvoff;
+    float s = 0.f;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) s += on ? q[x] * ST<T>::to_f(K[x]) : 0.f;
+    s = wave_sum(s) * a.scale;
+    const float mnew = fmaxf(mrun, s);
+    const float alpha = expf(mrun - mnew), p = expf(s - mnew);
+    lrun = lrun * alpha + p;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) o[x] = o[x] * alpha + (on ? p * ST<T>::to_f(V[x]) : 0.f);
+    mrun = mnew;
+  }
+  if (on) {
+    T* O = reinterpret_cast<T*>(a.o) + (long long)i * a.H * dd + (long long)h * dd + lane * EPL;
+    const float inv = 1.f / lrun;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) O[x] = ST<T>::from_f(o[x] * inv);
+  }
+}
+
+hipError_t launch_depth_attention(const DepthAttnArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  if (a.dd > 128 || a.t < 0 || a.H % a.KV) return hipErrorInvalidValue;
+  const long long jobs = (long long)a.n * a.H;
+  dim3 grid((unsigned)((jobs + 3) / 4));
+  if (a.dtype == DT_F32) {
+    if (a.dd > 64) hipLaunchKernelGGL((k_depth_attention<float, 2>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_depth_attention<float, 1>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.dd > 64) hipLaunchKernelGGL((k_depth_attention<bf16_t, 2>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_depth_attention<bf16_t, 1>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -58,7 +58,8 @@ def _prefill_decode(cfg, inputs, W, T):
     return h.reshape(B * S, D), loops.reshape(-1), idx.reshape(T, B * S, -1), S0
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_bf16", "gqa_small", "mla_small", "act_small", "wide_small"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_bf16", "gqa_small", "mla_small", "act_small", "wide_small",
+                                  "dreamer_tiny", "dreamer_small", "parallel_small"])
 def test_prefill_then_decode_matches_full_forward(name):
     cfg = get_config(name)
     T = cfg["T"]

@@ -25,11 +25,14 @@ def _report(name, **kw):
     print(f"[parity] {name}: " + ", ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
 
 
-@pytest.mark.parametrize("name", ["tiny", "gqa_small", "wide_small", "act_small", "mla_small"])
+@pytest.mark.parametrize("name", ["tiny", "gqa_small", "wide_small", "act_small", "mla_small", "dreamer_small",
+                                  "parallel_small"])
 def test_closed_form_injection(name):
     cfg = get_config(name)
     inp = make_inputs(cfg)
     inp["Wo"] = np.zeros_like(inp["Wo"])
+    if cfg["da_heads"]:
+        inp["Wo_da"] = np.zeros_like(inp["Wo_da"])
     inp["Wd"] = np.zeros_like(inp["Wd"])
     if cfg["n_shared_experts"]:
         inp["Wsd"] = np.zeros_like(inp["Wsd"])
@@ -45,7 +48,8 @@ def test_closed_form_injection(name):
     assert err <= 1e-5 * max(1.0, np.max(np.abs(closed)))
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_bf16", "gqa_small", "wide_small", "act_small", "mla_small"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_bf16", "gqa_small", "wide_small", "act_small", "mla_small",
+                                  "dreamer_tiny", "dreamer_small", "parallel_small"])
 def test_end_to_end_forced(name):
     cfg = get_config(name)
     T = cfg["T"]
@@ -80,7 +84,7 @@ def test_end_to_end_forced(name):
         assert 0 < res["loops"].min() <= res["loops"].max() <= T
 
 
-@pytest.mark.parametrize("name", ["gqa_small", "act_small"])
+@pytest.mark.parametrize("name", ["gqa_small", "act_small", "dreamer_small"])
 def test_graph_matches_eager_bitwise(name):
     cfg = get_config(name)
     r1, inp, _, W = run_gpu(cfg, dumps=False, graph=True)
