@@ -49,6 +49,12 @@ def describe(cfg: dict) -> str:
         extra += f", depth-wise LoRA r{cfg['lora_rank']}"
     if cfg["act"]:
         extra += f", ACT halting at {cfg['act_threshold']}"
+    if cfg.get("da_heads"):
+        extra += f", depth attention {cfg['da_heads']}/{cfg['da_kv_heads']} of {cfg['da_head_dim']}"
+    if cfg.get("parallel"):
+        extra += ", parallel sublayers"
+    if cfg.get("shared_scale"):
+        extra += ", shared expert weighted by the max router probability"
     return (f"{cfg['name']}: batch {cfg['batch']}, seq {cfg['seq']}, dim {cfg['dim']}, {att}, {moe}, "
             f"SwiGLU hidden {cfg['expert_dim']}, T={cfg['T']}{extra}, {cfg['dtype']}")
 
@@ -89,6 +95,31 @@ def gate_up_bytes(cfg: dict, counts_per_loop, elt: int) -> float:
         all_rows = rows + cfg["n_shared_experts"] * n_tok
         tot += used * 2 * F * D * elt + all_rows * D * elt + all_rows * F * elt
     return tot / max(1, len(counts_per_loop))
+
+
+def decode_step_bytes(cfg: dict, route_idx, pos: int, elt: int) -> float:
+    """Algorithmic HBM bytes of one decode step (one token per sequence through
+    T loops): per loop the attention and router weights, the gate/up/down
+    matrices of every expert some token chose (and the shared experts), the
+    cached keys/values of positions 0..pos, and the state rows."""
+    D, F, B, T = cfg["dim"], cfg["expert_dim"], cfg["batch"], cfg["T"]
+    H, KV, d = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    attn_w = (H * d + 2 * KV * d) * D + D * H * d
+    tot = 0.0
+    for t in range(T):
+        used = len({int(x) for x in route_idx[t].reshape(-1) if x >= 0}) + cfg["n_shared_experts"]
+        tot += (attn_w + cfg["n_experts"] * D) * elt + used * 3 * F * D * elt
+        tot += B * (pos + 1) * 2 * KV * d * elt + B * D * 4 * 4
+    return tot
+
+
+def depth_attention_bytes(cfg: dict, elt: int) -> float:
+    """Algorithmic bytes of one depth-attention launch, averaged over loops:
+    every token reads its query, the keys and values of loops 0..t and writes
+    its output (mean t + 1 = (T + 1) / 2)."""
+    N, T = cfg["batch"] * cfg["seq"], cfg["T"]
+    Hd, KVd, dd = cfg["da_heads"], cfg["da_kv_heads"], cfg["da_head_dim"]
+    return N * (2 * Hd * dd + (T + 1) / 2 * 2 * KVd * dd) * elt
 
 
 def source_hash(names) -> str:
@@ -144,6 +175,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also print the per-stage breakdown to stderr")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the decode-step and depth-attention (dreamer workload) measurements")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (calibrates HBM counters) and exit")
     args = ap.parse_args()
@@ -231,6 +264,10 @@ def main():
                            else "k_grouped_gemm<bf16,192,128,0,2>") + " (expert gate/up + SwiGLU)",
                 "avg_launch_us": round(gu_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(gu_bytes)}
 
+    extras = None
+    if not args.no_extras:
+        extras = {"decode": bench_decode(args, cfg, W, stream), "dreamer": bench_dreamer(args)}
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -248,8 +285,87 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages_us": {k: round(v[0] * 1e3, 2) for k, v in stage_avg.items() if v[1]},
+        "extras": extras,
     }
     print(json.dumps(res), flush=True)
+
+
+def _time(fn, steps: int, warmup: int, stream) -> float:
+    """Mean milliseconds of fn() over `steps` calls after `warmup` calls,
+    HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_decode(args, cfg: dict, W: dict, stream) -> dict:
+    """One-token decode step on the bench workload: prefill seq-1 positions,
+    then time steps at the last position (each step rewrites the same cache
+    row, so every step does the same work)."""
+    import torch
+
+    import recurrent_depth_transformer_amd as rdt
+    B, S, D, T = cfg["batch"], cfg["seq"], cfg["dim"], cfg["T"]
+    blk = rdt.RecurrentBlock(dict(cfg, seq=S - 1), graph=True)
+    cache = blk.new_cache(T, S)
+    h0, e = W["h0"].view(B, S, D), W["e"].view(B, S, D)
+    blk.prefill(h0[:, :S - 1].contiguous().view(-1, D), e[:, :S - 1].contiguous().view(-1, D), W, T, cache, S)
+    ht, et = h0[:, S - 1].contiguous(), e[:, S - 1].contiguous()
+    out = torch.empty_like(ht)
+    ridx = torch.empty(T, B, cfg["top_k"], dtype=torch.int32, device="cuda")
+    blk.decode_step(ht, et, W, T, S - 1, cache, S, out=out, aux={"route_idx": ridx})
+    torch.cuda.synchronize()
+    ms = _time(lambda: blk.decode_step(ht, et, W, T, S - 1, cache, S, out=out), args.steps, args.warmup, stream)
+    elt = 4 if cfg["dtype"] == "f32" else 2
+    nbytes = decode_step_bytes(cfg, ridx.cpu().numpy(), S - 1, elt)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"{cfg['name']}: {B} sequence(s), one token at position {S - 1} after a {S - 1}-token "
+                        f"prefill, T={T}, per-loop KV cache",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "whole decode step (weights, chosen experts, cache)",
+                         "algorithmic_bytes_per_step": int(nbytes)},
+            "cache_bytes": blk.cache_size(T, S)}
+
+
+def bench_dreamer(args) -> dict:
+    """Forward throughput of the full-size Dreamer workload (depth attention,
+    max-score shared expert) and the roofline of the depth-attention kernel."""
+    import torch
+
+    import recurrent_depth_transformer_amd as rdt
+    from rdt_inputs import get_config, make_inputs
+    cfg = get_config("dreamer")
+    T, N = cfg["T"], cfg["batch"] * cfg["seq"]
+    W = rdt.device_weights(make_inputs(cfg), cfg, "cuda")
+    blk = rdt.RecurrentBlock(cfg, graph=True)
+    out = torch.empty_like(W["h0"])
+    ws = blk.workspace(T)
+    stream = torch.cuda.current_stream()
+    steps = max(3, args.steps // 10)
+    ms = _time(lambda: blk.forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws), steps, 2, stream)
+    _, st = blk.profile_forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws)
+    da_ms, da_n = st["depth_attention"]
+    da_us = da_ms / max(1, da_n) * 1e3
+    elt = 2
+    nbytes = depth_attention_bytes(cfg, elt)
+    achieved = nbytes / (da_us * 1e-6) / 1e9
+    return {"workload": describe(cfg), "ms_per_step": round(ms, 4),
+            "value": round(N * T / (ms * 1e-3), 1), "unit": "token-loops/s",
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "k_depth_attention (Dreamer depth attention)", "avg_launch_us": round(da_us, 2),
+                         "algorithmic_bytes_per_launch": int(nbytes)},
+            "stages_us": {k: round(v[0] / v[1] * 1e3, 2) for k, v in st.items() if v[1]}}
 
 
 if __name__ == "__main__":

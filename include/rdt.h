@@ -342,7 +342,8 @@ typedef enum rdt_stage {
   RDT_STAGE_COMBINE = 9,  /* MoE combine + LTI injection (+ ACT) */
   RDT_STAGE_COMPACT = 10, /* ACT active-list compaction */
   RDT_STAGE_OTHER = 11,   /* per-forward set-up, fills and dump copies */
-  RDT_N_STAGES = 12
+  RDT_STAGE_DEPTH_ATTN = 12, /* Dreamer depth attention over a token's own loop states */
+  RDT_N_STAGES = 13
 } rdt_stage;
 
 /*

@@ -19,6 +19,9 @@ gains = 1, router bias = 0):
             depth-wise LoRA rank 16 per loop on the attention output (~ N(0, 0.01)),
             ACT halting with w ~ N(0, 0.05), threshold 0.99
 
+  dreamer   bf16, 4x2048, D 1024, GQA 16/4 of 64, depth attention 16/4 of 64, 16 experts
+            top-2 + 1 shared weighted by the max router probability, F 1408, T 8
+
 The ``*_small`` workloads keep each family's structure at sizes a CPU reference
 finishes in seconds, with sequence lengths and widths that leave ragged tiles.
 
@@ -97,6 +100,10 @@ WORKLOADS = {
                       lora_rank=8, n_lora=4, act=True),
     # ---- Dreamer block variants (depth attention, parallel sublayers,
     # shared expert scaled by the max router score) ----
+    "dreamer": _cfg(batch=4, seq=2048, dim=1024, n_heads=16, n_kv_heads=4, head_dim=64,
+                    da_heads=16, da_kv_heads=4, da_head_dim=64, n_experts=16,
+                    n_shared_experts=1, shared_scale=1, top_k=2, expert_dim=1408, T=8,
+                    dtype="bf16"),
     "dreamer_small": _cfg(batch=2, seq=72, dim=256, n_heads=4, n_kv_heads=2, head_dim=64,
                           da_heads=4, da_kv_heads=2, da_head_dim=32, n_experts=8,
                           n_shared_experts=1, shared_scale=1, top_k=2, expert_dim=192,

@@ -27,7 +27,7 @@ EXPORTED_SYMBOLS = [
     "rdt_cache_size", "rdt_prefill", "rdt_decode_workspace_size", "rdt_decode_step",
     "rdt_router_bias_update", "rdt_expert_depths",
 ]
-N_STAGES = 12
+N_STAGES = 13
 
 RDT_OK, RDT_E_INVALID, RDT_E_UNSUPPORTED, RDT_E_UNSTABLE, RDT_E_WORKSPACE, RDT_E_HIP = 0, -1, -2, -3, -4, -5
 _STATUS = {RDT_E_INVALID: "RDT_E_INVALID", RDT_E_UNSUPPORTED: "RDT_E_UNSUPPORTED",

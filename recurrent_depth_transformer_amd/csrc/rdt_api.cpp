@@ -329,7 +329,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       DepthAttnArgs da{};
       da.dtype = dt; da.q = dq; da.k = dk; da.v = dvb; da.o = dout; da.lstride = (long long)lpl;
       da.n = N; da.H = P.Hd; da.KV = P.KVd; da.dd = P.dd; da.t = t; da.scale = 1.f / sqrtf((float)P.dd);
-      LAUNCH(RDT_STAGE_ATTN, launch_depth_attention(da, s));
+      LAUNCH(RDT_STAGE_DEPTH_ATTN, launch_depth_attention(da, s));
       DenseGemm gdo{};
       gdo.dtype = dt; gdo.A = dout; gdo.lda = qw; gdo.K = qw; gdo.batch = 1; gdo.epi = EPI_STORE;
       gdo.rows = nullptr; gdo.gather = 0; gdo.M = N; gdo.Mdev = nullptr;
@@ -674,7 +674,7 @@ static rdt_status launch(rdt_handle* h, const Fwd& f, hipStream_t s) {
 
 static const char* kStageNames[RDT_N_STAGES] = {"norm1", "qkv", "attention", "out_proj", "norm2", "router",
                                                 "permute", "expert_gate_up", "expert_down", "combine",
-                                                "compact", "other"};
+                                                "compact", "other", "depth_attention"};
 
 extern "C" const char* rdt_stage_name(int32_t stage) {
   return (stage >= 0 && stage < RDT_N_STAGES) ? kStageNames[stage] : "";

@@ -67,3 +67,25 @@ def test_fullsize(name):
         err = np.max(np.abs(res["h"] - ref["h"]))
         print(f"[fullsize] gqa end-to-end max|dh|/rms={err / rms(ref['h']):.3e}", flush=True)
         assert err <= TOL * rms(ref["h"])
+
+
+@pytest.mark.parametrize("name", ["gqa", "mla", "dreamer"])
+def test_fullsize_decode_last_position_matches_forward(name):
+    """At the sizes bench.py times: prefill seq-1 positions, decode the last
+    one, and compare with the full-sequence forward (same kernels: equal)."""
+    import torch
+
+    from recurrent_depth_transformer_amd import RecurrentBlock
+    cfg = get_config(name)
+    B, S, D, T = cfg["batch"], cfg["seq"], cfg["dim"], cfg["T"]
+    full, _, _, W = run_gpu(cfg, dumps=False)
+    blk = RecurrentBlock(dict(cfg, seq=S - 1))
+    cache = blk.new_cache(T, S)
+    h0, e = W["h0"].view(B, S, D), W["e"].view(B, S, D)
+    pre = blk.prefill(h0[:, :S - 1].contiguous().view(-1, D), e[:, :S - 1].contiguous().view(-1, D), W, T, cache, S)
+    last = blk.decode_step(h0[:, S - 1].contiguous(), e[:, S - 1].contiguous(), W, T, S - 1, cache, S)
+    torch.cuda.synchronize()
+    hf = full["h"].reshape(B, S, D)
+    print(f"[fullsize-decode] {name}: prefill {S - 1} x {B}, decode position {S - 1}", flush=True)
+    np.testing.assert_array_equal(pre.cpu().numpy().reshape(B, S - 1, D), hf[:, :S - 1])
+    np.testing.assert_array_equal(last.cpu().numpy(), hf[:, S - 1])
