@@ -371,8 +371,10 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
         pick_tile(N, 2 * KVd, P.d, &gkv.bm, &gkv.bn);
         LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(gkv, s));
       }
-      LAUNCH(RDT_STAGE_QKV, append(t, 0, kb));
-      LAUNCH(RDT_STAGE_QKV, append(t, 1, vb));
+      if (f.cache) {
+        LAUNCH(RDT_STAGE_QKV, append(t, 0, kb));
+        LAUNCH(RDT_STAGE_QKV, append(t, 1, vb));
+      }
       AttnArgs aa{};
       aa.dtype = dt; aa.dqk = P.d; aa.dv = P.d;
       aa.q = q; aa.q_ld = Hd; aa.q_hs = P.d;
@@ -408,7 +410,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       mn.rows = prev; mn.ndev = nprev; mn.n = N; mn.cqn = cqn; mn.latent = latent;
       mn.cosb = cosb; mn.sinb = sinb; mn.S = P.S; mn.pos_dev = pos_dev;
       LAUNCH(RDT_STAGE_QKV, launch_mla_norm(mn, s));
-      LAUNCH(RDT_STAGE_QKV, append(t, 0, latent));
+      if (f.cache) LAUNCH(RDT_STAGE_QKV, append(t, 0, latent));
       // query up-projection (compacted rows)
       DenseGemm g2{};
       g2.dtype = dt; g2.A = cqn; g2.lda = P.ql; g2.K = P.ql; g2.batch = 1; g2.epi = EPI_STORE;

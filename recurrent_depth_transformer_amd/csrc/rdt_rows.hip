@@ -65,7 +65,10 @@ hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
 // ---------------------------------------------------------- combine + inject
 // m = sum_j gate_j * Y[inv_j] + sum_s Y_shared_s;  h = A*h + B*e + a + m
 // ACT: cum += sigmoid(w . h); loops = t + 1.
-template <typename T>
+// All column vectors of a row are handled at once (NV float4 per lane), so the
+// expert-output gathers of every column are in flight together; the next
+// loop's RMSNorm works from the registers that hold h' + e.
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave;
@@ -74,29 +77,43 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int tok = a.rows ? a.rows[i] : i;
   const int D = a.D, k = a.k;
   const T* Y = reinterpret_cast<const T*>(a.Y);
-  float z = 0.f;
-#pragma unroll 1
-  for (int c = 0; c < MAXV; ++c) {
+  float m[NV][4];
+#pragma unroll
+  for (int c = 0; c < NV; ++c) m[c][0] = m[c][1] = m[c][2] = m[c][3] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int p = a.inv[(long long)i * k + j];
+    const float gt = a.gates[(long long)i * k + j];
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      const int col = (c * 64 + lane) * 4;
+      if (col < D) {
+        float y[4];
+        load4f<T>(Y + (long long)p * D + col, y);
+        m[c][0] += gt * y[0]; m[c][1] += gt * y[1]; m[c][2] += gt * y[2]; m[c][3] += gt * y[3];
+      }
+    }
+  }
+  const float sw = a.smax ? a.smax[i] : 1.f;   // shared-expert weight
+  for (int s = 0; s < a.Se; ++s) {
+    const long long p = (long long)n * k + (long long)s * n + i;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      const int col = (c * 64 + lane) * 4;
+      if (col < D) {
+        float y[4];
+        load4f<T>(Y + p * D + col, y);
+        m[c][0] += sw * y[0]; m[c][1] += sw * y[1]; m[c][2] += sw * y[2]; m[c][3] += sw * y[3];
+      }
+    }
+  }
+  float z = 0.f, ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
     const int col = (c * 64 + lane) * 4;
-    if (col >= D) break;
-    float m[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int p = a.inv[(long long)i * k + j];
-      const float gt = a.gates[(long long)i * k + j];
-      float y[4];
-      load4f<T>(Y + (long long)p * D + col, y);
-      m[0] += gt * y[0]; m[1] += gt * y[1]; m[2] += gt * y[2]; m[3] += gt * y[3];
-    }
-    const float sw = a.smax ? a.smax[i] : 1.f;   // shared-expert weight
-    for (int s = 0; s < a.Se; ++s) {
-      const long long p = (long long)n * k + (long long)s * n + i;
-      float y[4];
-      load4f<T>(Y + p * D + col, y);
-      m[0] += sw * y[0]; m[1] += sw * y[1]; m[2] += sw * y[2]; m[3] += sw * y[3];
-    }
+    if (col >= D) continue;
     if (a.d) {
       const float4 dv = *reinterpret_cast<const float4*>(a.d + (long long)i * D + col);
-      m[0] += dv.x; m[1] += dv.y; m[2] += dv.z; m[3] += dv.w;
+      m[c][0] += dv.x; m[c][1] += dv.y; m[c][2] += dv.z; m[c][3] += dv.w;
     }
     float* hp = a.h + (long long)tok * D + col;
     const float4 hv = *reinterpret_cast<const float4*>(hp);
@@ -105,39 +122,30 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     const float4 Av = *reinterpret_cast<const float4*>(a.A + col);
     const float4 Bv = *reinterpret_cast<const float4*>(a.B + col);
     float4 hn;
-    hn.x = Av.x * hv.x + Bv.x * ev.x + av.x + m[0];
-    hn.y = Av.y * hv.y + Bv.y * ev.y + av.y + m[1];
-    hn.z = Av.z * hv.z + Bv.z * ev.z + av.z + m[2];
-    hn.w = Av.w * hv.w + Bv.w * ev.w + av.w + m[3];
+    hn.x = Av.x * hv.x + Bv.x * ev.x + av.x + m[c][0];
+    hn.y = Av.y * hv.y + Bv.y * ev.y + av.y + m[c][1];
+    hn.z = Av.z * hv.z + Bv.z * ev.z + av.z + m[c][2];
+    hn.w = Av.w * hv.w + Bv.w * ev.w + av.w + m[c][3];
     *reinterpret_cast<float4*>(hp) = hn;
     if (a.a_dump) *reinterpret_cast<float4*>(a.a_dump + (long long)tok * D + col) = av;
     if (a.act) {
       const float4 wv = *reinterpret_cast<const float4*>(a.w_halt + col);
       z += wv.x * hn.x + wv.y * hn.y + wv.z * hn.z + wv.w * hn.w;
     }
+    // u = h' + e for the next loop's first RMSNorm
+    m[c][0] = hn.x + ev.x; m[c][1] = hn.y + ev.y; m[c][2] = hn.z + ev.z; m[c][3] = hn.w + ev.w;
+    ss += m[c][0] * m[c][0] + m[c][1] * m[c][1] + m[c][2] * m[c][2] + m[c][3] * m[c][3];
   }
   if (a.n1_out) {
-    // next loop's first RMSNorm of u = h' + e, for the rows just updated
-    float ss = 0.f;
-    for (int c = 0; c < MAXV; ++c) {
-      const int col = (c * 64 + lane) * 4;
-      if (col >= D) break;
-      const float4 hv = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + col);
-      const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
-      const float u0 = hv.x + ev.x, u1 = hv.y + ev.y, u2 = hv.z + ev.z, u3 = hv.w + ev.w;
-      ss += u0 * u0 + u1 * u1 + u2 * u2 + u3 * u3;
-    }
     ss = wave_sum(ss);
     const float inv = 1.f / sqrtf(ss / (float)D + a.eps);
     T* dst = reinterpret_cast<T*>(a.n1_out) + (long long)tok * D;
-    for (int c = 0; c < MAXV; ++c) {
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
       const int col = (c * 64 + lane) * 4;
-      if (col >= D) break;
-      const float4 hv = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + col);
-      const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
+      if (col >= D) continue;
       const float4 gv = *reinterpret_cast<const float4*>(a.g1 + col);
-      float y[4] = {(hv.x + ev.x) * inv * gv.x, (hv.y + ev.y) * inv * gv.y, (hv.z + ev.z) * inv * gv.z,
-                    (hv.w + ev.w) * inv * gv.w};
+      float y[4] = {m[c][0] * inv * gv.x, m[c][1] * inv * gv.y, m[c][2] * inv * gv.z, m[c][3] * inv * gv.w};
       store4<T>(dst + col, y);
     }
   }
@@ -153,12 +161,21 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   if (lane == 0 && a.loops) a.loops[tok] = a.t + 1;
 }
 
+template <typename T>
+static hipError_t combine_t(const CombineArgs& a, hipStream_t s) {
+  dim3 grid((a.n + 3) / 4);
+  const int nv = (a.D + 255) / 256;
+  if (nv <= 1) hipLaunchKernelGGL((k_combine<T, 1>), grid, dim3(256), 0, s, a);
+  else if (nv <= 2) hipLaunchKernelGGL((k_combine<T, 2>), grid, dim3(256), 0, s, a);
+  else if (nv <= 4) hipLaunchKernelGGL((k_combine<T, 4>), grid, dim3(256), 0, s, a);
+  else if (nv <= 8) hipLaunchKernelGGL((k_combine<T, 8>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_combine<T, 16>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
-  dim3 grid((a.n + 3) / 4);
-  if (a.dtype == DT_F32) hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_combine<bf16_t>, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return a.dtype == DT_F32 ? combine_t<float>(a, s) : combine_t<bf16_t>(a, s);
 }
 
 // ------------------------------------------------------ expert permutation
@@ -617,62 +634,57 @@ hipError_t launch_copy_f32(float* dst, const float* src, long long n, hipStream_
 }
 
 // --------------------------------------------------------- depth attention
-// One wave per (row, query head): the row's token attends over its own keys
-// and values of loops 0..t (at most 64 loops), online softmax in loop order.
-// Lane l holds elements [l*EPL, l*EPL + EPL) of the head (dd = 64 * EPL, or
-// dd < 64 with lanes >= dd idle).
-template <typename T, int EPL>
+// A wave serves one token and 256/dd of its query heads: a head owns dd/4
+// consecutive lanes, each holding 4 of its elements, so the dot products
+// reduce over dd/4 lanes only. Keys and values of loops 0..t of the same
+// token; online softmax in loop order.
+template <typename T>
 __global__ __launch_bounds__(256) void k_depth_attention(DepthAttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int dd = a.dd, lph = dd >> 2, hpw = 64 / lph;   // lanes per head, heads per wave
+  const int wpt = (a.H + hpw - 1) / hpw;                 // waves per token
   const long long job = (long long)blockIdx.x * 4 + wave;
-  if (job >= (long long)a.n * a.H) return;
-  const int i = (int)(job / a.H), h = (int)(job % a.H);
-  const int kvh = (h * a.KV) / a.H;
-  const int dd = a.dd;
-  const bool on = lane * EPL < dd;
-  const T* Q = reinterpret_cast<const T*>(a.q) + (long long)i * a.H * dd + (long long)h * dd + lane * EPL;
-  const long long kvoff = (long long)i * a.KV * dd + (long long)kvh * dd + lane * EPL;
-  float q[EPL], o[EPL];
-#pragma unroll
-  for (int x = 0; x < EPL; ++x) {
-    q[x] = on ? ST<T>::to_f(Q[x]) : 0.f;
-    o[x] = 0.f;
-  }
+  if (job >= (long long)a.n * wpt) return;
+  const int i = (int)(job / wpt);
+  const int h = (int)(job % wpt) * hpw + lane / lph;
+  const bool on = h < a.H;
+  const int e0 = (lane % lph) * 4;
+  const int kvh = on ? (h * a.KV) / a.H : 0;
+  const long long kvoff = (long long)i * a.KV * dd + (long long)kvh * dd + e0;
+  float q[4] = {0.f, 0.f, 0.f, 0.f}, o[4] = {0.f, 0.f, 0.f, 0.f};
+  if (on) load4f<T>(reinterpret_cast<const T*>(a.q) + (long long)i * a.H * dd + (long long)h * dd + e0, q);
   float mrun = -INFINITY, lrun = 0.f;
   for (int tau = 0; tau <= a.t; ++tau) {
-    const T* K = reinterpret_cast<const T*>(a.k) + tau * a.lstride + kvoff;
-    const T* V = reinterpret_cast<const T*>(a.v) + tau * a.lstride + kvoff;
-    float s = 0.f;
-#pragma unroll
-    for (int x = 0; x < EPL; ++x) s += on ? q[x] * ST<T>::to_f(K[x]) : 0.f;
-    s = wave_sum(s) * a.scale;
+    float k[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (on) {
+      load4f<T>(reinterpret_cast<const T*>(a.k) + tau * a.lstride + kvoff, k);
+      load4f<T>(reinterpret_cast<const T*>(a.v) + tau * a.lstride + kvoff, v);
+    }
+    float s = q[0] * k[0] + q[1] * k[1] + q[2] * k[2] + q[3] * k[3];
+    for (int off = lph >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    s *= a.scale;
     const float mnew = fmaxf(mrun, s);
     const float alpha = expf(mrun - mnew), p = expf(s - mnew);
     lrun = lrun * alpha + p;
 #pragma unroll
-    for (int x = 0; x < EPL; ++x) o[x] = o[x] * alpha + (on ? p * ST<T>::to_f(V[x]) : 0.f);
+    for (int x = 0; x < 4; ++x) o[x] = o[x] * alpha + p * v[x];
     mrun = mnew;
   }
   if (on) {
-    T* O = reinterpret_cast<T*>(a.o) + (long long)i * a.H * dd + (long long)h * dd + lane * EPL;
     const float inv = 1.f / lrun;
-#pragma unroll
-    for (int x = 0; x < EPL; ++x) O[x] = ST<T>::from_f(o[x] * inv);
+    float r[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    store4<T>(reinterpret_cast<T*>(a.o) + (long long)i * a.H * dd + (long long)h * dd + e0, r);
   }
 }
 
 hipError_t launch_depth_attention(const DepthAttnArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
-  if (a.dd > 128 || a.t < 0 || a.H % a.KV) return hipErrorInvalidValue;
-  const long long jobs = (long long)a.n * a.H;
+  if (a.dd < 16 || a.dd > 128 || (a.dd & (a.dd - 1)) || a.t < 0 || a.H % a.KV) return hipErrorInvalidValue;
+  const int hpw = 256 / a.dd;
+  const long long jobs = (long long)a.n * ((a.H + hpw - 1) / hpw);
   dim3 grid((unsigned)((jobs + 3) / 4));
-  if (a.dtype == DT_F32) {
-    if (a.dd > 64) hipLaunchKernelGGL((k_depth_attention<float, 2>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_depth_attention<float, 1>), grid, dim3(256), 0, s, a);
-  } else {
-    if (a.dd > 64) hipLaunchKernelGGL((k_depth_attention<bf16_t, 2>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_depth_attention<bf16_t, 1>), grid, dim3(256), 0, s, a);
-  }
+  if (a.dtype == DT_F32) hipLaunchKernelGGL(k_depth_attention<float>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_depth_attention<bf16_t>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
