@@ -270,16 +270,12 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   int* idx = at<int>(ws, P.idx);
   float* gates = at<float>(ws, P.gates);
   float* gap = at<float>(ws, P.gap);
-  int* counts = at<int>(ws, P.counts);
-  int* offs = at<int>(ws, P.offs);
-  int* ts_gu = at<int>(ws, P.ts_gu);
-  int* ts_dn = at<int>(ws, P.ts_dn);
-  int* perm = at<int>(ws, P.perm);
-  int* inv = at<int>(ws, P.inv);
+  int* cnt2 = at<int>(ws, P.cnt);      // per-expert counts of even / odd loops
+  int* slot = at<int>(ws, P.slot);
+  int* pcap = at<int>(ws, P.pcap);
   char* hmid = at<char>(ws, P.hmid);
   char* ybuf = at<char>(ws, P.y);
-  unsigned int* done = at<unsigned int>(ws, P.done);
-  LAUNCH(RDT_STAGE_OTHER, launch_fill_i32(reinterpret_cast<int*>(done), 0, 1, s));
+  LAUNCH(RDT_STAGE_OTHER, launch_fill_i32(cnt2, 0, E, s));   // loop 0's counts; the combine clears the next
   // down-projection tile height: large tiles when experts see many rows
   // Expert GEMM tiles (measured on MI355X): gate/up 192x128 with a two-stage
   // ring (two workgroups per CU) for every shape; down 128x128 when experts
@@ -491,25 +487,21 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     nr.idx = idx; nr.gates = gates; nr.gap = gap;
     nr.dump_idx = f.aux.route_idx ? f.aux.route_idx + (size_t)t * N * k : nullptr;
     nr.dump_gap = f.aux.route_gap ? f.aux.route_gap + (size_t)t * N : nullptr;
-    PermuteArgs& pa = nr.perm;
-    pa.idx = idx; pa.ndev = ncur; pa.n_static = N; pa.E = E; pa.Se = P.Se; pa.k = k;
-    pa.counts = counts; pa.offs = offs; pa.perm = perm; pa.inv = inv;
-    pa.ts_gu = ts_gu; pa.bm_gu = gu_bm; pa.ts_dn = ts_dn; pa.bm_dn = dn_bm;
-    pa.counts_dump = f.aux.expert_counts ? f.aux.expert_counts + (size_t)t * E : nullptr;
-    nr.done = done;
+    int* cnt = cnt2 + (t & 1) * E;
+    nr.cnt = cnt; nr.slot = slot; nr.pcap = pcap; nr.cap = N;
     LAUNCH(RDT_STAGE_ROUTER, launch_norm_route(nr, s));
 
     // a7: grouped SwiGLU experts
     GroupedGemm gu{};
     gu.dtype = dt; gu.kind = 0; gu.A = n2; gu.lda = D;
-    gu.perm = perm; gu.offs = offs; gu.counts = counts; gu.tile_start = ts_gu; gu.ndev = ncur; gu.n_static = N;
+    gu.cnt = cnt; gu.pcap = pcap; gu.cap = N; gu.ndev = ncur; gu.n_static = N;
     gu.E = E; gu.Se = P.Se; gu.k = k; gu.W1 = w.Wg; gu.W2 = w.Wu; gu.S1 = w.Wsg; gu.S2 = w.Wsu;
     gu.N = P.F; gu.K = D; gu.C = hmid; gu.ldc = P.F; gu.max_mtiles = P.gu_max_mtiles;
     gu.bm = gu_bm; gu.bn = gu_bn; gu.ns = 2;
     LAUNCH(RDT_STAGE_EXPERT_GU, launch_grouped_gemm(gu, s));
     GroupedGemm gd{};
     gd.dtype = dt; gd.kind = 1; gd.A = hmid; gd.lda = P.F;
-    gd.perm = perm; gd.offs = offs; gd.counts = counts; gd.tile_start = ts_dn; gd.ndev = ncur; gd.n_static = N;
+    gd.cnt = cnt; gd.pcap = pcap; gd.cap = N; gd.ndev = ncur; gd.n_static = N;
     gd.E = E; gd.Se = P.Se; gd.k = k; gd.W1 = w.Wd; gd.W2 = nullptr; gd.S1 = w.Wsd; gd.S2 = nullptr;
     gd.N = D; gd.K = P.F; gd.C = ybuf; gd.ldc = D; gd.max_mtiles = P.dn_max_mtiles;
     // many rows per expert: large tiles; few rows: small tiles, deeper ring
@@ -520,7 +512,10 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     // a8: combine + LTI injection (+ ACT)
     CombineArgs ca{};
     ca.dtype = dt; ca.h = f.out; ca.e = f.e; ca.a = abuf; ca.A = w.A; ca.B = w.B;
-    ca.Y = ybuf; ca.gates = gates; ca.inv = inv; ca.k = k; ca.Se = P.Se; ca.D = D;
+    ca.Y = ybuf; ca.gates = gates; ca.idx = idx; ca.slot = slot; ca.cnt = cnt; ca.E = E;
+    ca.cnt_next = cnt2 + ((t + 1) & 1) * E;
+    ca.counts_dump = f.aux.expert_counts ? f.aux.expert_counts + (size_t)t * E : nullptr;
+    ca.k = k; ca.Se = P.Se; ca.D = D;
     ca.rows = cur; ca.ndev = ncur; ca.n = N;
     ca.act = act; ca.w_halt = w.w_halt; ca.thr = c.act_threshold; ca.cum = cum; ca.loops = f.aux.loops; ca.t = t;
     ca.cum_dump = f.aux.act_cum ? f.aux.act_cum + (size_t)t * N : nullptr;

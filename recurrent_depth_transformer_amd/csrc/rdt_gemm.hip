@@ -532,28 +532,48 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
   // KIND 0 produces BN/2 SwiGLU outputs per tile from BN/2 gate + BN/2 up rows
   const int OUTW = KIND == 0 ? BN / 2 : BN;
   const int ntn = (g.N + OUTW - 1) / OUTW;
-  // The grid is sized for the worst case; only the first total_mt * ntn
-  // blocks have a tile. Those are spread over the XCDs by dispatch order, and
-  // each XCD's share is remapped to consecutive tiles (shared A rows in L2).
-  const int total_mt = g.tile_start[G];
+  // Tile schedule from the per-expert counts: expert g (routed: cnt[g] rows;
+  // shared: n rows) owns ceil(rows / BM) consecutive m-tiles. The grid is
+  // sized for the worst case; only the first total_mt * ntn blocks have a
+  // tile. Those are spread over the XCDs by dispatch order, and each XCD's
+  // share is remapped to consecutive tiles (shared A rows in L2).
+  const int lane = threadIdx.x & 63;
+  auto rows_of = [&](int gg) { return gg < G ? (gg < g.E ? g.cnt[gg] : n) : 0; };
+  auto scan = [&](int v) {  // inclusive prefix sum over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(v, o, 64);
+      if (lane >= o) v += y;
+    }
+    return v;
+  };
+  int total_mt = 0;
+  for (int b0 = 0; b0 < G; b0 += 64) total_mt += __shfl(scan((rows_of(b0 + lane) + BM - 1) / BM), 63, 64);
   const int nb = total_mt * ntn;
   if ((int)blockIdx.x >= nb) return;
   const int L = xcd_remap(blockIdx.x, nb);
   const int mt = L / ntn, nt = L % ntn;  // consecutive tiles share the A rows
-  // group of this tile: number of groups that end at or before it (one ballot per 64 groups)
-  int grp = 0;
-  {
-    const int lane = threadIdx.x & 63;
-    for (int b0 = 0; b0 < G; b0 += 64) {
-      const bool ended = (b0 + lane < G) && g.tile_start[b0 + lane + 1] <= mt;
-      grp += __popcll(__ballot(ended));
+  // this tile's expert, its first tile and the first output row of its rows
+  int grp = -1, tstart = 0, rbase = 0;
+  for (int b0 = 0, ct = 0, cr = 0; b0 < G && grp < 0; b0 += 64) {
+    const int gg = b0 + lane, rows = rows_of(gg), tl = (rows + BM - 1) / BM;
+    const int it = scan(tl), ir = scan(gg < g.E ? rows : 0);
+    const int end = ct + it;
+    const unsigned long long hit = __ballot(gg < G && mt >= end - tl && mt < end);
+    if (hit) {
+      const int w = __ffsll((long long)hit) - 1;
+      grp = b0 + w;
+      tstart = __shfl(end - tl, w, 64);
+      rbase = cr + __shfl(ir - (gg < g.E ? rows : 0), w, 64);
     }
-    grp = __builtin_amdgcn_readfirstlane(grp);
+    ct += __shfl(it, 63, 64);
+    cr += __shfl(ir, 63, 64);
   }
+  grp = __builtin_amdgcn_readfirstlane(grp);
   const bool routed = grp < g.E;
-  const int rows_g = routed ? g.counts[grp] : n;
-  const int pbase = routed ? g.offs[grp] : n * g.k + (grp - g.E) * n;
-  const int ml0 = (mt - g.tile_start[grp]) * BM;
+  const int rows_g = routed ? g.cnt[grp] : n;
+  const int pbase = routed ? rbase : n * g.k + (grp - g.E) * n;
+  const int ml0 = (mt - tstart) * BM;
   const int n0 = nt * OUTW;
   const int tid = threadIdx.x;
   const T* A = reinterpret_cast<const T*>(g.A);
@@ -566,7 +586,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
     ap[i] = nullptr;
     if (m < rows_g) {
       int src;
-      if (KIND == 0) src = routed ? g.perm[pbase + m] : m;
+      if (KIND == 0) src = routed ? g.pcap[(long long)grp * g.cap + m] : m;
       else src = pbase + m;
       ap[i] = A + (long long)src * g.lda;
     }

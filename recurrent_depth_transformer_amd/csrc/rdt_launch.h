@@ -66,14 +66,17 @@ struct DenseGemm {
 hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s);
 
 // --------------------------------------------------------------- grouped GEMM
-// Experts 0..E-1 (routed, rows gathered through perm) and E..E+Se-1 (shared,
-// every active row). Output rows are in permuted order: routed rows of expert
-// g start at offs[g]; shared expert s starts at n*k + s*n.
+// Experts 0..E-1 (routed) and E..E+Se-1 (shared, every active row). Routed
+// expert g received cnt[g] rows, listed in pcap[g * cap + 0 .. cnt[g] - 1]
+// (any order). Output rows are grouped by expert: routed expert g starts at
+// the exclusive prefix sum of cnt, shared expert s at n*k + s*n. Every
+// workgroup rebuilds the prefix sums and the tile schedule (ceil(rows / bm)
+// tiles per expert) from cnt.
 struct GroupedGemm {
   int dtype;
   int kind;              // 0: gate/up + SwiGLU, 1: down projection
   const void* A; int lda;
-  const int* perm; const int* offs; const int* counts; const int* tile_start;
+  const int* cnt; const int* pcap; int cap;
   const int* ndev; int n_static;
   int E, Se, k;
   const void* W1; const void* W2;  // routed weights (gate/up: Wg, Wu; down: Wd)
@@ -81,7 +84,7 @@ struct GroupedGemm {
   int N, K;
   void* C; int ldc;
   int max_mtiles;
-  int bm, bn, ns;        // tile rows (must match the tile_start schedule), columns, stages
+  int bm, bn, ns;        // tile rows, columns, stages
 };
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s);
 
@@ -120,7 +123,12 @@ hipError_t launch_norm(const NormArgs& a, hipStream_t s);
 struct CombineArgs {
   int dtype;
   float* h; const float* e; const float* a; const float* A; const float* B;
-  const void* Y; const float* gates; const int* inv;
+  const void* Y; const float* gates;
+  // routed output row of (i, j): exclusive prefix of cnt at expert idx[i][j],
+  // plus slot[i][j]
+  const int* idx; const int* slot; const int* cnt; int E;
+  int* cnt_next;         // zeroed by workgroup 0 for the next loop's router
+  int* counts_dump;      // [E] copy of cnt (may be null)
   int k, Se, D;
   const int* rows; const int* ndev; int n;
   int act; const float* w_halt; float thr; float* cum; int* loops; int t;
@@ -133,23 +141,17 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
-struct PermuteArgs {
-  const int* idx; const int* ndev; int n_static;
-  int E, Se, k;
-  int* counts; int* offs; int* perm; int* inv;
-  int* ts_gu; int bm_gu; int* ts_dn; int bm_dn;
-  int* counts_dump;      // [E] may be null
-};
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 
-// Second RMSNorm + router + top-k; the last workgroup builds the permutation.
+
+// Second RMSNorm + router + top-k + expert slots. Each pick (i, j) of expert
+// e takes slot[i][j] = a unique index below cnt[e] (an atomic reservation per
+// workgroup and expert); pcap[e * cap + slot] = i. cnt must be zero on entry.
 struct NormRouteArgs {
-  NormArgs norm;         // x = h + e + a[i]; out = n2 (compacted rows), dump by token
+  NormArgs norm;         // x = h + e (+ a2[i]) (+ a[i]); out = n2 (compacted rows), dump by token
   const void* Wr; int E, k; const float* bias;
   int* idx; float* gates; float* gap; int* dump_idx; float* dump_gap;
   float* smax;           // optional [n]: maximum router probability of row i
-  PermuteArgs perm;
-  unsigned int* done;    // completion counter, zero between launches
+  int* cnt; int* slot; int* pcap; int cap;
 };
 hipError_t launch_norm_route(const NormRouteArgs& a, hipStream_t s);
 

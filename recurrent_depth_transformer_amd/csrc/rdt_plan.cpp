@@ -90,7 +90,6 @@ Plan make_plan(const rdt_config& c, int T) {
     p.dq = p.d; p.dv = p.d; p.hv = p.H * p.d; p.dr = p.d;
   }
   const size_t N = p.N, D = p.D, e = p.elt;
-  const int G = p.E + p.Se;
   p.gu_max_mtiles = (int)((N * p.k) / kGuBM + p.E + p.Se * ((N + kGuBM - 1) / kGuBM));
   p.dn_max_mtiles = (int)((N * p.k) / kDnBM + p.E + p.Se * ((N + kDnBM - 1) / kDnBM));
   size_t off = 0;
@@ -119,12 +118,9 @@ Plan make_plan(const rdt_config& c, int T) {
   p.idx = take(N * p.k * 4);
   p.gates = take(N * p.k * 4);
   p.gap = take(N * 4);
-  p.counts = take((size_t)(p.E + 1) * 4);
-  p.offs = take((size_t)(p.E + 1) * 4);
-  p.ts_gu = take((size_t)(G + 1) * 4);
-  p.ts_dn = take((size_t)(G + 1) * 4);
-  p.perm = take(N * p.k * 4);
-  p.inv = take(N * p.k * 4);
+  p.cnt = take((size_t)2 * p.E * 4);          // two loops' counts, used alternately
+  p.slot = take(N * p.k * 4);
+  p.pcap = take((size_t)p.E * N * 4);
   p.hmid = take(N * (p.k + p.Se) * p.F * e);
   p.y = take(N * (p.k + p.Se) * D * e);
   const size_t Tp = (size_t)(T > 0 ? T : 0) + 1;
@@ -132,7 +128,6 @@ Plan make_plan(const rdt_config& c, int T) {
   p.ncount = take(Tp * 4);
   p.seg = take(Tp * (p.B + 1) * 4);
   p.cum = take(N * 4);
-  p.done = take(4);
   p.pos = take(4);
   p.smax = take(N * 4);
   p.da = c.da_heads > 0;

@@ -22,10 +22,9 @@ struct Plan {
   // workspace byte offsets
   size_t cosb, sinb, n1, q, k_, v_, o, z, a, n2;
   size_t cq_raw, lat_raw, cqn, latent, qfull, qattn, olat, wukT;
-  size_t idx, gates, gap, counts, offs, ts_gu, ts_dn, perm, inv;
+  size_t idx, gates, gap, cnt, slot, pcap;
   size_t hmid, y;
   size_t lists, ncount, seg, cum;
-  size_t done;              // completion counter of the fused router kernel
   size_t pos;               // decode position (one int, written before each step)
   int rope_len;             // positions in the RoPE tables
   size_t smax;              // [N] float: maximum router probability per row

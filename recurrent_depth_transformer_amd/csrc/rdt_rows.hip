@@ -70,9 +70,26 @@ hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
 // loop's RMSNorm works from the registers that hold h' + e.
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  __shared__ int s_off[MAX_EXPERTS];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave;
   const int n = a.ndev ? *a.ndev : a.n;
+  // exclusive prefix of the per-expert counts (wave 0, one lane per expert)
+  if (wave == 0) {
+    const int c = lane < a.E ? a.cnt[lane] : 0;
+    int inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane < a.E) s_off[lane] = inc - c;
+    if (blockIdx.x == 0 && lane < a.E) {
+      if (a.counts_dump) a.counts_dump[lane] = c;
+      a.cnt_next[lane] = 0;                        // the next loop's router starts from zero
+    }
+  }
+  __syncthreads();
   if (i >= n) return;
   const int tok = a.rows ? a.rows[i] : i;
   const int D = a.D, k = a.k;
@@ -81,7 +98,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 #pragma unroll
   for (int c = 0; c < NV; ++c) m[c][0] = m[c][1] = m[c][2] = m[c][3] = 0.f;
   for (int j = 0; j < k; ++j) {
-    const int p = a.inv[(long long)i * k + j];
+    const int p = s_off[a.idx[(long long)i * k + j]] + a.slot[(long long)i * k + j];
     const float gt = a.gates[(long long)i * k + j];
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
@@ -178,84 +195,6 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   return a.dtype == DT_F32 ? combine_t<float>(a, s) : combine_t<bf16_t>(a, s);
 }
 
-// ------------------------------------------------------ expert permutation
-// One workgroup of 1024 threads. Rows are taken in chunks of 1024; a ballot per
-// expert ranks the rows of one wave that chose it, wave totals are scanned per
-// expert, and a running count carries across chunks. Positions inside an
-// expert therefore follow row order (a stable counting sort, no atomics).
-__device__ void permute_block(const PermuteArgs& a) {
-  __shared__ unsigned long long wmask[16][MAX_EXPERTS];
-  __shared__ int wbase[16][MAX_EXPERTS];
-  __shared__ int run[MAX_EXPERTS];
-  __shared__ int offs_s[MAX_EXPERTS + 1];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n = a.ndev ? *a.ndev : a.n_static;
-  const int E = a.E, k = a.k;
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  if (tid < MAX_EXPERTS) run[tid] = 0;
-  __syncthreads();
-  for (int c0 = 0; c0 < n; c0 += 1024) {
-    const int i = c0 + tid;
-    unsigned long long sel = 0;
-    if (i < n)
-      for (int j = 0; j < k; ++j) sel |= 1ull << a.idx[(long long)i * k + j];
-    for (int e = 0; e < E; ++e) {
-      const unsigned long long m = __ballot((sel >> e) & 1ull);
-      if (lane == 0) wmask[wave][e] = m;
-    }
-    __syncthreads();
-    if (tid < E) {
-      int acc = run[tid];
-      for (int w = 0; w < 16; ++w) {
-        wbase[w][tid] = acc;
-        acc += __popcll(wmask[w][tid]);
-      }
-      run[tid] = acc;
-    }
-    __syncthreads();
-    if (i < n)
-      for (int j = 0; j < k; ++j) {
-        const int e = a.idx[(long long)i * k + j];
-        a.inv[(long long)i * k + j] = wbase[wave][e] + __popcll(wmask[wave][e] & lt);
-      }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      offs_s[e] = acc;
-      acc += run[e];
-    }
-    offs_s[E] = acc;
-    const int G = E + a.Se;
-    int tg = 0, td = 0;
-    for (int g = 0; g < G; ++g) {
-      const int cnt = g < E ? run[g] : n;
-      a.ts_gu[g] = tg;
-      a.ts_dn[g] = td;
-      tg += (cnt + a.bm_gu - 1) / a.bm_gu;
-      td += (cnt + a.bm_dn - 1) / a.bm_dn;
-    }
-    a.ts_gu[G] = tg;
-    a.ts_dn[G] = td;
-  }
-  __syncthreads();
-  if (tid < E) {
-    a.counts[tid] = run[tid];
-    a.offs[tid] = offs_s[tid];
-    if (a.counts_dump) a.counts_dump[tid] = run[tid];
-  }
-  if (tid == 0) a.offs[E] = offs_s[E];
-  for (int i = tid; i < n; i += 1024)
-    for (int j = 0; j < k; ++j) {
-      const long long q = (long long)i * k + j;
-      const int p = offs_s[a.idx[q]] + a.inv[q];
-      a.inv[q] = p;
-      a.perm[p] = i;
-    }
-}
-
-__global__ __launch_bounds__(1024) void k_permute(PermuteArgs a) { permute_block(a); }
 
 // ----------------------------------------- second RMSNorm + router + permute
 // A workgroup of 16 waves takes 16 compacted rows. Each wave forms one row
@@ -264,15 +203,18 @@ __global__ __launch_bounds__(1024) void k_permute(PermuteArgs a) { permute_block
 // from 16x16x32 MFMAs: wave w takes expert tile (w % NT) and every (16/NT)-th
 // k-step, partial tiles are summed through LDS. Then one wave per row: softmax
 // gates over all experts, top-k on logit + bias by k rounds of a wave argmax
-// (equal scores go to the lower expert). The last workgroup to finish (an
-// atomic completion count) builds the stable expert permutation.
+// (equal scores go to the lower expert). Expert slots: the workgroup counts
+// its picks per expert in LDS, reserves a contiguous range of slots per
+// expert with one atomic add on cnt, and hands the slots out; the slot order
+// inside an expert is arbitrary (each row's expert output does not depend on
+// which rows share its GEMM tile).
 template <typename T, int NV>
 __global__ __launch_bounds__(1024) void k_norm_route(NormRouteArgs a) {
   constexpr int KC = 4096 / (int)sizeof(T);        // columns per LDS chunk
   constexpr int LDA = KC + 16 / (int)sizeof(T);    // padded row stride
   __shared__ __align__(16) T As[16 * LDA];
   __shared__ int s_idx[16][MAX_EXPERTS];         // chosen experts of the 16 rows
-  __shared__ int is_last;
+  __shared__ int s_cnt[MAX_EXPERTS], s_base[MAX_EXPERTS];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const NormArgs& na = a.norm;
   const int i = blockIdx.x * 16 + wave;
@@ -384,27 +326,26 @@ __global__ __launch_bounds__(1024) void k_norm_route(NormRouteArgs a) {
       if (a.dump_gap) a.dump_gap[tok] = gp;
     }
   }
-  // Wave 0 publishes the block's expert choices (the only data the permutation
-  // reads) and releases them with one device-scope fence; the last workgroup
-  // to count in acquires and builds the permutation. A fence per wave would
-  // write back the XCD's L2 once per wave.
+  // expert slots: local ranks through LDS counters, one global reservation
+  // per expert and workgroup
+  if (threadIdx.x < MAX_EXPERTS) s_cnt[threadIdx.x] = 0;
   __syncthreads();
-  if (wave == 0) {
-    for (int q = lane; q < 16 * k; q += 64) {
-      const int r = q / k, row = blockIdx.x * 16 + r;
-      if (row < n) a.idx[(long long)row * k + (q - r * k)] = s_idx[r][q - r * k];
-    }
-    __threadfence();
-    if (lane == 0) {
-      const bool last = atomicAdd(a.done, 1u) == gridDim.x - 1;
-      if (last) __threadfence();
-      is_last = last;
-    }
+  int local = 0, ex = -1;
+  const int q = threadIdx.x;                       // pick q = (row r, choice j)
+  const int r = q / (k > 0 ? k : 1), jj = q - r * k;
+  const int row = blockIdx.x * 16 + r;
+  if (q < 16 * k && row < n) {
+    ex = s_idx[r][jj];
+    local = atomicAdd(&s_cnt[ex], 1);
   }
   __syncthreads();
-  if (is_last) {
-    permute_block(a.perm);
-    if (threadIdx.x == 0) atomicExch(a.done, 0u);  // ready for the next launch
+  if (threadIdx.x < E && s_cnt[threadIdx.x] > 0) s_base[threadIdx.x] = atomicAdd(&a.cnt[threadIdx.x], s_cnt[threadIdx.x]);
+  __syncthreads();
+  if (ex >= 0) {
+    const int sl = s_base[ex] + local;
+    a.idx[(long long)row * k + jj] = ex;
+    a.slot[(long long)row * k + jj] = sl;
+    a.pcap[(long long)ex * a.cap + sl] = row;
   }
 }
 
@@ -421,14 +362,11 @@ static hipError_t norm_route_t(const NormRouteArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_norm_route(const NormRouteArgs& a, hipStream_t s) {
-  if (a.norm.n <= 0 || a.E > MAX_EXPERTS || a.E < 1 || a.k > a.E || a.norm.D % 8) return hipErrorInvalidValue;
+  if (a.norm.n <= 0 || a.E > MAX_EXPERTS || a.E < 1 || a.k > a.E || a.norm.D % 8 || 16 * a.k > 1024)
+    return hipErrorInvalidValue;
   return a.norm.dtype == DT_F32 ? norm_route_t<float>(a, s) : norm_route_t<bf16_t>(a, s);
 }
 
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, a);
-  return hipGetLastError();
-}
 
 // -------------------------------------------------------- ACT compaction
 // Stable filter of the active list (tokens whose cumulative halting sum is
