@@ -96,6 +96,14 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   }
   const float sc = a.scale * 1.4426950408889634f;  // exp2 domain
   const int nkt = (kmax + KT - 1) / KT;
+  // first query position of this wave: tiles that end at or before it need
+  // no causal mask
+  int qlo = 0x7fffffff;
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs)
+    if (qpos[qs] >= 0) qlo = min(qlo, qpos[qs]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) qlo = min(qlo, __shfl_xor(qlo, o, 64));
 
   // ---- K/V tile: global -> registers -> LDS (V transposed)
   uint4 rk[KL], rv0[VL], rv1[VL];
@@ -183,31 +191,41 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
           for (int qs = 0; qs < QS; ++qs) mma(s[kb][qs], kf, qf[qs][ks]);
         }
       }
-      // scale, causal mask, online softmax (per query = per lane column)
+      // scale, causal mask (only on tiles that reach a query or the end of
+      // the keys), online softmax (per query = per lane column)
+      const bool masked = k0 + KT - 1 > qlo || k0 + KT > kmax;
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) {
         float mx = -INFINITY;
+        if (masked) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+          for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kp = k0 + kb * 16 + lg * 4 + r;
-            float x = s[kb][qs][r] * sc;
-            if (kp > qpos[qs] || kp >= kmax) x = -INFINITY;
-            s[kb][qs][r] = x;
-            mx = fmaxf(mx, x);
-          }
+            for (int r = 0; r < 4; ++r) {
+              const int kp = k0 + kb * 16 + lg * 4 + r;
+              float x = s[kb][qs][r];
+              if (kp > qpos[qs] || kp >= kmax) x = -INFINITY;
+              s[kb][qs][r] = x;
+              mx = fmaxf(mx, x);
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][qs][r]);
+        }
+        mx *= sc;  // scores stay raw; the scale (> 0) is applied inside the exponent
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mnew = fmaxf(mrow[qs], mx);
         const float base = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = exp2f(mrow[qs] - base);
+        const float alpha = __builtin_amdgcn_exp2f(mrow[qs] - base);
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = exp2f(s[kb][qs][r] - base);
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qs][r], sc, -base));
             s[kb][qs][r] = p;
             rs += p;
           }
@@ -215,12 +233,14 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
         rs += __shfl_xor(rs, 32, 64);
         lrow[qs] = lrow[qs] * alpha + rs;
         mrow[qs] = mnew;
+        if (__ballot(alpha != 1.f)) {  // some row's running max moved
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-          oacc[ds][qs][0] *= alpha;
-          oacc[ds][qs][1] *= alpha;
-          oacc[ds][qs][2] *= alpha;
-          oacc[ds][qs][3] *= alpha;
+          for (int ds = 0; ds < DS; ++ds) {
+            oacc[ds][qs][0] *= alpha;
+            oacc[ds][qs][1] *= alpha;
+            oacc[ds][qs][2] *= alpha;
+            oacc[ds][qs][3] *= alpha;
+          }
         }
       }
       // O^T += V^T P^T, two 32-key chunks; k-slot order: 4 keys of block 2c then 4 of 2c+1
@@ -231,10 +251,10 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
         for (int qs = 0; qs < QS; ++qs) {
           if constexpr (sizeof(T) == 2) {
             uint4 u;
-            u.x = (uint32_t)f2bf(s[2 * c][qs][0]) | ((uint32_t)f2bf(s[2 * c][qs][1]) << 16);
-            u.y = (uint32_t)f2bf(s[2 * c][qs][2]) | ((uint32_t)f2bf(s[2 * c][qs][3]) << 16);
-            u.z = (uint32_t)f2bf(s[2 * c + 1][qs][0]) | ((uint32_t)f2bf(s[2 * c + 1][qs][1]) << 16);
-            u.w = (uint32_t)f2bf(s[2 * c + 1][qs][2]) | ((uint32_t)f2bf(s[2 * c + 1][qs][3]) << 16);
+            u.x = pack_bf16x2(s[2 * c][qs][0], s[2 * c][qs][1]);
+            u.y = pack_bf16x2(s[2 * c][qs][2], s[2 * c][qs][3]);
+            u.z = pack_bf16x2(s[2 * c + 1][qs][0], s[2 * c + 1][qs][1]);
+            u.w = pack_bf16x2(s[2 * c + 1][qs][2], s[2 * c + 1][qs][3]);
             pf[qs].v[0] = u;
           } else {
             pf[qs].v[0] = make_uint4(__float_as_uint(s[2 * c][qs][0]), __float_as_uint(s[2 * c][qs][1]),

@@ -19,6 +19,15 @@ RDT_DEV bf16_t f2bf(float f) {
   return (bf16_t)(u >> 16);
 }
 
+// Two floats -> packed bfloat16 pair (low half = a) with the hardware
+// conversion (round to nearest even, the same rounding as f2bf).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+RDT_DEV uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 template <typename T> struct ST;
 template <> struct ST<float> {
   static constexpr int VEC = 4;  // elements per 16-byte vector
