@@ -11,18 +11,14 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 RDT_DEV float bf2f(bf16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
 
-// float -> bfloat16, round to nearest even (NaN kept quiet)
-RDT_DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
-
-// Two floats -> packed bfloat16 pair (low half = a) with the hardware
-// conversion (round to nearest even, the same rounding as f2bf).
+// float -> bfloat16 with the hardware conversion: round to nearest even, NaN
+// kept quiet (checked on MI355X against the bit-level rounding for 4M values
+// including ties, denormals, infinities and NaNs: identical).
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+RDT_DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
+// Two floats -> packed bfloat16 pair (low half = a), one instruction.
 RDT_DEV uint32_t pack_bf16x2(float a, float b) {
   const f32x2_t v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
@@ -94,10 +90,10 @@ template <> RDT_DEV void store8<float>(float* dst, const float* v) {
 }
 template <> RDT_DEV void store8<bf16_t>(bf16_t* dst, const float* v) {
   uint4 o;
-  o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-  o.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-  o.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  o.x = pack_bf16x2(v[0], v[1]);
+  o.y = pack_bf16x2(v[2], v[3]);
+  o.z = pack_bf16x2(v[4], v[5]);
+  o.w = pack_bf16x2(v[6], v[7]);
   *reinterpret_cast<uint4*>(dst) = o;
 }
 template <typename T> RDT_DEV void load4f(const T* src, float* v);
@@ -116,7 +112,7 @@ template <> RDT_DEV void store4<float>(float* dst, const float* v) {
 }
 template <> RDT_DEV void store4<bf16_t>(bf16_t* dst, const float* v) {
   uint2 o;
-  o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  o.x = pack_bf16x2(v[0], v[1]);
+  o.y = pack_bf16x2(v[2], v[3]);
   *reinterpret_cast<uint2*>(dst) = o;
 }
