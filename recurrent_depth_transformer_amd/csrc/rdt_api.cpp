@@ -208,7 +208,9 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   const rdt_weights& w = *f.w;
   const bool act = c.act_enabled != 0;
 
-  if (f.out != f.h0) LAUNCH(RDT_STAGE_OTHER, hipMemcpyAsync(f.out, f.h0, (size_t)N * D * 4, hipMemcpyDeviceToDevice, s));
+  // T > 0: the first loop's RMSNorm kernel copies h0 into out as it reads it
+  if (f.out != f.h0 && f.T == 0)
+    LAUNCH(RDT_STAGE_OTHER, hipMemcpyAsync(f.out, f.h0, (size_t)N * D * 4, hipMemcpyDeviceToDevice, s));
   if (f.aux.h_dump) LAUNCH(RDT_STAGE_OTHER, launch_copy_f32(f.aux.h_dump, f.h0, (long long)N * D, s));
   if (f.T == 0) {
     if (f.aux.loops) LAUNCH(RDT_STAGE_OTHER, launch_fill_i32(f.aux.loops, 0, N, s));
@@ -216,7 +218,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   }
   float* cosb = at<float>(ws, P.cosb);
   float* sinb = at<float>(ws, P.sinb);
-  LAUNCH(RDT_STAGE_OTHER, launch_rope_tables(cosb, sinb, P.rope_len, P.dr, c.rope_base, s));
+  // the RoPE tables are built by the first loop's RMSNorm kernel
   int* pos_dev = f.decode ? at<int>(ws, P.pos) : nullptr;
   // loop t's cache: GQA keys then values, or MLA latents (rows b*max_seq + p)
   const size_t crow = P.mla ? (size_t)(P.kvl + P.nr) : (size_t)P.KV * P.d;  // elements per row
@@ -262,7 +264,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   float* dbuf = P.da ? at<float>(ws, P.da_buf) : nullptr;
   float* dcos = P.da ? at<float>(ws, P.da_cos) : nullptr;
   float* dsin = P.da ? at<float>(ws, P.da_sin) : nullptr;
-  if (P.da) LAUNCH(RDT_STAGE_OTHER, launch_rope_tables(dcos, dsin, f.T, P.dd, c.rope_base, s));
+
   char* o = at<char>(ws, P.o);
   char* z = at<char>(ws, P.z);
   float* abuf = at<float>(ws, P.a);
@@ -275,7 +277,8 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   int* pcap = at<int>(ws, P.pcap);
   char* hmid = at<char>(ws, P.hmid);
   char* ybuf = at<char>(ws, P.y);
-  LAUNCH(RDT_STAGE_OTHER, launch_fill_i32(cnt2, 0, E, s));   // loop 0's counts; the combine clears the next
+  // loop 0's expert counts are cleared by the first RMSNorm kernel; each
+  // loop's combine clears the next loop's
   // down-projection tile height: large tiles when experts see many rows
   // Expert GEMM tiles (measured on MI355X): gate/up 192x128 with a two-stage
   // ring (two workgroups per CU) for every shape; down 128x128 when experts
@@ -303,6 +306,13 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       n1a.dtype = dt; n1a.h = f.out; n1a.e = f.e; n1a.a = nullptr; n1a.g = P.da ? w.g_da : w.g1;
       n1a.eps = c.norm_eps; n1a.D = D;
       n1a.rows = prev; n1a.ndev = nprev; n1a.n = N; n1a.out = P.da ? nd : n1; n1a.out_scatter = 1; n1a.dump = nullptr;
+      // per-forward set-up in the same launch: h0 -> out, RoPE tables, counts
+      n1a.h = f.h0;
+      n1a.h_copy = f.out != f.h0 ? f.out : nullptr;
+      n1a.rope_cos[0] = cosb; n1a.rope_sin[0] = sinb; n1a.rope_S[0] = P.rope_len; n1a.rope_dr[0] = P.dr;
+      if (P.da) { n1a.rope_cos[1] = dcos; n1a.rope_sin[1] = dsin; n1a.rope_S[1] = f.T; n1a.rope_dr[1] = P.dd; }
+      n1a.rope_base = c.rope_base;
+      n1a.zero = cnt2; n1a.zero_n = E;
       LAUNCH(RDT_STAGE_NORM1, launch_norm(n1a, s));
     }
     if (P.da) {

@@ -117,6 +117,12 @@ struct NormArgs {
   const int* rows; const int* ndev; int n;
   void* out; int out_scatter;
   void* dump;            // optional copy of the output scattered by token
+  // first-loop extras, all optional: write the h rows read to h_copy (the
+  // forward's output buffer), fill up to two RoPE tables (positions 0..S-1,
+  // rotary width dr) from extra workgroups, clear zero[0..zero_n)
+  float* h_copy;
+  float* rope_cos[2]; float* rope_sin[2]; int rope_S[2], rope_dr[2]; float rope_base;
+  int* zero; int zero_n;
 };
 hipError_t launch_norm(const NormArgs& a, hipStream_t s);
 

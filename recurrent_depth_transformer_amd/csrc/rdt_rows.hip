@@ -13,9 +13,40 @@ constexpr int MAXV = 16;  // float4 vectors per lane: rows up to 4096 wide
 
 // ------------------------------------------------------------------ RMSNorm
 // x = h[tok] + e[tok] (+ a[i]); out = x / sqrt(mean(x^2) + eps) * g
+// angle table entry g of cos/sin (position g / (dr/2), frequency g % (dr/2)):
+// the angle and its reduction to [-pi, pi] in double precision, the cosine and
+// sine of the remainder in single precision
+__device__ __forceinline__ void rope_entry(float* cosb, float* sinb, int dr, float base, int g) {
+  const int half = dr >> 1;
+  const int s = g / half, i = g % half;
+  const double inv = exp2(-2.0 * (double)i / (double)dr * log2((double)base));
+  const double ang = (double)s * inv;
+  const double r = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+  float sn, cs;
+  sincosf((float)r, &sn, &cs);
+  cosb[g] = cs;
+  sinb[g] = sn;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row_blocks = (a.n + 3) / 4;
+  if ((int)blockIdx.x >= row_blocks) {            // first-loop extras: RoPE tables
+    int g = ((int)blockIdx.x - row_blocks) * 256 + threadIdx.x;
+    for (int j = 0; j < 2; ++j) {
+      if (!a.rope_cos[j]) continue;
+      const int tot = a.rope_S[j] * (a.rope_dr[j] >> 1);
+      if (g < tot) {
+        rope_entry(a.rope_cos[j], a.rope_sin[j], a.rope_dr[j], a.rope_base, g);
+        return;
+      }
+      g -= tot;
+    }
+    return;
+  }
+  if (blockIdx.x == 0 && a.zero)
+    for (int z = threadIdx.x; z < a.zero_n; z += 256) a.zero[z] = 0;
   const int i = blockIdx.x * 4 + wave;
   const int n = a.ndev ? *a.ndev : a.n;
   if (i >= n) return;
@@ -28,6 +59,7 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
     const int col = (c * 64 + lane) * 4;
     if (col < D) {
       const float4 hv = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + col);
+      if (a.h_copy) *reinterpret_cast<float4*>(a.h_copy + (long long)tok * D + col) = hv;
       const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
       x[c][0] = hv.x + ev.x; x[c][1] = hv.y + ev.y; x[c][2] = hv.z + ev.z; x[c][3] = hv.w + ev.w;
       if (a.a) {
@@ -56,7 +88,10 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
 
 hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
-  dim3 grid((a.n + 3) / 4);
+  long long extra = 0;
+  for (int j = 0; j < 2; ++j)
+    if (a.rope_cos[j]) extra += (long long)a.rope_S[j] * (a.rope_dr[j] / 2);
+  dim3 grid((unsigned)((a.n + 3) / 4 + (extra + 255) / 256));
   if (a.dtype == DT_F32) hipLaunchKernelGGL(k_norm<float>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_norm<bf16_t>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
