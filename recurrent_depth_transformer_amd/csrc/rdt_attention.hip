@@ -4,13 +4,17 @@
 // read the same kv head, and 4/NHB consecutive slices of QW query rows (rows of
 // the compacted active list when ACT is on). Wave w handles head w % NHB and
 // slice w / NHB. Key/value tiles of 64 positions are shared by all four waves:
-// they are double-buffered in LDS and the next tile's global loads are in
-// flight while the current tile is multiplied.
+// they are double-buffered in LDS, and the global loads of the next tile (of
+// the next two, in two register sets, for 16-row slices) are in flight while
+// the current tile is multiplied.
+// Workgroups are numbered longest query tile first over the whole grid.
 //
 // The scores are formed transposed, S^T = K Q^T, so that a lane holds four
 // consecutive keys of one query: that is exactly the k-slot layout the second
 // MFMA needs for P, so O^T = V^T P^T is accumulated without moving P through
-// LDS. V is written to LDS transposed (Vt[d][key]) for the same reason.
+// LDS. V is written to LDS transposed (Vt[d][key]) for the same reason; in
+// bf16 the 4-key groups of each row are permuted (vswz) against LDS bank
+// conflicts of the transposing stores.
 //
 // Multi-latent attention in absorbed form is the same computation with one kv
 // head whose key is [c_kv | k_rope] and whose value is the c_kv prefix of the
@@ -22,6 +26,13 @@ namespace rdt {
 
 constexpr int KT = 64;  // keys per tile
 
+// slot of the 4-key group g in row d of the transposed bf16 V tile: g ^ vswz(d).
+// With rows padded to 68 keys, the 16-row fragment reads are conflict-free
+// and the transposing stores (8 rows 8 apart per pass) at most 2-way; vswz is
+// constant over each 16-row block, so every address stays a base plus an
+// immediate offset.
+__device__ __forceinline__ int vswz(int d) { return (d >> 4) & 3; }
+
 template <typename T, int DQK, int DV, int QW, int NHB>
 __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   constexpr int DQKP = (DQK + 31) / 32 * 32;
@@ -30,7 +41,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   constexpr int DS = DV / 16;
   constexpr int VEC = ST<T>::VEC;
   constexpr int KLD = DQKP + VEC;
-  constexpr int VLD = KT + (sizeof(T) == 2 ? 8 : 4);
+  constexpr int VLD = KT + 4;
   constexpr int SLICES = 4 / NHB;
   constexpr int BQ = QW * SLICES;  // query rows per workgroup (per head)
   // per-thread share of one K tile and one V tile (256 threads)
@@ -43,9 +54,13 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lg = lane >> 4, lc = lane & 15;
-  const int b = blockIdx.y;
-  const int qt = gridDim.x - 1 - blockIdx.x;  // long (late) query tiles first
-  const int h = blockIdx.z * NHB + (wave % NHB);
+  // linear workgroup id -> (query tile, sequence, head group), late query
+  // tiles (the most keys) first
+  const int nhg = a.H / NHB;
+  const int bz = a.B * nhg;
+  const int qt = (int)(gridDim.x / bz) - 1 - (int)(blockIdx.x / bz);
+  const int b = (blockIdx.x % bz) / nhg;
+  const int h = (blockIdx.x % nhg) * NHB + (wave % NHB);
   const int slice = wave / NHB;
   const int kvh = (h * a.KV) / a.H;
   const int S = a.S;
@@ -105,9 +120,13 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) qlo = min(qlo, __shfl_xor(qlo, o, 64));
 
-  // ---- K/V tile: global -> registers -> LDS (V transposed)
-  uint4 rk[KL], rv0[VL], rv1[VL];
-  auto gload = [&](int k0) {
+  // ---- K/V tile: global -> registers -> LDS (V transposed); two register
+  // sets so that two tiles can be in flight
+  typedef uint4 RK[KL];
+  typedef uint4 RV[VL];
+  RK rk0, rk1;
+  RV rv00, rv10, rv01, rv11;
+  auto gload = [&](int k0, RK& rk, RV& rv0, RV& rv1) {
 #pragma unroll
     for (int u = 0; u < KL; ++u) {
       const int v = tid + u * 256;
@@ -135,7 +154,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
       }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, const RK& rk, const RV& rv0, const RV& rv1) {
 #pragma unroll
     for (int u = 0; u < KL; ++u) {
       const int v = tid + u * 256;
@@ -149,6 +168,8 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
       const int v = tid + u * 256;
       if (v >= VV) continue;
       if constexpr (sizeof(T) == 2) {
+        // keys 2kp, 2kp+1 of rows dc..dc+7: one dword per row, at 4-key
+        // group kp/2 (slot (kp/2) ^ vswz(row)), half kp%2
         const int kp = v / (DV / 8), dc = (v % (DV / 8)) * 8;
         const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&rv0[u]);
         const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&rv1[u]);
@@ -156,8 +177,9 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
         for (int x = 0; x < 4; ++x) {
           const uint32_t lo = (p0[x] & 0xffffu) | (p1[x] << 16);
           const uint32_t hi = (p0[x] >> 16) | (p1[x] & 0xffff0000u);
-          *reinterpret_cast<uint32_t*>(&Vt[buf][(dc + 2 * x) * VLD + 2 * kp]) = lo;
-          *reinterpret_cast<uint32_t*>(&Vt[buf][(dc + 2 * x + 1) * VLD + 2 * kp]) = hi;
+          const int d0 = dc + 2 * x, d1 = d0 + 1;
+          *reinterpret_cast<uint32_t*>(&Vt[buf][d0 * VLD + (((kp >> 1) ^ vswz(d0)) << 2) + ((kp & 1) << 1)]) = lo;
+          *reinterpret_cast<uint32_t*>(&Vt[buf][d1 * VLD + (((kp >> 1) ^ vswz(d1)) << 2) + ((kp & 1) << 1)]) = hi;
         }
       } else {
         const int kr = v / (DV / 4), dc = (v % (DV / 4)) * 4;
@@ -168,13 +190,8 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     }
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
+  auto tile = [&](int kt, int buf) {
     const int k0 = kt * KT;
-    if (kt + 1 < nkt) gload(k0 + KT);  // next tile in flight during this one
     if (nq > 0) {
       const T* Kb = Ks[buf];
       const T* Vb = Vt[buf];
@@ -266,13 +283,17 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
         }
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-          const T* vrow = Vb + (ds * 16 + lc) * VLD + 32 * c + lg * 4;
+          const int vr = ds * 16 + lc;
+          const T* vrow = Vb + vr * VLD;
           Frag<T> vf;
           if constexpr (sizeof(T) == 2) {
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+            // keys 32c + 4lg.. (group 8c + lg) and 32c + 16 + 4lg.. (group 8c + 4 + lg)
+            const int sw = vswz(vr);
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((8 * c + lg) ^ sw) << 2));
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((8 * c + 4 + lg) ^ sw) << 2));
             vf.v[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
           } else {
+            vrow += 32 * c + lg * 4;
             vf.v[0] = *reinterpret_cast<const uint4*>(vrow);
             vf.v[sizeof(T) / 2 - 1] = *reinterpret_cast<const uint4*>(vrow + 16);
           }
@@ -281,8 +302,39 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
         }
       }
     }
-    if (kt + 1 < nkt) sstore(buf ^ 1);  // the other buffer was last read before the previous barrier
+  };
+  if constexpr (QW == 16) {
+    // tile kt sits in LDS buffer kt & 1; register set (kt & 1) receives tile
+    // kt + 2 while tile kt is multiplied, and tile kt + 1 (in the other set,
+    // loaded one tile earlier) is written to the other LDS buffer afterwards
+    gload(0, rk0, rv00, rv10);
+    if (nkt > 1) gload(KT, rk1, rv01, rv11);
+    sstore(0, rk0, rv00, rv10);
     __syncthreads();
+    for (int kt = 0; kt < nkt; kt += 2) {
+      if (kt + 2 < nkt) gload((kt + 2) * KT, rk0, rv00, rv10);
+      tile(kt, 0);
+      if (kt + 1 < nkt) sstore(1, rk1, rv01, rv11);
+      __syncthreads();
+      if (kt + 1 >= nkt) break;
+      if (kt + 3 < nkt) gload((kt + 3) * KT, rk1, rv01, rv11);
+      tile(kt + 1, 1);
+      if (kt + 2 < nkt) sstore(0, rk0, rv00, rv10);
+      __syncthreads();
+    }
+  } else {
+    // wide query slices keep one tile in flight (fewer registers, more
+    // workgroups per CU)
+    gload(0, rk0, rv00, rv10);
+    sstore(0, rk0, rv00, rv10);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nkt) gload((kt + 1) * KT, rk0, rv00, rv10);
+      tile(kt, buf);
+      if (kt + 1 < nkt) sstore(buf ^ 1, rk0, rv00, rv10);
+      __syncthreads();
+    }
   }
 
   T* O = reinterpret_cast<T*>(a.o);
@@ -304,7 +356,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 template <typename T, int DQK, int DV, int QW, int NHB>
 static hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
   constexpr int BQ = QW * (4 / NHB);
-  dim3 grid(a.dec ? 1 : (a.S + BQ - 1) / BQ, a.B, a.H / NHB);
+  dim3 grid((a.dec ? 1 : (a.S + BQ - 1) / BQ) * a.B * (a.H / NHB));
   hipLaunchKernelGGL((k_attention<T, DQK, DV, QW, NHB>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
-// Bandwidth-bound row kernels of the recurrent block: the two RMSNorms, the MoE
-// combine fused with the LTI injection and ACT halting, the stable expert
-// permutation, the active-list compaction, and small utilities.
+// Bandwidth-bound row kernels of the recurrent block: the two RMSNorms (the
+// second fused with the router and the expert slot assignment), the MoE
+// combine fused with the LTI injection and ACT halting, depth attention, the
+// active-list compaction, and small utilities.
 //
 // Row kernels give one wave64 to one token row; each lane moves 16-byte
 // vectors, so a row of D floats is read in D/256 fully coalesced passes.
@@ -231,7 +232,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
 }
 
 
-// ----------------------------------------- second RMSNorm + router + permute
+// ----------------------------------------- second RMSNorm + router + slots
 // A workgroup of 16 waves takes 16 compacted rows. Each wave forms one row
 // x = h + e + a, n2 = RMSNorm(x) * g2 (stored in the storage type, and staged
 // in LDS in column chunks). The router logits n2 . Wr^T of the 16 rows come
