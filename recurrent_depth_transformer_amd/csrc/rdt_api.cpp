@@ -200,6 +200,22 @@ static void pick_tile(long long M, long long N, int min_bn, int* bm, int* bn) {
   *bn = 64;
 }
 
+// bf16 128x192 tiles where 128x128 ones would need a second round of
+// workgroups (two per CU) that costs more than the wider tiles of one round;
+// every RoPE head has to lie inside one tile.
+static void widen_tile(DenseGemm& g) {
+  if (g.dtype != DT_BF16 || g.bm != 128 || g.bn != 128 || g.batch > 1 || g.A2 || g.epi != EPI_STORE) return;
+  long long ncols = 0;
+  for (int i = 0; i < g.nseg; ++i) {
+    if (g.seg[i].rope && (ncols % g.rope_dim || 192 % g.rope_dim)) return;
+    ncols += g.seg[i].ncols;
+  }
+  const long long slots = 512, mt = (g.M + 127) / 128;
+  const long long r128 = (mt * ((ncols + 127) / 128) + slots - 1) / slots;
+  const long long r192 = (mt * ((ncols + 191) / 192) + slots - 1) / slots;
+  if (3 * r192 < 2 * r128) g.bn = 192;
+}
+
 static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   const rdt_config& c = *f.c;
   const Plan& P = f.P;
@@ -331,6 +347,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g.cosb = dcos; g.sinb = dsin; g.rope_dim = P.dd; g.seq = 1;
       g.drope = 1; g.dpos0 = t; g.dpos1 = f.T - 1 - t;
       pick_tile(N, qw + 2 * kw, P.dd, &g.bm, &g.bn);
+      widen_tile(g);
       LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g, s));
       DepthAttnArgs da{};
       da.dtype = dt; da.q = dq; da.k = dk; da.v = dvb; da.o = dout; da.lstride = (long long)lpl;
@@ -366,6 +383,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
         g.rows = nullptr; g.gather = 0; g.Mdev = nullptr;
         g.nseg = 3; g.seg[0] = sq; g.seg[1] = sk; g.seg[2] = sv;
         pick_tile(N, Hd + 2 * KVd, P.d, &g.bm, &g.bn);
+        widen_tile(g);
         LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g, s));
       } else {
         DenseGemm gq = g;

@@ -506,6 +506,8 @@ static hipError_t dense_ns(const DenseGemm& g, hipStream_t s) {
 
 template <typename T>
 static hipError_t dense_dispatch(const DenseGemm& g, hipStream_t s) {
+  if constexpr (sizeof(T) == 2)
+    if (g.bm == 128 && g.bn == 192) return dense_ns<T, 128, 192>(g, s);
   if (g.bm == 64 && g.bn == 64) return dense_ns<T, 64, 64>(g, s);
   if (g.bm == 64 && g.bn == 128) return dense_ns<T, 64, 128>(g, s);
   if (g.bm == 128 && g.bn == 64) return dense_ns<T, 128, 64>(g, s);
