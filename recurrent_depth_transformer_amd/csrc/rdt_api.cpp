@@ -375,6 +375,12 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       GemmSeg sq{w.Wq, Hd, q, Hd, act ? 0 : 1, 1, 0};
       GemmSeg sk{w.Wk, KVd, kb, KVd, 1, 1, 0};
       GemmSeg sv{w.Wv, KVd, vb, KVd, 1, 0, 0};
+      // one-token decode without ACT: k and v go straight into the cache rows
+      const bool direct = f.decode && !act;
+      if (direct) {
+        sk.C = cache_at(t, 0); sk.row_mul = f.max_seq;
+        sv.C = cache_at(t, 1); sv.row_mul = f.max_seq;
+      }
       DenseGemm g{};
       g.dtype = dt; g.A = n1; g.lda = D; g.K = D; g.batch = 1;
       g.cosb = cosb; g.sinb = sinb; g.rope_dim = P.d; g.seq = P.S; g.epi = EPI_STORE; g.pos_dev = pos_dev;
@@ -395,7 +401,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
         pick_tile(N, 2 * KVd, P.d, &gkv.bm, &gkv.bn);
         LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(gkv, s));
       }
-      if (f.cache) {
+      if (f.cache && !direct) {
         LAUNCH(RDT_STAGE_QKV, append(t, 0, kb));
         LAUNCH(RDT_STAGE_QKV, append(t, 1, vb));
       }

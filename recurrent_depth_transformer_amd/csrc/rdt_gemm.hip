@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
         const GemmSeg& sg = g.seg[s];
         const int lc = gc - base;
         const int tok = g.rows ? g.rows[row] : row;
-        const int orow = sg.scatter ? tok : row;
+        const long long orow = sg.row_mul ? (long long)tok * sg.row_mul + *g.pos_dev : (sg.scatter ? tok : row);
         const float* crow = Cs + r * S::EPI_LD;
         float v[8];
 #pragma unroll

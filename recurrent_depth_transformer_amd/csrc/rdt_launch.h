@@ -30,6 +30,8 @@ struct GemmSeg {
   int scatter;     // 1: destination row = token id of row i; 0: row i
   int rope;        // apply half-split RoPE per head of width rope_dim
   int out_f32;     // write float instead of the storage type
+  int row_mul;     // nonzero: destination row = token id * row_mul + *pos_dev
+                   // (one-token decode writing straight into a per-loop cache)
 };
 
 enum { EPI_STORE = 0, EPI_ROUTER = 1 };
