@@ -295,15 +295,20 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   char* ybuf = at<char>(ws, P.y);
   // loop 0's expert counts are cleared by the first RMSNorm kernel; each
   // loop's combine clears the next loop's
-  // down-projection tile height: large tiles when experts see many rows
   // Expert GEMM tiles (measured on MI355X): gate/up 192x128 with a two-stage
-  // ring (two workgroups per CU) for every shape; down 128x128 when experts
-  // see many rows, else 64x64 with a three-stage ring.
+  // ring (two workgroups per CU), or 64x128 with a three-stage ring when
+  // experts see under 64 rows (decode); down 128x128 when experts see many
+  // rows, else 64x64 with a three-stage ring.
   const long long rows_per_expert = (long long)N * k / E;
   const bool bf = dt == DT_BF16;
-  const int gu_bm = bf ? 192 : GU_BM;
+  const int gu_bm = bf ? (rows_per_expert < 64 ? 64 : 192) : GU_BM;
   const int gu_bn = GU_BN;
   const int dn_bm = (rows_per_expert >= 256 && bf) ? 128 : 64;
+  // grid bound of a grouped GEMM with bm-row tiles: sum_e ceil(c_e / bm) over
+  // the routed experts is at most N*k/bm + E; each shared expert adds ceil(N/bm)
+  auto max_mtiles = [&](int bm) {
+    return (int)((long long)N * k / bm + E + (long long)P.Se * ((N + bm - 1) / bm));
+  };
 
   for (int t = 0; t < f.T; ++t) {
     const int* cur = act ? lists + (size_t)t * N : nullptr;
@@ -530,17 +535,18 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     gu.dtype = dt; gu.kind = 0; gu.A = n2; gu.lda = D;
     gu.cnt = cnt; gu.pcap = pcap; gu.cap = N; gu.ndev = ncur; gu.n_static = N;
     gu.E = E; gu.Se = P.Se; gu.k = k; gu.W1 = w.Wg; gu.W2 = w.Wu; gu.S1 = w.Wsg; gu.S2 = w.Wsu;
-    gu.N = P.F; gu.K = D; gu.C = hmid; gu.ldc = P.F; gu.max_mtiles = P.gu_max_mtiles;
-    gu.bm = gu_bm; gu.bn = gu_bn; gu.ns = 2;
+    gu.N = P.F; gu.K = D; gu.C = hmid; gu.ldc = P.F;
+    gu.bm = gu_bm; gu.bn = gu_bn; gu.ns = gu_bm == 64 ? 3 : 2; gu.max_mtiles = max_mtiles(gu.bm);
     LAUNCH(RDT_STAGE_EXPERT_GU, launch_grouped_gemm(gu, s));
     GroupedGemm gd{};
     gd.dtype = dt; gd.kind = 1; gd.A = hmid; gd.lda = P.F;
     gd.cnt = cnt; gd.pcap = pcap; gd.cap = N; gd.ndev = ncur; gd.n_static = N;
     gd.E = E; gd.Se = P.Se; gd.k = k; gd.W1 = w.Wd; gd.W2 = nullptr; gd.S1 = w.Wsd; gd.S2 = nullptr;
-    gd.N = D; gd.K = P.F; gd.C = ybuf; gd.ldc = D; gd.max_mtiles = P.dn_max_mtiles;
+    gd.N = D; gd.K = P.F; gd.C = ybuf; gd.ldc = D;
     // many rows per expert: large tiles; few rows: small tiles, deeper ring
     if (dn_bm == 128) { gd.bm = 128; gd.bn = 128; gd.ns = 2; }
     else { gd.bm = 64; gd.bn = 64; gd.ns = 3; }
+    gd.max_mtiles = max_mtiles(gd.bm);
     LAUNCH(RDT_STAGE_EXPERT_DOWN, launch_grouped_gemm(gd, s));
 
     // a8: combine + LTI injection (+ ACT)

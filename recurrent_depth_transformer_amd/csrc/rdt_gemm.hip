@@ -500,7 +500,8 @@ static hipError_t dense_ns(const DenseGemm& g, hipStream_t s) {
   switch (g.ns) {
     case 3: return dense_launch<T, BM, BN, 3>(g, s);
     case 4: return dense_launch<T, BM, BN, 4>(g, s);
-    default: return dense_launch<T, BM, BN, 2>(g, s);
+    // a few rows (one-token decode): a four-stage ring, the grid is small
+    default: return g.M <= 64 ? dense_launch<T, BM, BN, 4>(g, s) : dense_launch<T, BM, BN, 2>(g, s);
   }
 }
 
@@ -668,7 +669,7 @@ static hipError_t grouped_dispatch(const GroupedGemm& g, hipStream_t s) {
   } else {
 #define RDT_G(K, BM, BN, NS) \
     if (g.kind == K && g.bm == BM && g.bn == BN && g.ns == NS) return grouped_launch<T, BM, BN, K, NS>(g, s);
-    RDT_G(0, 128, 128, 2) RDT_G(0, 192, 128, 2)
+    RDT_G(0, 64, 128, 3) RDT_G(0, 128, 128, 2) RDT_G(0, 192, 128, 2)
     RDT_G(1, 64, 64, 3) RDT_G(1, 64, 64, 4) RDT_G(1, 128, 128, 2)
 #undef RDT_G
     return hipErrorInvalidValue;

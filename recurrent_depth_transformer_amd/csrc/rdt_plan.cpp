@@ -8,8 +8,6 @@ namespace rdt {
 // Smallest tile heights the grouped expert GEMMs use (kept in step with the
 // host orchestration; this file does not include the HIP headers). Taller
 // tiles need fewer tiles, so these bound the grid from above.
-static constexpr int kGuBM = 128;  // gate/up
-static constexpr int kDnBM = 64;   // down projection
 
 static rdt_status fail(std::string* why, rdt_status st, const char* msg) {
   if (why) *why = msg;
@@ -90,8 +88,6 @@ Plan make_plan(const rdt_config& c, int T) {
     p.dq = p.d; p.dv = p.d; p.hv = p.H * p.d; p.dr = p.d;
   }
   const size_t N = p.N, D = p.D, e = p.elt;
-  p.gu_max_mtiles = (int)((N * p.k) / kGuBM + p.E + p.Se * ((N + kGuBM - 1) / kGuBM));
-  p.dn_max_mtiles = (int)((N * p.k) / kDnBM + p.E + p.Se * ((N + kDnBM - 1) / kDnBM));
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
   p.cosb = take((size_t)p.S * (p.dr / 2) * 4);

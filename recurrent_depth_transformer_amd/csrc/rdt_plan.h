@@ -18,7 +18,6 @@ struct Plan {
   int hv;                   // width of the concatenated attention output
   int dr;                   // rope width
   int elt;                  // bytes per stored element (2 or 4)
-  int gu_max_mtiles, dn_max_mtiles;
   // workspace byte offsets
   size_t cosb, sinb, n1, q, k_, v_, o, z, a, n2;
   size_t cq_raw, lat_raw, cqn, latent, qfull, qattn, olat, wukT;
