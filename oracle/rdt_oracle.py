@@ -460,6 +460,64 @@ def step_rows(cfg, W, h, e, t, rows, forced_idx_rows, tables=None):
     return h_new, a, n2
 
 
+def step_rows_depth(cfg, W, h_hist, e, t, T, rows, forced_idx_rows, tables=None):
+    """step_rows for the Dreamer block with depth attention (GQA sequence
+    attention; sequential or parallel sublayers; optional max-score shared
+    expert), same definitions as block_step. h_hist[tau] is the state of every
+    token at the start of loop tau for tau = 0..t: depth attention at loop t
+    needs a token's own states of loops 0..t, and sequence attention needs the
+    keys and values of every token of the sampled rows' sequences, so depth
+    attention runs on those sequences only. Returns (h_new_rows, d_rows,
+    a_rows, n2_rows) for loop t."""
+    if not cfg.get("da_heads", 0) or cfg["attn"] != "gqa":
+        raise NotImplementedError("step_rows_depth covers depth attention with GQA sequence attention")
+    e = np.asarray(e, F64)
+    rows = np.asarray(rows)
+    S, eps = cfg["seq"], cfg["norm_eps"]
+    par = bool(cfg.get("parallel", 0))
+    if tables is None:
+        tables = rope_tables(S, cfg["head_dim"], cfg["rope_base"])
+    cos, sin = tables
+    seqs = np.unique(rows // S)
+    R = (seqs[:, None] * S + np.arange(S)[None, :]).reshape(-1)   # tokens of those sequences
+    where = {int(n): i for i, n in enumerate(R)}
+    hist = {"k": [], "v": []}
+    for tau in range(t + 1):
+        u_tau = np.asarray(h_hist[tau], F64)[R] + e[R]
+        d = depth_attention(cfg, W, rmsnorm(u_tau, W["g_da"], eps), tau, T, hist)
+    h = np.asarray(h_hist[t], F64)
+    u = h[R] + e[R]
+    u1 = u if par else u + d
+    n1 = rmsnorm(u1, W["g1"], eps)
+    H, KV, dh = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    pos = R % S
+    k = apply_rope((n1 @ W["Wk"].astype(F64).T).reshape(R.size, KV, dh), pos, cos, sin)
+    v = (n1 @ W["Wv"].astype(F64).T).reshape(R.size, KV, dh)
+    loc = np.array([where[int(n)] for n in rows])
+    q = apply_rope((n1[loc] @ W["Wq"].astype(F64).T).reshape(rows.size, H, dh), pos[loc], cos, sin)
+    o = np.empty((rows.size, H * dh))
+    for r, n in enumerate(rows):
+        i0 = loc[r] - (int(n) % S)                # the sequence's first token in R
+        for i in range(H):
+            j = (i * KV) // H
+            sc = (k[i0:loc[r] + 1, j] @ q[r, i]) / np.sqrt(dh)
+            o[r, i * dh:(i + 1) * dh] = softmax(sc) @ v[i0:loc[r] + 1, j]
+    a = o @ W["Wo"].astype(F64).T
+    if cfg["lora_rank"]:
+        tl = min(t, cfg["n_lora"] - 1)
+        a = a + (o @ W["lora_down"][tl].astype(F64).T) @ W["lora_up"][tl].astype(F64).T
+    x = u[loc] if par else u1[loc] + a
+    n2 = rmsnorm(x, W["g2"], eps)
+    idx = np.asarray(forced_idx_rows, np.int64)
+    p = softmax(n2 @ W["Wr"].astype(F64).T, axis=1)
+    gates = p[np.arange(rows.size)[:, None], idx]
+    sw = p.max(axis=1) if cfg.get("shared_scale", 0) else None
+    m = moe(n2, idx, gates, W, cfg["n_shared_experts"], sw)
+    d_rows = d[loc]
+    h_new = np.asarray(W["A"], F64) * h[rows] + np.asarray(W["B"], F64) * e[rows] + d_rows + a + m
+    return h_new, d_rows, a, n2
+
+
 # ----------------------------------------------------------------------------
 # between forwards: router-bias balancing and expert depth usage
 # ----------------------------------------------------------------------------

@@ -69,6 +69,31 @@ def test_fullsize(name):
         assert err <= TOL * rms(ref["h"])
 
 
+def test_fullsize_dreamer():
+    """The Dreamer workload at the size bench.py times: routing of every row
+    teacher-forced each loop, and on sampled rows of the first sequence the
+    loop update from the GPU's own states (depth attention over the token's
+    loops 0..t, sequence attention over its sequence)."""
+    cfg = get_config("dreamer")
+    T, S = cfg["T"], cfg["seq"]
+    print("[fullsize] dreamer: running the GPU forward with dumps", flush=True)
+    res, inp, *_ = run_gpu(cfg, T=T)
+    assert np.all(np.isfinite(res["h"]))
+    mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro)
+    print(f"[fullsize] dreamer: routing mismatches={mism} near_ties={near} compared={comp}", flush=True)
+    assert mism == 0
+    rng = np.random.default_rng(321)
+    tables = ro.rope_tables(S, cfg["head_dim"], cfg["rope_base"])
+    rows = np.unique(np.concatenate([rng.choice(S, size=40, replace=False), [S - 1]]))
+    for t in _loops_to_check(T):
+        hn, d, a, _ = ro.step_rows_depth(cfg, inp, res["h_dump"][:t + 1], inp["e"], t, T, rows,
+                                         res["route_idx"][t][rows], tables=tables)
+        err = np.max(np.abs(res["h_dump"][t + 1][rows] - hn))
+        scale = rms(res["h_dump"][t + 1])
+        print(f"[fullsize] dreamer loop {t}: rows={rows.size} max|dh|/rms={err / scale:.3e}", flush=True)
+        assert err <= TOL * scale
+
+
 @pytest.mark.parametrize("name", ["gqa", "mla", "dreamer"])
 def test_fullsize_decode_last_position_matches_forward(name):
     """At the sizes bench.py times: prefill seq-1 positions, decode the last

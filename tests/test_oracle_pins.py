@@ -490,6 +490,24 @@ def test_step_rows_matches_block_step(name):
     np.testing.assert_allclose(hn, ref, rtol=1e-11, atol=1e-12)
 
 
+@pytest.mark.parametrize("name", ["dreamer_tiny", "dreamer_small"])
+@pytest.mark.parametrize("par", [0, 1])
+def test_step_rows_depth_matches_forward(name, par):
+    """The per-row Dreamer loop update equals the full forward's loop update
+    (block_step with depth attention) on the same states."""
+    cfg, W = _tiny(name)
+    cfg["parallel"] = par
+    T = 3
+    N = cfg["batch"] * cfg["seq"]
+    rec = ro.forward(cfg, W, T=T, record=True)
+    S = cfg["seq"]
+    rows = np.unique(np.minimum([0, 3, S - 1, N - 1, S + 2], N - 1))
+    for t in (0, T - 1):
+        hn, d, a, n2 = ro.step_rows_depth(cfg, W, rec["h"][:t + 1], W["e"], t, T, rows, rec["idx"][t][rows])
+        np.testing.assert_allclose(n2, rec["n2"][t][rows], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(hn, rec["h"][t + 1][rows], rtol=1e-10, atol=1e-11)
+
+
 # ---------------------------------------------------------------------------
 # router-bias balancing and expert depth usage (between forwards)
 # ---------------------------------------------------------------------------
