@@ -84,6 +84,47 @@ def test_end_to_end_forced(name):
         assert 0 < res["loops"].min() <= res["loops"].max() <= T
 
 
+# The limits of the block: the widest row (dim 4096: 16 float4 per lane and
+# more than one router k-chunk), the most routed experts (64) with top-8, the
+# pages' maximum of 16 loops, and a ragged sequence length. In bf16 over 16
+# loops at this width the rounding of the bf16 operands compounds (each loop
+# adds 3e-3..7e-3 of RMS, measured), so the bf16 cases check every loop from
+# the GPU's own state; the fp32 case also checks the end state.
+LIMITS = {
+    "wide_max": dict(base="wide_small", dim=4096, seq=37, n_experts=64, top_k=8, expert_dim=64, T=16,
+                     n_bias_rows=16),
+    "wide_max_f32": dict(base="wide_small", dim=4096, seq=37, n_experts=64, top_k=8, expert_dim=64, T=16,
+                         n_bias_rows=16, dtype="f32"),
+    "act_max": dict(base="act_small", dim=4096, seq=37, T=16),
+    "mla_max": dict(base="mla_small", dim=4096, seq=37, T=16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LIMITS))
+def test_size_limits_forced(name):
+    over = dict(LIMITS[name])
+    cfg = get_config(over.pop("base"), **over)
+    T = cfg["T"]
+    res, inp, *_ = run_gpu(cfg, T=T)
+    mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro)
+    assert mism == 0
+    worst = 0.0
+    for t in range(T):
+        act = np.nonzero(res["loops"] > t)[0]
+        if act.size == 0:
+            break
+        hn, _, _ = ro.step_rows(cfg, inp, res["h_dump"][t], inp["e"], t, act, res["route_idx"][t][act])
+        g = res["h_dump"][t + 1][act]
+        worst = max(worst, float(np.max(np.abs(g - hn))) / rms(g))
+    _report(name, worst_loop_ratio=f"{worst:.3e}", route_mismatch=mism, near_ties=near, compared=comp)
+    assert worst <= TOL
+    if cfg["dtype"] == "f32":
+        ref = ro.forward(cfg, inp, T=T, forced_idx=res["route_idx"], forced_loops=res["loops"] if cfg["act"] else None)
+        err = np.max(np.abs(res["h"] - ref["h"]))
+        _report(name, end_ratio=f"{err / rms(ref['h']):.3e}")
+        assert err <= 1e-4 * rms(ref["h"])
+
+
 @pytest.mark.parametrize("name", ["gqa_small", "act_small", "dreamer_small"])
 def test_graph_matches_eager_bitwise(name):
     cfg = get_config(name)
