@@ -125,6 +125,48 @@ def test_size_limits_forced(name):
         assert err <= 1e-4 * rms(ref["h"])
 
 
+# Degenerate cases of the method: every expert chosen (k = E: the dense softmax
+# mixture, no next-best score), a single expert, one-token sequences (attention
+# over one key), one loop.
+DEGENERATE = {
+    "dense_mixture": dict(base="gqa_small", top_k=8),
+    "single_expert": dict(base="gqa_small", n_experts=1, top_k=1),
+    "one_token_sequences": dict(base="gqa_small", batch=5, seq=1),
+    "one_loop": dict(base="act_small", T=1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEGENERATE))
+def test_degenerate_forced(name):
+    over = dict(DEGENERATE[name])
+    cfg = get_config(over.pop("base"), **over)
+    T = cfg["T"]
+    res, inp, *_ = run_gpu(cfg, T=T)
+    mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro)
+    ref = ro.forward(cfg, inp, T=T, forced_idx=res["route_idx"], forced_loops=res["loops"] if cfg["act"] else None)
+    err = np.max(np.abs(res["h"] - ref["h"]))
+    _report(name, ratio=f"{err / rms(ref['h']):.3e}", route_mismatch=mism, near_ties=near, compared=comp)
+    assert mism == 0
+    assert err <= TOL * rms(ref["h"])
+    if cfg["top_k"] == cfg["n_experts"]:
+        assert np.all(np.isinf(res["route_gap"]))           # no expert left out: no gap
+        assert np.all(res["expert_counts"] == cfg["batch"] * cfg["seq"])
+
+
+def test_act_zero_halting_vector_halts_after_two_loops():
+    """w = 0 gives p = 1/2 every loop: the cumulative sum reaches 1.0 >= 0.99
+    at the second loop, so every token runs exactly two loops whatever T."""
+    cfg = get_config("act_small", T=6)
+    inp = make_inputs(cfg)
+    inp["w_halt"] = np.zeros_like(inp["w_halt"])
+    res, *_ = run_gpu(cfg, inp, T=6)
+    assert np.all(res["loops"] == 2)
+    np.testing.assert_array_equal(res["act_cum"][1], np.ones_like(res["act_cum"][1]))
+    ref = ro.forward(cfg, inp, T=6)
+    assert np.all(ref["loops"] == 2)
+    assert np.max(np.abs(res["h"] - ref["h"])) <= TOL * rms(ref["h"])
+
+
 @pytest.mark.parametrize("name", ["gqa_small", "act_small", "dreamer_small"])
 def test_graph_matches_eager_bitwise(name):
     cfg = get_config(name)
