@@ -543,6 +543,8 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     gd.cnt = cnt; gd.pcap = pcap; gd.cap = N; gd.ndev = ncur; gd.n_static = N;
     gd.E = E; gd.Se = P.Se; gd.k = k; gd.W1 = w.Wd; gd.W2 = nullptr; gd.S1 = w.Wsd; gd.S2 = nullptr;
     gd.N = D; gd.K = P.F; gd.C = ybuf; gd.ldc = D;
+    const long long ystride = (long long)N * (k + P.Se) * D;
+    gd.ksplit = P.ksplit; gd.part = P.ksplit > 1 ? reinterpret_cast<float*>(ybuf) : nullptr; gd.pstride = ystride;
     // many rows per expert: large tiles; few rows: small tiles, deeper ring
     if (dn_bm == 128) { gd.bm = 128; gd.bn = 128; gd.ns = 2; }
     else { gd.bm = 64; gd.bn = 64; gd.ns = 3; }
@@ -552,7 +554,8 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     // a8: combine + LTI injection (+ ACT)
     CombineArgs ca{};
     ca.dtype = dt; ca.h = f.out; ca.e = f.e; ca.a = abuf; ca.A = w.A; ca.B = w.B;
-    ca.Y = ybuf; ca.gates = gates; ca.idx = idx; ca.slot = slot; ca.cnt = cnt; ca.E = E;
+    ca.Y = ybuf; ca.ksplit = P.ksplit; ca.Yp = reinterpret_cast<const float*>(ybuf); ca.ystride = ystride;
+    ca.gates = gates; ca.idx = idx; ca.slot = slot; ca.cnt = cnt; ca.E = E;
     ca.cnt_next = cnt2 + ((t + 1) & 1) * E;
     ca.counts_dump = f.aux.expert_counts ? f.aux.expert_counts + (size_t)t * E : nullptr;
     ca.k = k; ca.Se = P.Se; ca.D = D;

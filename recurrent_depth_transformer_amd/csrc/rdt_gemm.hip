@@ -618,7 +618,19 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
     const T* bd = bp[0] ? bp[0] : reinterpret_cast<const T*>(routed ? g.W1 : g.S1);
     char* const Ls[4] = {L0, L1, L2, L3};
     char* const (&Lr)[NS] = *reinterpret_cast<char* const(*)[NS]>(Ls);
-    gemm_mainloop_ring<BM, BN, NS, false>(acc, Lr, ap, bp, g.K, ap, bp, 0, A, bd, A, bd);
+    int Kl = g.K;
+    if (KIND == 1 && gridDim.y > 1) {   // K slice blockIdx.y of gridDim.y (whole 64-wide stages)
+      const int Ks = (((g.K + 63) / 64 + (int)gridDim.y - 1) / (int)gridDim.y) * 64;
+      const int k0 = (int)blockIdx.y * Ks;
+      Kl = g.K - k0 < Ks ? g.K - k0 : Ks;
+#pragma unroll
+      for (int i = 0; i < S::A_LD; ++i)
+        if (ap[i]) ap[i] += k0;
+#pragma unroll
+      for (int i = 0; i < S::B_LD; ++i)
+        if (bp[i]) bp[i] += k0;
+    }
+    gemm_mainloop_ring<BM, BN, NS, false>(acc, Lr, ap, bp, Kl, ap, bp, 0, A, bd, A, bd);
   } else {
     gemm_mainloop<T, BM, BN, false>(acc, smem, ap, bp, g.K, ap, bp, 0);
   }
@@ -647,7 +659,10 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
 #pragma unroll
         for (int x = 0; x < 8; ++x) v[x] = crow[c8 + x];
       }
-      store8<T>(C + (long long)(pbase + m) * g.ldc + col, v);
+      if (KIND == 1 && gridDim.y > 1)
+        store8<float>(g.part + (long long)blockIdx.y * g.pstride + (long long)(pbase + m) * g.ldc + col, v);
+      else
+        store8<T>(C + (long long)(pbase + m) * g.ldc + col, v);
     }
     __syncthreads();
   }
@@ -657,7 +672,7 @@ template <typename T, int BM, int BN, int KIND, int NS>
 static hipError_t grouped_launch(const GroupedGemm& g, hipStream_t s) {
   const int outw = KIND == 0 ? BN / 2 : BN;
   const int ntn = (g.N + outw - 1) / outw;
-  dim3 grid(g.max_mtiles * ntn);
+  dim3 grid(g.max_mtiles * ntn, KIND == 1 && sizeof(T) == 2 && g.ksplit > 1 ? g.ksplit : 1);
   hipLaunchKernelGGL((k_grouped_gemm<T, BM, BN, KIND, NS>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
@@ -678,6 +693,8 @@ static hipError_t grouped_dispatch(const GroupedGemm& g, hipStream_t s) {
 
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s) {
   if (g.max_mtiles <= 0) return hipSuccess;
+  if (g.ksplit > 1 && (g.kind != 1 || g.dtype != DT_BF16 || !g.part || g.ksplit > (g.K + 63) / 64))
+    return hipErrorInvalidValue;
   return g.dtype == DT_F32 ? grouped_dispatch<float>(g, s) : grouped_dispatch<bf16_t>(g, s);
 }
 

@@ -87,6 +87,10 @@ struct GroupedGemm {
   void* C; int ldc;
   int max_mtiles;
   int bm, bn, ns;        // tile rows, columns, stages
+  // down projection only: ksplit > 1 cuts K into ksplit slices of whole
+  // 64-wide stages; slice s writes its float partial sums to
+  // part + s * pstride (row-major, ldc) instead of C
+  int ksplit; float* part; long long pstride;
 };
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s);
 
@@ -146,6 +150,9 @@ struct CombineArgs {
   const float* g1; float eps;
   const float* d;        // optional depth-attention output (row i), added to h'
   const float* smax;     // optional: shared experts weighted by smax[i] (else 1)
+  // ksplit > 1: the expert outputs are ksplit float partial sums at
+  // Yp + s * ystride (row-major, D), added in slice order; Y is unused
+  int ksplit; const float* Yp; long long ystride;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 

@@ -118,7 +118,13 @@ Plan make_plan(const rdt_config& c, int T) {
   p.slot = take(N * p.k * 4);
   p.pcap = take((size_t)p.E * N * 4);
   p.hmid = take(N * (p.k + p.Se) * p.F * e);
-  p.y = take(N * (p.k + p.Se) * D * e);
+  // The down projection's K loop (F / 64 stages per tile) is latency-bound
+  // once it is long: it is cut into slices of at most 32 stages, each written
+  // as a float partial sum that the combine adds in slice order. The count
+  // depends on the config only, so prefill, decode and the full forward sum
+  // every row the same way.
+  p.ksplit = c.dtype == RDT_BF16 ? ((p.F + 63) / 64 + 31) / 32 : 1;
+  p.y = take(N * (p.k + p.Se) * D * (p.ksplit > 1 ? 4 * (size_t)p.ksplit : e));
   const size_t Tp = (size_t)(T > 0 ? T : 0) + 1;
   p.lists = take(Tp * N * 4);
   p.ncount = take(Tp * 4);

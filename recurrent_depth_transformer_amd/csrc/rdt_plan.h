@@ -23,6 +23,8 @@ struct Plan {
   size_t cq_raw, lat_raw, cqn, latent, qfull, qattn, olat, wukT;
   size_t idx, gates, gap, cnt, slot, pcap;
   size_t hmid, y;
+  int ksplit;                // K slices of the expert down projection (y then holds
+                            // ksplit float partial sums, [ksplit][N*(k+Se)][D])
   size_t lists, ncount, seg, cum;
   size_t pos;               // decode position (one int, written before each step)
   int rope_len;             // positions in the RoPE tables

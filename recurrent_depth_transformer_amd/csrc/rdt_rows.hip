@@ -130,6 +130,20 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int tok = a.rows ? a.rows[i] : i;
   const int D = a.D, k = a.k;
   const T* Y = reinterpret_cast<const T*>(a.Y);
+  // expert output row p, columns col..col+3: stored values, or the sum of the
+  // K-slice partials in slice order
+  auto yrow = [&](long long p, int col, float* y) {
+    if (a.ksplit > 1) {
+      const float4 v0 = *reinterpret_cast<const float4*>(a.Yp + p * D + col);
+      y[0] = v0.x; y[1] = v0.y; y[2] = v0.z; y[3] = v0.w;
+      for (int s = 1; s < a.ksplit; ++s) {
+        const float4 v = *reinterpret_cast<const float4*>(a.Yp + s * a.ystride + p * D + col);
+        y[0] += v.x; y[1] += v.y; y[2] += v.z; y[3] += v.w;
+      }
+    } else {
+      load4f<T>(Y + p * D + col, y);
+    }
+  };
   float m[NV][4];
 #pragma unroll
   for (int c = 0; c < NV; ++c) m[c][0] = m[c][1] = m[c][2] = m[c][3] = 0.f;
@@ -141,7 +155,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       const int col = (c * 64 + lane) * 4;
       if (col < D) {
         float y[4];
-        load4f<T>(Y + (long long)p * D + col, y);
+        yrow(p, col, y);
         m[c][0] += gt * y[0]; m[c][1] += gt * y[1]; m[c][2] += gt * y[2]; m[c][3] += gt * y[3];
       }
     }
@@ -154,7 +168,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       const int col = (c * 64 + lane) * 4;
       if (col < D) {
         float y[4];
-        load4f<T>(Y + p * D + col, y);
+        yrow(p, col, y);
         m[c][0] += sw * y[0]; m[c][1] += sw * y[1]; m[c][2] += sw * y[2]; m[c][3] += sw * y[3];
       }
     }
