@@ -236,6 +236,16 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   float* sinb = at<float>(ws, P.sinb);
   // the RoPE tables are built by the first loop's RMSNorm kernel
   int* pos_dev = f.decode ? at<int>(ws, P.pos) : nullptr;
+  // decode without ACT: the cached keys are cut into P.att_split ranges, one
+  // workgroup each, merged by a second launch
+  auto set_split = [&](AttnArgs& aa) {
+    aa.nsplit = (f.decode && !act && P.att_split > 1) ? P.att_split : 1;
+    if (aa.nsplit > 1) {
+      aa.part_o = at<float>(ws, P.att_po);
+      aa.part_m = at<float>(ws, P.att_pm);
+      aa.part_l = at<float>(ws, P.att_pl);
+    }
+  };
   // loop t's cache: GQA keys then values, or MLA latents (rows b*max_seq + p)
   const size_t crow = P.mla ? (size_t)(P.kvl + P.nr) : (size_t)P.KV * P.d;  // elements per row
   const size_t cplane = (size_t)P.B * f.max_seq * crow * elt;                 // bytes per array per loop
@@ -419,7 +429,9 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       aa.H = P.H; aa.KV = P.KV; aa.rows = cur; aa.seg = seg; aa.B = P.B;
       aa.S = f.decode ? f.max_seq : P.S; aa.dec = f.decode; aa.dec_pos = pos_dev;
       aa.scale = 1.f / sqrtf((float)P.d);
+      set_split(aa);
       LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, s));
+      if (aa.nsplit > 1) LAUNCH(RDT_STAGE_ATTN, launch_attention_merge(aa, s));
     } else {
       const int W = P.kvl + P.nr, qw = P.nope + P.nr;
       char* cq_raw = at<char>(ws, P.cq_raw);
@@ -477,7 +489,9 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       aa.H = P.H; aa.KV = 1; aa.rows = cur; aa.seg = seg; aa.B = P.B;
       aa.S = f.decode ? f.max_seq : P.S; aa.dec = f.decode; aa.dec_pos = pos_dev;
       aa.scale = 1.f / sqrtf((float)(P.nope + P.nr));
+      set_split(aa);
       LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, s));
+      if (aa.nsplit > 1) LAUNCH(RDT_STAGE_ATTN, launch_attention_merge(aa, s));
       // value up-projection per head: o[h] = o_lat[h] . Wuv[h]^T
       DenseGemm g4{};
       g4.dtype = dt; g4.A = olat; g4.lda = P.H * P.kvl; g4.a_bstride = P.kvl; g4.K = P.kvl; g4.epi = EPI_STORE;

@@ -58,7 +58,9 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   // tiles (the most keys) first
   const int nhg = a.H / NHB;
   const int bz = a.B * nhg;
-  const int qt = (int)(gridDim.x / bz) - 1 - (int)(blockIdx.x / bz);
+  const int outer = (int)(blockIdx.x / bz);
+  const bool split = a.dec && a.nsplit > 1;     // key range `outer` of a decode step
+  const int qt = a.dec ? 0 : (int)(gridDim.x / bz) - 1 - outer;
   const int b = (blockIdx.x % bz) / nhg;
   const int h = (blockIdx.x % nhg) * NHB + (wave % NHB);
   const int slice = wave / NHB;
@@ -110,7 +112,13 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     for (int ds = 0; ds < DS; ++ds) oacc[ds][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sc = a.scale * 1.4426950408889634f;  // exp2 domain
-  const int nkt = (kmax + KT - 1) / KT;
+  // key tiles [kt_begin, nkt) of this workgroup
+  int nkt = (kmax + KT - 1) / KT, kt_begin = 0;
+  if (split) {
+    const int per = (nkt + a.nsplit - 1) / a.nsplit;
+    kt_begin = min(nkt, outer * per);
+    nkt = min(nkt, kt_begin + per);
+  }
   // first query position of this wave: tiles that end at or before it need
   // no causal mask
   int qlo = 0x7fffffff;
@@ -307,11 +315,11 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     // tile kt sits in LDS buffer kt & 1; register set (kt & 1) receives tile
     // kt + 2 while tile kt is multiplied, and tile kt + 1 (in the other set,
     // loaded one tile earlier) is written to the other LDS buffer afterwards
-    gload(0, rk0, rv00, rv10);
-    if (nkt > 1) gload(KT, rk1, rv01, rv11);
-    sstore(0, rk0, rv00, rv10);
+    if (kt_begin < nkt) gload(kt_begin * KT, rk0, rv00, rv10);
+    if (kt_begin + 1 < nkt) gload((kt_begin + 1) * KT, rk1, rv01, rv11);
+    if (kt_begin < nkt) sstore(0, rk0, rv00, rv10);
     __syncthreads();
-    for (int kt = 0; kt < nkt; kt += 2) {
+    for (int kt = kt_begin; kt < nkt; kt += 2) {
       if (kt + 2 < nkt) gload((kt + 2) * KT, rk0, rv00, rv10);
       tile(kt, 0);
       if (kt + 1 < nkt) sstore(1, rk1, rv01, rv11);
@@ -325,11 +333,13 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   } else {
     // wide query slices keep one tile in flight (fewer registers, more
     // workgroups per CU)
-    gload(0, rk0, rv00, rv10);
-    sstore(0, rk0, rv00, rv10);
+    if (kt_begin < nkt) {
+      gload(kt_begin * KT, rk0, rv00, rv10);
+      sstore(0, rk0, rv00, rv10);
+    }
     __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int buf = kt & 1;
+    for (int kt = kt_begin; kt < nkt; ++kt) {
+      const int buf = (kt - kt_begin) & 1;
       if (kt + 1 < nkt) gload((kt + 1) * KT, rk0, rv00, rv10);
       tile(kt, buf);
       if (kt + 1 < nkt) sstore(buf ^ 1, rk0, rv00, rv10);
@@ -337,6 +347,23 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     }
   }
 
+  if (split) {  // partial result of this key range, unnormalised
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      const int qq = qs * 16 + lc;
+      if (qq >= nq) continue;
+      const long long pr = ((long long)outer * a.B + (qfirst + qq)) * a.H + h;
+      if (lg == 0) {
+        a.part_m[pr] = mrow[qs];
+        a.part_l[pr] = lrow[qs];
+      }
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        *reinterpret_cast<float4*>(a.part_o + pr * DV + ds * 16 + lg * 4) =
+            make_float4(oacc[ds][qs][0], oacc[ds][qs][1], oacc[ds][qs][2], oacc[ds][qs][3]);
+    }
+    return;
+  }
   T* O = reinterpret_cast<T*>(a.o);
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) {
@@ -359,7 +386,7 @@ static hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
   // ACT workloads); 64-key tiles otherwise (LDS and registers)
   constexpr int KT = (sizeof(T) == 2 && DQK <= 64) ? 128 : 64;
   constexpr int BQ = QW * (4 / NHB);
-  dim3 grid((a.dec ? 1 : (a.S + BQ - 1) / BQ) * a.B * (a.H / NHB));
+  dim3 grid((a.dec ? (a.nsplit > 1 ? a.nsplit : 1) : (a.S + BQ - 1) / BQ) * a.B * (a.H / NHB));
   hipLaunchKernelGGL((k_attention<T, DQK, DV, QW, NHB, KT>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -391,7 +418,47 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.H % a.KV) return hipErrorInvalidValue;
+  if (a.dec && a.nsplit > 1 && (!a.part_o || !a.part_m || !a.part_l || a.rows || a.seg)) return hipErrorInvalidValue;
   return a.dtype == DT_F32 ? attn_dispatch<float>(a, s) : attn_dispatch<bf16_t>(a, s);
+}
+
+// One wave per (query row i, head h); lane l owns output columns 2l, 2l+1.
+template <typename T>
+__global__ __launch_bounds__(256) void k_attention_merge(AttnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + wave;
+  if (w >= a.B * a.H) return;
+  const int i = w / a.H, h = w % a.H;
+  float M = -INFINITY;
+  for (int r = 0; r < a.nsplit; ++r) M = fmaxf(M, a.part_m[((long long)r * a.B + i) * a.H + h]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  const int d = 2 * lane;
+  for (int r = 0; r < a.nsplit; ++r) {
+    const long long pr = ((long long)r * a.B + i) * a.H + h;
+    const float m = a.part_m[pr];
+    if (m == -INFINITY) continue;                 // an empty key range
+    const float wgt = exp2f(m - M);
+    L += wgt * a.part_l[pr];
+    if (d < a.dv) {
+      o0 += wgt * a.part_o[pr * a.dv + d];
+      o1 += wgt * a.part_o[pr * a.dv + d + 1];
+    }
+  }
+  if (d < a.dv) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    T* O = reinterpret_cast<T*>(a.o) + (long long)i * a.o_ld + (long long)h * a.o_hs + d;
+    O[0] = ST<T>::from_f(o0 * inv);
+    O[1] = ST<T>::from_f(o1 * inv);
+  }
+}
+
+hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s) {
+  if (!a.dec || a.nsplit <= 1) return hipSuccess;
+  if (a.dv > 128 || a.dv % 2) return hipErrorInvalidValue;
+  dim3 grid((a.B * a.H + 3) / 4);
+  if (a.dtype == DT_F32) hipLaunchKernelGGL(k_attention_merge<float>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_attention_merge<bf16_t>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace rdt

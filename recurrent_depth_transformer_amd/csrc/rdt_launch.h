@@ -111,8 +111,16 @@ struct AttnArgs {
   // *dec_pos, its keys are rows s*S .. s*S + *dec_pos of the K/V cache (S is
   // the cache length), and sequence b of the grid is slot b
   int dec; const int* dec_pos;
+  // decode only, nsplit > 1: the keys are cut into nsplit ranges of whole
+  // tiles, one workgroup each; range r writes its unnormalised output and its
+  // running max / sum (exp2 domain) for query row i, head h to
+  // part_o[((r * nq + i) * H + h) * dv + d], part_m / part_l[(r * nq + i) * H + h]
+  // (nq = B query rows), and launch_attention_merge forms o from them
+  int nsplit; float* part_o; float* part_m; float* part_l;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// o[i, h] = sum_r 2^(m_r - M) part_o_r / sum_r 2^(m_r - M) l_r over the ranges
+hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- row kernels
 struct NormArgs {

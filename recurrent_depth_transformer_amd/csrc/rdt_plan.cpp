@@ -158,6 +158,14 @@ Plan make_decode_plan(const rdt_config& c, int T, int max_seq) {
   p.cosb = take((size_t)max_seq * (p.dr / 2) * 4);
   p.sinb = take((size_t)max_seq * (p.dr / 2) * 4);
   p.rope_len = max_seq;
+  // one workgroup per 256 cached positions (at most 16) per sequence and head group
+  p.att_split = max_seq / 256 < 1 ? 1 : (max_seq / 256 > 16 ? 16 : max_seq / 256);
+  if (p.att_split > 1) {
+    const size_t rows = (size_t)p.att_split * p.B * p.H;
+    p.att_po = take(rows * p.dv * 4);
+    p.att_pm = take(rows * 4);
+    p.att_pl = take(rows * 4);
+  }
   p.total = off;
   return p;
 }

@@ -33,6 +33,9 @@ struct Plan {
   // [T+1][N][KVd*dd], attention output, projected output (float), depth RoPE
   int da, Hd, KVd, dd;
   size_t da_nd, da_q, da_k, da_v, da_out, da_buf, da_cos, da_sin;
+  // decode attention: key ranges per step and their partial results
+  int att_split;
+  size_t att_po, att_pm, att_pl;
   size_t total;
 };
 

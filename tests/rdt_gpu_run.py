@@ -18,26 +18,35 @@ def run_gpu(cfg: dict, inputs: dict | None = None, T: int | None = None, dumps: 
     W = device_weights(inputs, cfg, "cuda") if weights is None else weights
     blk = block or RecurrentBlock(dict(cfg, max_T=max(T, cfg["T"])), graph=graph)
     N, D, k, E = n_tokens(cfg), cfg["dim"], cfg["top_k"], cfg["n_experts"]
-    aux = None
-    if dumps:
-        store = torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16
-        aux = dict(
-            loops=torch.empty(N, dtype=torch.int32, device="cuda"),
-            route_idx=torch.empty(max(T, 1), N, k, dtype=torch.int32, device="cuda"),
-            route_gap=torch.empty(max(T, 1), N, dtype=torch.float32, device="cuda"),
-            expert_counts=torch.empty(max(T, 1), E, dtype=torch.int32, device="cuda"),
-            act_cum=torch.empty(max(T, 1), N, dtype=torch.float32, device="cuda"),
-            n2_dump=torch.empty(max(T, 1), N, D, dtype=store, device="cuda"),
-            a_dump=torch.empty(max(T, 1), N, D, dtype=torch.float32, device="cuda"),
-            h_dump=torch.empty(T + 1, N, D, dtype=torch.float32, device="cuda"),
-        )
+    aux = make_aux(cfg, N, T) if dumps else None
     out = blk.forward(W["h0"], W["e"], W, T=T, aux=aux)
     torch.cuda.synchronize()
     res = dict(h=out.float().cpu().numpy())
     if dumps:
-        for k_, v in aux.items():
-            res[k_] = v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy()
+        res.update(aux_to_numpy(aux))
     return res, inputs, blk, W
+
+
+def make_aux(cfg: dict, N: int, T: int) -> dict:
+    """Device buffers for every per-loop dump of N rows."""
+    import torch
+    D, k, E = cfg["dim"], cfg["top_k"], cfg["n_experts"]
+    store = torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16
+    return dict(
+        loops=torch.empty(N, dtype=torch.int32, device="cuda"),
+        route_idx=torch.empty(max(T, 1), N, k, dtype=torch.int32, device="cuda"),
+        route_gap=torch.empty(max(T, 1), N, dtype=torch.float32, device="cuda"),
+        expert_counts=torch.empty(max(T, 1), E, dtype=torch.int32, device="cuda"),
+        act_cum=torch.empty(max(T, 1), N, dtype=torch.float32, device="cuda"),
+        n2_dump=torch.empty(max(T, 1), N, D, dtype=store, device="cuda"),
+        a_dump=torch.empty(max(T, 1), N, D, dtype=torch.float32, device="cuda"),
+        h_dump=torch.empty(T + 1, N, D, dtype=torch.float32, device="cuda"),
+    )
+
+
+def aux_to_numpy(aux: dict) -> dict:
+    import torch
+    return {k_: (v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k_, v in aux.items()}
 
 
 def rms(x):

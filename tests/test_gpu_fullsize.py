@@ -8,7 +8,7 @@ import pytest
 from oracle import rdt_oracle as ro
 from rdt_inputs import get_config
 
-from rdt_gpu_run import check_routing_teacher_forced, rms, run_gpu
+from rdt_gpu_run import aux_to_numpy, check_routing_teacher_forced, make_aux, rms, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -95,22 +95,57 @@ def test_fullsize_dreamer():
 
 
 @pytest.mark.parametrize("name", ["gqa", "mla", "dreamer"])
-def test_fullsize_decode_last_position_matches_forward(name):
-    """At the sizes bench.py times: prefill seq-1 positions, decode the last
-    one, and compare with the full-sequence forward (same kernels: equal)."""
+def test_fullsize_decode_last_position(name):
+    """At the sizes bench.py times: prefill seq-1 positions (the same kernels as
+    the full forward: equal bit for bit), then decode the last position. The
+    decode step cuts the cached keys into ranges (one workgroup each, merged
+    afterwards), so it is checked against the oracle loop by loop from the
+    GPU's own states: the cached positions' states come from the prefill dumps,
+    the new token's from the decode dumps, routing teacher-forced."""
     import torch
 
     from recurrent_depth_transformer_amd import RecurrentBlock
     cfg = get_config(name)
     B, S, D, T = cfg["batch"], cfg["seq"], cfg["dim"], cfg["T"]
-    full, _, _, W = run_gpu(cfg, dumps=False)
+    full, inp, _, W = run_gpu(cfg, dumps=False)
     blk = RecurrentBlock(dict(cfg, seq=S - 1))
     cache = blk.new_cache(T, S)
     h0, e = W["h0"].view(B, S, D), W["e"].view(B, S, D)
-    pre = blk.prefill(h0[:, :S - 1].contiguous().view(-1, D), e[:, :S - 1].contiguous().view(-1, D), W, T, cache, S)
-    last = blk.decode_step(h0[:, S - 1].contiguous(), e[:, S - 1].contiguous(), W, T, S - 1, cache, S)
+    aux_p, aux_d = make_aux(cfg, B * (S - 1), T), make_aux(cfg, B, T)
+    pre = blk.prefill(h0[:, :S - 1].contiguous().view(-1, D), e[:, :S - 1].contiguous().view(-1, D), W, T, cache, S,
+                      aux=aux_p)
+    last = blk.decode_step(h0[:, S - 1].contiguous(), e[:, S - 1].contiguous(), W, T, S - 1, cache, S, aux=aux_d)
     torch.cuda.synchronize()
     hf = full["h"].reshape(B, S, D)
     print(f"[fullsize-decode] {name}: prefill {S - 1} x {B}, decode position {S - 1}", flush=True)
     np.testing.assert_array_equal(pre.cpu().numpy().reshape(B, S - 1, D), hf[:, :S - 1])
-    np.testing.assert_array_equal(last.cpu().numpy(), hf[:, S - 1])
+    dp, dd = aux_to_numpy(aux_p), aux_to_numpy(aux_d)
+    last = last.cpu().numpy()
+    np.testing.assert_array_equal(last, dd["h_dump"][T])
+
+    def states(t):   # every token's state at the start of loop t, token order b*S + s
+        x = np.concatenate([dp["h_dump"][t].reshape(B, S - 1, D), dd["h_dump"][t][:, None]], axis=1)
+        return x.reshape(B * S, D)
+
+    seqs = [0] if cfg.get("da_heads", 0) else list(range(B))   # depth attention runs per sequence
+    rows = np.array([b * S + S - 1 for b in seqs])
+    d_r = cfg["head_dim"] if cfg["attn"] == "gqa" else cfg["qk_rope_head_dim"]
+    tables = ro.rope_tables(S, d_r, cfg["rope_base"])
+    for t in _loops_to_check(T):
+        idx = dd["route_idx"][t][seqs]
+        # the decode token's routing from its own router input
+        n2 = dd["n2_dump"][t][seqs].astype(np.float64)
+        idx_o, _, gap_o, _ = ro.route(n2, inp["Wr"], inp["router_bias"][min(t, cfg["n_bias_rows"] - 1)], cfg["top_k"])
+        same = np.all(np.sort(idx_o, 1) == np.sort(idx, 1), axis=1)
+        assert np.all(same | (gap_o < 1e-3))
+        if cfg.get("da_heads", 0):
+            hn, _, _, _ = ro.step_rows_depth(cfg, inp, [states(u) for u in range(t + 1)], inp["e"], t, T, rows, idx,
+                                             tables=tables)
+        else:
+            hn, _, _ = ro.step_rows(cfg, inp, states(t), inp["e"], t, rows, idx, tables=tables)
+        g = dd["h_dump"][t + 1][seqs]
+        err = float(np.max(np.abs(g - hn))) / rms(g)
+        print(f"[fullsize-decode] {name} loop {t}: max|dh|/rms={err:.3e}", flush=True)
+        assert err <= TOL
+    dev = float(np.max(np.abs(last - hf[:, S - 1]))) / rms(hf[:, S - 1])
+    print(f"[fullsize-decode] {name}: decode vs full forward max|dh|/rms={dev:.3e}", flush=True)
