@@ -500,8 +500,12 @@ static hipError_t dense_ns(const DenseGemm& g, hipStream_t s) {
   switch (g.ns) {
     case 3: return dense_launch<T, BM, BN, 3>(g, s);
     case 4: return dense_launch<T, BM, BN, 4>(g, s);
-    // a few rows (one-token decode): a four-stage ring, the grid is small
-    default: return g.M <= 64 ? dense_launch<T, BM, BN, 4>(g, s) : dense_launch<T, BM, BN, 2>(g, s);
+    // a few rows (one-token decode): a four-stage ring, the grid is small;
+    // 64x64 tiles: three stages (measured in place on the gqa forward)
+    default:
+      if (g.M <= 64) return dense_launch<T, BM, BN, 4>(g, s);
+      if (BM == 64 && BN == 64) return dense_launch<T, BM, BN, 3>(g, s);
+      return dense_launch<T, BM, BN, 2>(g, s);
   }
 }
 
