@@ -152,6 +152,9 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // One wave-wide direct load: every lane moves 16 bytes from src into LDS at
 // lds + 16 * lane. Issued through asm so that the compiler does not insert
 // conservative waits for the LDS write; the ring waits explicitly (wait_vmcnt).
+// m0 (the LDS base of the load) is set inside the same asm statement; the
+// compiler keeps nothing of its own in m0 in these kernels (the generated code
+// has no other m0 access), so the clobber cannot disturb it.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
