@@ -153,6 +153,22 @@ def test_degenerate_forced(name):
         assert np.all(res["expert_counts"] == cfg["batch"] * cfg["seq"])
 
 
+def test_k_sliced_down_projection():
+    """An expert hidden width of 2112 (33 stages of 64) cuts the down
+    projection into two K slices of 17 and 16 stages whose float partial sums
+    the combine adds; end to end against the oracle, and prefill + decode
+    still equal the forward bit for bit (the slice count is the config's)."""
+    cfg = get_config("gqa_small", expert_dim=2112)
+    T = cfg["T"]
+    res, inp, *_ = run_gpu(cfg, T=T)
+    mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro)
+    ref = ro.forward(cfg, inp, T=T, forced_idx=res["route_idx"])
+    err = np.max(np.abs(res["h"] - ref["h"]))
+    _report("k_sliced", ratio=f"{err / rms(ref['h']):.3e}", route_mismatch=mism, near_ties=near)
+    assert mism == 0
+    assert err <= TOL * rms(ref["h"])
+
+
 def test_act_zero_halting_vector_halts_after_two_loops():
     """w = 0 gives p = 1/2 every loop: the cumulative sum reaches 1.0 >= 0.99
     at the second loop, so every token runs exactly two loops whatever T."""
