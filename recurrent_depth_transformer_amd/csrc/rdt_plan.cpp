@@ -158,8 +158,9 @@ Plan make_decode_plan(const rdt_config& c, int T, int max_seq) {
   p.cosb = take((size_t)max_seq * (p.dr / 2) * 4);
   p.sinb = take((size_t)max_seq * (p.dr / 2) * 4);
   p.rope_len = max_seq;
-  // one workgroup per 256 cached positions (at most 16) per sequence and head group
-  p.att_split = max_seq / 256 < 1 ? 1 : (max_seq / 256 > 16 ? 16 : max_seq / 256);
+  // one workgroup per 128 cached positions, at most 8, per sequence and head
+  // group (measured in place: 4 ranges for the gqa decode, 8 for the MLA one)
+  p.att_split = max_seq / 128 < 1 ? 1 : (max_seq / 128 > 8 ? 8 : max_seq / 128);
   if (p.att_split > 1) {
     const size_t rows = (size_t)p.att_split * p.B * p.H;
     p.att_po = take(rows * p.dv * 4);

@@ -81,7 +81,7 @@ def test_prefill_then_decode_matches_full_forward(name):
 
 @pytest.mark.parametrize("name,seq", [("tiny", 520), ("gqa_small", 600), ("mla_small", 560)])
 def test_long_cache_decode_against_oracle(name, seq):
-    """Caches of 512 positions or more are cut into key ranges merged after the
+    """Caches of 256 positions or more are cut into key ranges merged after the
     attention launch, so the decoded rows round differently from the
     single-pass forward: they are checked against the oracle's full forward,
     forced to the GPU's routing, and the prefilled rows still equal the
