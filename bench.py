@@ -236,6 +236,16 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     value = executed / (ms * 1e-3)
     print(f"[bench] {ms:.4f} ms per forward (wall {wall * 1e3 / args.steps:.4f} ms)", file=sys.stderr, flush=True)
+    # spread of single steps (an event pair around each forward, after the timed run)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a_, b_ in evs:
+        a_.record(stream)
+        blk.forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    single = np.array([a_.elapsed_time(b_) for a_, b_ in evs])
+    step_ms = {"median": round(float(np.median(single)), 5), "p10": round(float(np.percentile(single, 10)), 5),
+               "p90": round(float(np.percentile(single, 90)), 5)}
 
     # per-stage device time: kernels launched one by one with HIP events around
     # each launch on the launch stream
@@ -264,6 +274,8 @@ def main():
                            else "k_grouped_gemm<bf16,192,128,0,2>") + " (expert gate/up + SwiGLU)",
                 "avg_launch_us": round(gu_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(gu_bytes)}
 
+    calibration = None if args.no_extras else machine_calibration(stream)
+
     extras = None
     if not args.no_extras:
         extras = {"decode": bench_decode(args, cfg, W, stream), "dreamer": bench_dreamer(args)}
@@ -285,6 +297,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages_us": {k: round(v[0] * 1e3, 2) for k, v in stage_avg.items() if v[1]},
+        "step_ms": step_ms,
+        "calibration": calibration,
         "extras": extras,
     }
     print(json.dumps(res), flush=True)
@@ -304,6 +318,25 @@ def _time(fn, steps: int, warmup: int, stream) -> float:
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def machine_calibration(stream) -> dict:
+    """What this MI355X delivers outside librdt, as context for the roofline
+    fractions (which use the published peaks): a 1 GiB device-to-device copy
+    (read + write bytes per second) and torch's library bf16 GEMM at
+    8192 x 8192 x 8192."""
+    import torch
+    x = torch.empty(1 << 29, dtype=torch.float16, device="cuda")
+    y = torch.empty_like(x)
+    copy_ms = _time(lambda: y.copy_(x), 10, 2, stream)
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    c = torch.empty(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    mm_ms = _time(lambda: torch.matmul(a, b, out=c), 5, 2, stream)
+    del x, y, a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+            "library_bf16_gemm_TFLOPs": round(2 * 8192 ** 3 / (mm_ms * 1e-3) / 1e12, 1)}
 
 
 def bench_decode(args, cfg: dict, W: dict, stream) -> dict:
