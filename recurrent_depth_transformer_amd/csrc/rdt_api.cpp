@@ -307,8 +307,9 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   // loop's combine clears the next loop's
   // Expert GEMM tiles (measured on MI355X): gate/up 192x128 with a two-stage
   // ring (two workgroups per CU), or 64x128 with a three-stage ring when
-  // experts see under 64 rows (decode); down 128x128 when experts see many
-  // rows, else 64x64 with a three-stage ring.
+  // experts see under 64 rows (decode); down 192x128 with a two-stage ring
+  // when experts see many rows (measured in place: 0.3-1.5 % faster forwards
+  // than 128x128), else 64x64 with a three-stage ring.
   const long long rows_per_expert = (long long)N * k / E;
   const bool bf = dt == DT_BF16;
   const int gu_bm = bf ? (rows_per_expert < 64 ? 64 : 192) : GU_BM;
@@ -560,7 +561,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     const long long ystride = (long long)N * (k + P.Se) * D;
     gd.ksplit = P.ksplit; gd.part = P.ksplit > 1 ? reinterpret_cast<float*>(ybuf) : nullptr; gd.pstride = ystride;
     // many rows per expert: large tiles; few rows: small tiles, deeper ring
-    if (dn_bm == 128) { gd.bm = 128; gd.bn = 128; gd.ns = 2; }
+    if (dn_bm == 128) { gd.bm = 192; gd.bn = 128; gd.ns = 2; }
     else { gd.bm = 64; gd.bn = 64; gd.ns = 3; }
     gd.max_mtiles = max_mtiles(gd.bm);
     LAUNCH(RDT_STAGE_EXPERT_DOWN, launch_grouped_gemm(gd, s));
