@@ -341,11 +341,20 @@ __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
   int ntot = 0;
   for (int s = 0; s < g.nseg; ++s) ntot += g.seg[s].ncols;
   const int ntn = (ntot + BN - 1) / BN;
-  const int ntm = (g.M + BM - 1) / BM;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int nt = L / ntm, mt = L % ntm;  // consecutive tiles share a B column block
+  // Tiles of the active rows only (the grid covers M; compacted rows may be
+  // fewer), spread over the XCDs by dispatch order. Each XCD's share is walked
+  // in groups of GM row tiles, column block by column block, so the tiles an
+  // XCD runs together share both A rows and B columns in its L2 (measured in
+  // place against walking whole columns: -1.6 to -2.6 % on the large forwards).
+  constexpr int GM = 4;
+  const int ntm = ((Mact < g.M ? Mact : g.M) + BM - 1) / BM;
+  const int nb = ntm * ntn;
+  if ((int)blockIdx.x >= nb) return;
+  const int L = xcd_remap(blockIdx.x, nb);
+  const int gfirst = (L / (GM * ntn)) * GM, gr = L % (GM * ntn);
+  const int gsz = ntm - gfirst < GM ? ntm - gfirst : GM;
+  const int mt = gfirst + gr % gsz, nt = gr / gsz;
   const int m0 = mt * BM, n0 = nt * BN;
-  if (m0 >= Mact) return;
   const int z = blockIdx.z;
   const int tid = threadIdx.x;
 
