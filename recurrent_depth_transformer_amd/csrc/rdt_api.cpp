@@ -200,20 +200,14 @@ static void pick_tile(long long M, long long N, int min_bn, int* bm, int* bn) {
   *bn = 64;
 }
 
-// bf16 128x192 tiles where 128x128 ones would need a second round of
-// workgroups (two per CU) that costs more than the wider tiles of one round;
-// every RoPE head has to lie inside one tile.
-static void widen_tile(DenseGemm& g) {
-  if (g.dtype != DT_BF16 || g.bm != 128 || g.bn != 128 || g.batch > 1 || g.A2 || g.epi != EPI_STORE) return;
-  long long ncols = 0;
-  for (int i = 0; i < g.nseg; ++i) {
-    if (g.seg[i].rope && (ncols % g.rope_dim || 192 % g.rope_dim)) return;
-    ncols += g.seg[i].ncols;
-  }
-  const long long slots = 512, mt = (g.M + 127) / 128;
-  const long long r128 = (mt * ((ncols + 127) / 128) + slots - 1) / slots;
-  const long long r192 = (mt * ((ncols + 191) / 192) + slots - 1) / slots;
-  if (3 * r192 < 2 * r128) g.bn = 192;
+// bf16 dense GEMMs with square 64 or 128 tiles run eight waves per workgroup:
+// one wave keeps only a few direct-to-LDS loads in flight, so twice the waves
+// stream a tile about 1.5x faster. Measured in place against four waves:
+// forwards 1-6 % faster (MLA -4 %, ACT -5 %, Dreamer -2 % with 128x128 tiles
+// instead of 128x192 ones), one-token decode -3 %.
+static hipError_t dense_gemm(DenseGemm& g, hipStream_t s) {
+  if (g.dtype == DT_BF16 && g.bm == g.bn && (g.bm == 64 || g.bm == 128)) g.nw = 8;
+  return launch_dense_gemm(g, s);
 }
 
 static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
@@ -363,8 +357,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g.cosb = dcos; g.sinb = dsin; g.rope_dim = P.dd; g.seq = 1;
       g.drope = 1; g.dpos0 = t; g.dpos1 = f.T - 1 - t;
       pick_tile(N, qw + 2 * kw, P.dd, &g.bm, &g.bn);
-      widen_tile(g);
-      LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g, s));
+      LAUNCH(RDT_STAGE_QKV, dense_gemm(g, s));
       DepthAttnArgs da{};
       da.dtype = dt; da.q = dq; da.k = dk; da.v = dvb; da.o = dout; da.lstride = (long long)lpl;
       da.n = N; da.H = P.Hd; da.KV = P.KVd; da.dd = P.dd; da.t = t; da.scale = 1.f / sqrtf((float)P.dd);
@@ -374,7 +367,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       gdo.rows = nullptr; gdo.gather = 0; gdo.M = N; gdo.Mdev = nullptr;
       gdo.nseg = 1; gdo.seg[0] = GemmSeg{w.Wo_da, D, dbuf, D, 0, 0, 1};
       pick_tile(N, D, 16, &gdo.bm, &gdo.bn);
-      LAUNCH(RDT_STAGE_OPROJ, launch_dense_gemm(gdo, s));
+      LAUNCH(RDT_STAGE_OPROJ, dense_gemm(gdo, s));
       // sequence-attention input: RMSNorm(u + d) (sequential) or RMSNorm(u) (parallel)
       NormArgs n1a{};
       n1a.dtype = dt; n1a.h = f.out; n1a.e = f.e; n1a.a = par ? nullptr : dbuf; n1a.g = w.g1; n1a.eps = c.norm_eps;
@@ -405,17 +398,16 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
         g.rows = nullptr; g.gather = 0; g.Mdev = nullptr;
         g.nseg = 3; g.seg[0] = sq; g.seg[1] = sk; g.seg[2] = sv;
         pick_tile(N, Hd + 2 * KVd, P.d, &g.bm, &g.bn);
-        widen_tile(g);
-        LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g, s));
+        LAUNCH(RDT_STAGE_QKV, dense_gemm(g, s));
       } else {
         DenseGemm gq = g;
         gq.rows = cur; gq.gather = 1; gq.Mdev = ncur; gq.nseg = 1; gq.seg[0] = sq;
         pick_tile(N, Hd, P.d, &gq.bm, &gq.bn);
-        LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(gq, s));
+        LAUNCH(RDT_STAGE_QKV, dense_gemm(gq, s));
         DenseGemm gkv = g;
         gkv.rows = prev; gkv.gather = 1; gkv.Mdev = nprev; gkv.nseg = 2; gkv.seg[0] = sk; gkv.seg[1] = sv;
         pick_tile(N, 2 * KVd, P.d, &gkv.bm, &gkv.bn);
-        LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(gkv, s));
+        LAUNCH(RDT_STAGE_QKV, dense_gemm(gkv, s));
       }
       if (f.cache && !direct) {
         LAUNCH(RDT_STAGE_QKV, append(t, 0, kb));
@@ -451,7 +443,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g1.seg[0] = GemmSeg{w.Wdq, P.ql, cq_raw, P.ql, 1, 0, 1};
       g1.seg[1] = GemmSeg{w.Wdkv, W, lat_raw, W, 1, 0, 1};
       pick_tile(N, P.ql + W, 16, &g1.bm, &g1.bn);
-      LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g1, s));
+      LAUNCH(RDT_STAGE_QKV, dense_gemm(g1, s));
       MlaNormArgs mn{};
       mn.dtype = dt; mn.cq_raw = (const float*)cq_raw; mn.ql = P.ql; mn.lat_raw = (const float*)lat_raw;
       mn.kvl = P.kvl; mn.nr = P.nr; mn.gq = w.gq; mn.gkv = w.gkv; mn.eps = c.norm_eps;
@@ -465,7 +457,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g2.rows = cur; g2.gather = act ? 1 : 0; g2.M = N; g2.Mdev = ncur;
       g2.nseg = 1; g2.seg[0] = GemmSeg{w.Wuq, P.H * qw, qfull, P.H * qw, 0, 0, 0};
       pick_tile(N, P.H * qw, 16, &g2.bm, &g2.bn);
-      LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g2, s));
+      LAUNCH(RDT_STAGE_QKV, dense_gemm(g2, s));
       // absorb: q_lat[h] = q_nope[h] . Wuk[h]  (per head, B = Wuk[h]^T)
       DenseGemm g3{};
       g3.dtype = dt; g3.A = qfull; g3.lda = P.H * qw; g3.a_bstride = qw; g3.K = P.nope; g3.epi = EPI_STORE;
@@ -473,7 +465,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g3.nseg = 1; g3.seg[0] = GemmSeg{wukT, P.kvl, qattn, P.H * W, 0, 0, 0};
       g3.b_bstride = (long long)P.kvl * P.nope; g3.c_bstride = W;
       pick_tile(N, (long long)P.kvl * P.H, 16, &g3.bm, &g3.bn);
-      LAUNCH(RDT_STAGE_QKV, launch_dense_gemm(g3, s));
+      LAUNCH(RDT_STAGE_QKV, dense_gemm(g3, s));
       QRopeArgs qr{};
       qr.dtype = dt; qr.src = qfull; qr.src_ld = P.H * qw; qr.src_hs = qw; qr.src_off = P.nope;
       qr.dst = qattn; qr.dst_ld = P.H * W; qr.dst_hs = W; qr.dst_off = P.kvl;
@@ -500,7 +492,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g4.nseg = 1; g4.seg[0] = GemmSeg{w.Wuv, P.vd, o, P.hv, 0, 0, 0};
       g4.b_bstride = (long long)P.vd * P.kvl; g4.c_bstride = P.vd;
       pick_tile(N, (long long)P.vd * P.H, 16, &g4.bm, &g4.bn);
-      LAUNCH(RDT_STAGE_ATTN, launch_dense_gemm(g4, s));
+      LAUNCH(RDT_STAGE_ATTN, dense_gemm(g4, s));
     }
 
     // a5: output projection (+ depth-wise LoRA as a second K phase)
@@ -513,7 +505,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       gz.seg[0] = GemmSeg{elt_ptr(w.lora_down, (long long)tl * P.r * P.hv, elt), P.r, z, P.r, 0, 0, 0};
       gz.bm = 128; gz.bn = 64;
       if ((N + 127) / 128 < 256) gz.bm = 64;
-      LAUNCH(RDT_STAGE_OPROJ, launch_dense_gemm(gz, s));
+      LAUNCH(RDT_STAGE_OPROJ, dense_gemm(gz, s));
     }
     DenseGemm go{};
     go.dtype = dt; go.A = o; go.lda = P.hv; go.K = P.hv; go.batch = 1; go.epi = EPI_STORE;
@@ -523,7 +515,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       go.A2 = z; go.lda2 = P.r; go.B2 = elt_ptr(w.lora_up, (long long)tl * D * P.r, elt); go.K2 = P.r;
     }
     pick_tile(N, D, 16, &go.bm, &go.bn);
-    LAUNCH(RDT_STAGE_OPROJ, launch_dense_gemm(go, s));
+    LAUNCH(RDT_STAGE_OPROJ, dense_gemm(go, s));
 
     // a5-a6: x = u + a, n2 = RMSNorm(x) * g2 (compacted rows), router softmax /
     // top-k, and the stable expert permutation, in one kernel

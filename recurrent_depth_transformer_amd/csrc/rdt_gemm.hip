@@ -3,8 +3,9 @@
 //   C = A . B^T with A [M, K] (rows optionally gathered through a token list)
 //   and B [N, K] in the [out, in] layout of a linear layer, fp32 accumulation.
 //
-// One 256-thread workgroup computes a BM x BN tile; its four waves form a 2x2
-// grid of (BM/2) x (BN/2) wave tiles built from 16x16x32 MFMAs. Each K stage
+// One workgroup computes a BM x BN tile; its NW waves (4 or 8) form an
+// (NW/2) x 2 grid of (BM/(NW/2)) x (BN/2) wave tiles built from 16x16x32
+// MFMAs. Each K stage
 // moves 128 bytes per row (64 bf16 or 32 fp32) from HBM into registers while
 // the previous stage is multiplied out of LDS. The fp32 tile then goes back
 // through LDS so the epilogue can see whole head rows (RoPE pairs, SwiGLU gate
@@ -18,15 +19,16 @@
 
 namespace rdt {
 
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, int NW = 4>
 struct GemmShape {
+  static constexpr int NT = NW * 64;    // threads per workgroup
   static constexpr int BK = 128 / (int)sizeof(T);
   static constexpr int VEC = ST<T>::VEC;
   static constexpr int VPR = BK / VEC;  // 16-byte vectors per row per stage (8)
   static constexpr int LDK = BK + VEC;  // LDS row stride (elements), 16-byte pad
-  static constexpr int A_LD = BM * VPR / 256;
-  static constexpr int B_LD = BN * VPR / 256;
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int A_LD = BM * VPR / NT;
+  static constexpr int B_LD = BN * VPR / NT;
+  static constexpr int WM = BM / (NW / 2), WN = BN / 2;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr int KSUB = BK / 32;
   static constexpr int CR = 32;         // epilogue rows per LDS chunk
@@ -130,12 +132,15 @@ __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[S::FM][S::FN], char* 
 // row has no data load a valid dummy row (their products only reach discarded
 // outputs); k-chunks past the end of K are zeroed in LDS after they land.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int NS>
+template <int BM, int BN, int NS, int NW = 4>
 struct LdsRing {
-  static constexpr int AL = BM / 32, BL = BN / 32;  // load rounds (32 rows each) per stage
+  static constexpr int RR = NW * 8;                 // rows per load round (16 bytes per lane)
+  static constexpr int RB = NW * 1024;              // bytes per load round
+  static constexpr int AL = BM / RR, BL = BN / RR;  // load rounds per stage
   static constexpr int LPS = AL + BL;               // load instructions per thread per stage
   static constexpr int STAGE = (BM + BN) * 128;     // bytes per stage (>= the fp32 epilogue chunk)
-  static constexpr int FM = BM / 32, FN = BN / 32;  // 16x16 fragments per wave
+  static constexpr int WM = BM / (NW / 2);          // wave tile rows
+  static constexpr int FM = WM / 16, FN = BN / 32;  // 16x16 fragments per wave
 };
 
 // Waits until at most n vector-memory operations of this wave are in flight.
@@ -164,17 +169,16 @@ typedef __attribute__((address_space(3))) char lds_char;
 // Stage buffers are distinct __shared__ objects and the loop is unrolled by NS,
 // so every LDS access names its stage statically: the compiler can then tell the
 // DMA writes of one stage from the reads of another and does not serialise them.
-template <int BM, int BN, int NS, bool TWO>
-__device__ __forceinline__ void gemm_mainloop_ring(f32x4 (&acc)[BM / 32][BN / 32], char* const (&L)[NS],
-                                                   const bf16_t* (&ap)[BM / 32], const bf16_t* (&bp)[BN / 32],
-                                                   int K, const bf16_t* (&ap2)[BM / 32],
-                                                   const bf16_t* (&bp2)[BN / 32], int K2, const bf16_t* adummy,
+template <int BM, int BN, int NS, bool TWO, int NW, typename R = LdsRing<BM, BN, NS, NW>>
+__device__ __forceinline__ void gemm_mainloop_ring(f32x4 (&acc)[R::FM][R::FN], char* const (&L)[NS],
+                                                   const bf16_t* (&ap)[R::AL], const bf16_t* (&bp)[R::BL],
+                                                   int K, const bf16_t* (&ap2)[R::AL],
+                                                   const bf16_t* (&bp2)[R::BL], int K2, const bf16_t* adummy,
                                                    const bf16_t* bdummy, const bf16_t* adummy2,
                                                    const bf16_t* bdummy2) {
-  using R = LdsRing<BM, BN, NS>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int prow = tid >> 3;                        // row within a 32-row round
+  const int prow = tid >> 3;                        // row within a load round
   const int kchunk = ((tid & 7) ^ ((prow >> 1) & 7)) * 8;  // logical k offset this lane loads
   const int nk1 = (K + 63) >> 6;
   const int nk = nk1 + (TWO ? (K2 + 63) >> 6 : 0);
@@ -193,13 +197,13 @@ __device__ __forceinline__ void gemm_mainloop_ring(f32x4 (&acc)[BM / 32][BN / 32
     for (int i = 0; i < R::AL; ++i) {
       const bf16_t* p = ph2 ? ap2[i] : ap[i];
       const bf16_t* src = (p != nullptr && k < Kp) ? p + k : (ph2 ? adummy2 : adummy);
-      dma16(src, st + i * 4096);
+      dma16(src, st + i * R::RB);
     }
 #pragma unroll
     for (int i = 0; i < R::BL; ++i) {
       const bf16_t* p = ph2 ? bp2[i] : bp[i];
       const bf16_t* src = (p != nullptr && k < Kp) ? p + k : (ph2 ? bdummy2 : bdummy);
-      dma16(src, st + BM * 128 + i * 4096);
+      dma16(src, st + BM * 128 + i * R::RB);
     }
   };
   // one of the LPS load instructions of a stage (idx < AL: A rows, else B rows)
@@ -210,10 +214,10 @@ __device__ __forceinline__ void gemm_mainloop_ring(f32x4 (&acc)[BM / 32][BN / 32
     const uint32_t st = (uint32_t)(uintptr_t)(lds_char*)buf + __builtin_amdgcn_readfirstlane(wave) * 1024;
     if (idx < R::AL) {
       const bf16_t* p = ph2 ? ap2[idx] : ap[idx];
-      dma16((p != nullptr && k < Kp) ? p + k : (ph2 ? adummy2 : adummy), st + idx * 4096);
+      dma16((p != nullptr && k < Kp) ? p + k : (ph2 ? adummy2 : adummy), st + idx * R::RB);
     } else {
       const bf16_t* p = ph2 ? bp2[idx - R::AL] : bp[idx - R::AL];
-      dma16((p != nullptr && k < Kp) ? p + k : (ph2 ? bdummy2 : bdummy), st + BM * 128 + (idx - R::AL) * 4096);
+      dma16((p != nullptr && k < Kp) ? p + k : (ph2 ? bdummy2 : bdummy), st + BM * 128 + (idx - R::AL) * R::RB);
     }
   };
   // zero this lane's k-chunks that lie past the end of K (after they landed)
@@ -224,16 +228,16 @@ __device__ __forceinline__ void gemm_mainloop_ring(f32x4 (&acc)[BM / 32][BN / 32
     if (k < Kp) return;
     char* st = buf + tid * 16;
 #pragma unroll
-    for (int i = 0; i < R::AL; ++i) *reinterpret_cast<uint4*>(st + i * 4096) = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < R::AL; ++i) *reinterpret_cast<uint4*>(st + i * R::RB) = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < R::BL; ++i) *reinterpret_cast<uint4*>(st + BM * 128 + i * 4096) = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < R::BL; ++i) *reinterpret_cast<uint4*>(st + BM * 128 + i * R::RB) = make_uint4(0, 0, 0, 0);
   };
   // Fragments of one 32-wide k-step (ks) of a stage, read from LDS into registers.
   auto read_frags = [&](const char* st, int ks, Frag<bf16_t> (&fa)[R::FM], Frag<bf16_t> (&fb)[R::FN]) {
     const int kc = ks * 4 + (lane >> 4);
 #pragma unroll
     for (int i = 0; i < R::FM; ++i) {
-      const int row = wm * (BM / 2) + i * 16 + (lane & 15);
+      const int row = wm * R::WM + i * 16 + (lane & 15);
       fa[i].v[0] = *reinterpret_cast<const uint4*>(st + row * 128 + ((kc ^ ((row >> 1) & 7)) << 4));
     }
 #pragma unroll
@@ -310,7 +314,7 @@ __device__ __forceinline__ void gemm_mainloop_ring(f32x4 (&acc)[BM / 32][BN / 32
 }
 
 // Writes the accumulators of rows [c*CR, c*CR+CR) into the fp32 LDS tile.
-template <typename T, int BM, int BN, typename S = GemmShape<T, BM, BN>>
+template <typename T, int BM, int BN, int NW = 4, typename S = GemmShape<T, BM, BN, NW>>
 __device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[S::FM][S::FN], float* Cs, int c) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -328,10 +332,11 @@ __device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[S::FM][S::FN], flo
 }
 
 // ============================================================== dense GEMM
-template <typename T, int BM, int BN, bool TWO, int NS>
-__global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
-  using S = GemmShape<T, BM, BN>;
-  constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS>::STAGE : S::SMEM;
+template <typename T, int BM, int BN, bool TWO, int NS, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void k_dense_gemm(DenseGemm g) {
+  static_assert(sizeof(T) == 2 || NW == 4, "the fp32 path runs four waves");
+  using S = GemmShape<T, BM, BN, NW>;
+  constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS, NW>::STAGE : S::SMEM;
   __shared__ __align__(16) char L0[ST];
   __shared__ __align__(16) char L1[sizeof(T) == 2 ? ST : 16];
   __shared__ __align__(16) char L2[sizeof(T) == 2 && NS > 2 ? ST : 16];
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
   const T* A = reinterpret_cast<const T*>(g.A) + (long long)z * g.a_bstride;
 #pragma unroll
   for (int i = 0; i < S::A_LD; ++i) {
-    const int r = (tid + i * 256) / S::VPR;
+    const int r = (tid + i * S::NT) / S::VPR;
     const int row = m0 + r;
     ap[i] = nullptr;
     ap2[i] = nullptr;
@@ -377,7 +382,7 @@ __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
   }
 #pragma unroll
   for (int i = 0; i < S::B_LD; ++i) {
-    const int c = n0 + (tid + i * 256) / S::VPR;
+    const int c = n0 + (tid + i * S::NT) / S::VPR;
     bp[i] = nullptr;
     bp2[i] = nullptr;
     if (c < ntot) {
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
     const T* bd = reinterpret_cast<const T*>(g.seg[0].B) + (long long)z * g.b_bstride;
     char* const Ls[4] = {L0, L1, L2, L3};
     char* const (&Lr)[NS] = *reinterpret_cast<char* const(*)[NS]>(Ls);
-    gemm_mainloop_ring<BM, BN, NS, TWO>(acc, Lr, ap, bp, g.K, ap2, bp2, g.K2, A, bd,
+    gemm_mainloop_ring<BM, BN, NS, TWO, NW>(acc, Lr, ap, bp, g.K, ap2, bp2, g.K2, A, bd,
                                         reinterpret_cast<const T*>(g.A2), reinterpret_cast<const T*>(g.B2));
   } else {
     gemm_mainloop<T, BM, BN, TWO>(acc, smem, ap, bp, g.K, ap2, bp2, g.K2);
@@ -403,12 +408,12 @@ __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
   float* Cs = reinterpret_cast<float*>(smem);
 #pragma unroll 1
   for (int c = 0; c < BM / S::CR; ++c) {
-    acc_to_lds<T, BM, BN>(acc, Cs, c);
+    acc_to_lds<T, BM, BN, NW>(acc, Cs, c);
     __syncthreads();
     const int rbase = m0 + c * S::CR;
     const int nrows = S::CR;
     if (g.epi == EPI_STORE) {
-      for (int idx = tid; idx < nrows * (BN / 8); idx += 256) {
+      for (int idx = tid; idx < nrows * (BN / 8); idx += S::NT) {
         const int r = idx / (BN / 8), c8 = (idx % (BN / 8)) * 8;
         const int row = rbase + r, gc = n0 + c8;
         if (row >= Mact || gc >= ntot) continue;
@@ -492,16 +497,16 @@ __global__ __launch_bounds__(256) void k_dense_gemm(DenseGemm g) {
   }
 }
 
-template <typename T, int BM, int BN, int NS>
+template <typename T, int BM, int BN, int NS, int NW = 4>
 static hipError_t dense_launch(const DenseGemm& g, hipStream_t s) {
   int ntot = 0;
   for (int i = 0; i < g.nseg; ++i) ntot += g.seg[i].ncols;
   const int ntn = (ntot + BN - 1) / BN, ntm = (g.M + BM - 1) / BM;
   dim3 grid(ntn * ntm, 1, g.batch > 0 ? g.batch : 1);
   if (g.A2) {
-    hipLaunchKernelGGL((k_dense_gemm<T, BM, BN, true, NS>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_dense_gemm<T, BM, BN, true, NS, NW>), grid, dim3(NW * 64), 0, s, g);
   } else {
-    hipLaunchKernelGGL((k_dense_gemm<T, BM, BN, false, NS>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_dense_gemm<T, BM, BN, false, NS, NW>), grid, dim3(NW * 64), 0, s, g);
   }
   return hipGetLastError();
 }
@@ -523,8 +528,13 @@ static hipError_t dense_ns(const DenseGemm& g, hipStream_t s) {
 
 template <typename T>
 static hipError_t dense_dispatch(const DenseGemm& g, hipStream_t s) {
-  if constexpr (sizeof(T) == 2)
-    if (g.bm == 128 && g.bn == 192) return dense_ns<T, 128, 192>(g, s);
+  if constexpr (sizeof(T) == 2) {
+    if (g.nw == 8) {  // eight waves: 64x64 tiles with three stages, 128x128 with two
+      if (g.bm == 64 && g.bn == 64) return dense_launch<T, 64, 64, 3, 8>(g, s);
+      if (g.bm == 128 && g.bn == 128) return dense_launch<T, 128, 128, 2, 8>(g, s);
+      return hipErrorInvalidValue;
+    }
+  }
   if (g.bm == 64 && g.bn == 64) return dense_ns<T, 64, 64>(g, s);
   if (g.bm == 64 && g.bn == 128) return dense_ns<T, 64, 128>(g, s);
   if (g.bm == 128 && g.bn == 64) return dense_ns<T, 128, 64>(g, s);
@@ -537,10 +547,11 @@ hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s) {
 }
 
 // ============================================================ grouped GEMM
-template <typename T, int BM, int BN, int KIND, int NS>
-__global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
-  using S = GemmShape<T, BM, BN>;
-  constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS>::STAGE : S::SMEM;
+template <typename T, int BM, int BN, int KIND, int NS, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void k_grouped_gemm(GroupedGemm g) {
+  static_assert(sizeof(T) == 2 || NW == 4, "the fp32 path runs four waves");
+  using S = GemmShape<T, BM, BN, NW>;
+  constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS, NW>::STAGE : S::SMEM;
   __shared__ __align__(16) char L0[ST];
   __shared__ __align__(16) char L1[sizeof(T) == 2 ? ST : 16];
   __shared__ __align__(16) char L2[sizeof(T) == 2 && NS > 2 ? ST : 16];
@@ -601,7 +612,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
   const T* bp[S::B_LD];
 #pragma unroll
   for (int i = 0; i < S::A_LD; ++i) {
-    const int m = ml0 + (tid + i * 256) / S::VPR;
+    const int m = ml0 + (tid + i * S::NT) / S::VPR;
     ap[i] = nullptr;
     if (m < rows_g) {
       int src;
@@ -616,7 +627,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
     const T* wu = reinterpret_cast<const T*>(routed ? g.W2 : g.S2) + (routed ? grp : grp - g.E) * wsz;
 #pragma unroll
     for (int i = 0; i < S::B_LD; ++i) {
-      const int c = (tid + i * 256) / S::VPR;
+      const int c = (tid + i * S::NT) / S::VPR;
       const int f = n0 + (c % (BN / 2));
       bp[i] = f < g.N ? ((c < BN / 2 ? wg : wu) + (long long)f * g.K) : nullptr;
     }
@@ -624,7 +635,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
     const T* wd = reinterpret_cast<const T*>(routed ? g.W1 : g.S1) + (routed ? grp : grp - g.E) * wsz;
 #pragma unroll
     for (int i = 0; i < S::B_LD; ++i) {
-      const int c = n0 + (tid + i * 256) / S::VPR;
+      const int c = n0 + (tid + i * S::NT) / S::VPR;
       bp[i] = c < g.N ? wd + (long long)c * g.K : nullptr;
     }
   }
@@ -646,7 +657,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
       for (int i = 0; i < S::B_LD; ++i)
         if (bp[i]) bp[i] += k0;
     }
-    gemm_mainloop_ring<BM, BN, NS, false>(acc, Lr, ap, bp, Kl, ap, bp, 0, A, bd, A, bd);
+    gemm_mainloop_ring<BM, BN, NS, false, NW>(acc, Lr, ap, bp, Kl, ap, bp, 0, A, bd, A, bd);
   } else {
     gemm_mainloop<T, BM, BN, false>(acc, smem, ap, bp, g.K, ap, bp, 0);
   }
@@ -655,10 +666,10 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
   T* C = reinterpret_cast<T*>(g.C);
 #pragma unroll 1
   for (int c = 0; c < BM / S::CR; ++c) {
-    acc_to_lds<T, BM, BN>(acc, Cs, c);
+    acc_to_lds<T, BM, BN, NW>(acc, Cs, c);
     __syncthreads();
     const int nrows = S::CR;
-    for (int idx = tid; idx < nrows * (OUTW / 8); idx += 256) {
+    for (int idx = tid; idx < nrows * (OUTW / 8); idx += S::NT) {
       const int r = idx / (OUTW / 8), c8 = (idx % (OUTW / 8)) * 8;
       const int m = ml0 + c * S::CR + r;
       const int col = n0 + c8;
@@ -684,12 +695,12 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GroupedGemm g) {
   }
 }
 
-template <typename T, int BM, int BN, int KIND, int NS>
+template <typename T, int BM, int BN, int KIND, int NS, int NW = 4>
 static hipError_t grouped_launch(const GroupedGemm& g, hipStream_t s) {
   const int outw = KIND == 0 ? BN / 2 : BN;
   const int ntn = (g.N + outw - 1) / outw;
   dim3 grid(g.max_mtiles * ntn, KIND == 1 && sizeof(T) == 2 && g.ksplit > 1 ? g.ksplit : 1);
-  hipLaunchKernelGGL((k_grouped_gemm<T, BM, BN, KIND, NS>), grid, dim3(256), 0, s, g);
+  hipLaunchKernelGGL((k_grouped_gemm<T, BM, BN, KIND, NS, NW>), grid, dim3(NW * 64), 0, s, g);
   return hipGetLastError();
 }
 
@@ -698,6 +709,8 @@ static hipError_t grouped_dispatch(const GroupedGemm& g, hipStream_t s) {
   if constexpr (sizeof(T) == 4) {
     return g.kind == 0 ? grouped_launch<T, GU_BM, GU_BN, 0, 2>(g, s) : grouped_launch<T, DN_BM, DN_BN, 1, 2>(g, s);
   } else {
+    // four waves: eight-wave expert tiles were slower in place (192x128 spills
+    // at the register budget of two workgroups per CU; 128x128 needs more tiles)
 #define RDT_G(K, BM, BN, NS) \
     if (g.kind == K && g.bm == BM && g.bn == BN && g.ns == NS) return grouped_launch<T, BM, BN, K, NS>(g, s);
     RDT_G(0, 64, 128, 3) RDT_G(0, 128, 128, 2) RDT_G(0, 192, 128, 2)

@@ -64,6 +64,7 @@ struct DenseGemm {
   int drope, dpos0, dpos1; // depth RoPE: pairs below rope_dim/4 at dpos0, the rest at dpos1
   int bm, bn;            // tile shape (64 or 128 each)
   int ns;                // bf16 pipeline stages (2..4; 0 = default)
+  int nw;                // bf16 waves per workgroup: 8 (64x64 and 128x128 tiles), else 4
 };
 hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s);
 
