@@ -1,9 +1,9 @@
 // Causal flash attention for grouped-query and absorbed multi-latent attention.
 //
-// A 256-thread workgroup (4 waves) owns one sequence b, NHB query heads that
-// read the same kv head, and 4/NHB consecutive slices of QW query rows (rows of
-// the compacted active list when ACT is on). Wave w handles head w % NHB and
-// slice w / NHB. Key/value tiles of KT positions are shared by all four waves:
+// A workgroup of NW waves (4 or 8) owns one sequence b, NHB query heads that
+// read the same kv head, and NW/NHB consecutive slices of QW query rows (rows
+// of the compacted active list when ACT is on). Wave w handles head w % NHB
+// and slice w / NHB. Key/value tiles of KT positions are shared by all waves:
 // they are double-buffered in LDS, and the global loads of the next tile (of
 // the next two, in two register sets, for 16-row slices) are in flight while
 // the current tile is multiplied.
@@ -32,8 +32,9 @@ namespace rdt {
 // immediate offset.
 __device__ __forceinline__ int vswz(int d) { return (d >> 4) & 3; }
 
-template <typename T, int DQK, int DV, int QW, int NHB, int KT>
-__global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
+template <typename T, int DQK, int DV, int QW, int NHB, int KT, int NW>
+__global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
+  constexpr int NT = NW * 64;
   constexpr int KB = KT / 16;  // 16-key blocks per tile
   constexpr int DQKP = (DQK + 31) / 32 * 32;
   constexpr int KS = DQKP / 32;
@@ -42,13 +43,13 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   constexpr int VEC = ST<T>::VEC;
   constexpr int KLD = DQKP + VEC;
   constexpr int VLD = KT + 4;
-  constexpr int SLICES = 4 / NHB;
+  constexpr int SLICES = NW / NHB;
   constexpr int BQ = QW * SLICES;  // query rows per workgroup (per head)
-  // per-thread share of one K tile and one V tile (256 threads)
+  // per-thread share of one K tile and one V tile (NT threads)
   constexpr int KV_VECS = KT * (DQKP / VEC);
-  constexpr int KL = (KV_VECS + 255) / 256;
+  constexpr int KL = (KV_VECS + NT - 1) / NT;
   constexpr int VV = sizeof(T) == 2 ? (KT / 2) * (DV / 8) : KT * (DV / 4);
-  constexpr int VL = (VV + 255) / 256;
+  constexpr int VL = (VV + NT - 1) / NT;
   __shared__ __align__(16) T Ks[2][KT * KLD];
   __shared__ __align__(16) T Vt[2][DV * VLD];
 
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   auto gload = [&](int k0, RK& rk, RV& rv0, RV& rv1) {
 #pragma unroll
     for (int u = 0; u < KL; ++u) {
-      const int v = tid + u * 256;
+      const int v = tid + u * NT;
       const int kr = v / (DQKP / VEC), kc = (v % (DQKP / VEC)) * VEC;
       const int key = k0 + kr;
       rk[u] = (v < KV_VECS && key < kmax && kc < DQK)
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < VL; ++u) {
-      const int v = tid + u * 256;
+      const int v = tid + u * NT;
       if constexpr (sizeof(T) == 2) {
         const int kp = v / (DV / 8), dc = (v % (DV / 8)) * 8;
         const int key = k0 + 2 * kp;
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   auto sstore = [&](int buf, const RK& rk, const RV& rv0, const RV& rv1) {
 #pragma unroll
     for (int u = 0; u < KL; ++u) {
-      const int v = tid + u * 256;
+      const int v = tid + u * NT;
       if (v < KV_VECS) {
         const int kr = v / (DQKP / VEC), kc = (v % (DQKP / VEC)) * VEC;
         *reinterpret_cast<uint4*>(&Ks[buf][kr * KLD + kc]) = rk[u];
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < VL; ++u) {
-      const int v = tid + u * 256;
+      const int v = tid + u * NT;
       if (v >= VV) continue;
       if constexpr (sizeof(T) == 2) {
         // keys 2kp, 2kp+1 of rows dc..dc+7: one dword per row, at 4-key
@@ -380,14 +381,14 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   }
 }
 
-template <typename T, int DQK, int DV, int QW, int NHB>
+template <typename T, int DQK, int DV, int QW, int NHB, int NW = 4>
 static hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
   // 128-key tiles for bf16 heads up to 64 wide (measured faster on the gqa and
   // ACT workloads); 64-key tiles otherwise (LDS and registers)
   constexpr int KT = (sizeof(T) == 2 && DQK <= 64) ? 128 : 64;
-  constexpr int BQ = QW * (4 / NHB);
+  constexpr int BQ = QW * (NW / NHB);
   dim3 grid((a.dec ? (a.nsplit > 1 ? a.nsplit : 1) : (a.S + BQ - 1) / BQ) * a.B * (a.H / NHB));
-  hipLaunchKernelGGL((k_attention<T, DQK, DV, QW, NHB, KT>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_attention<T, DQK, DV, QW, NHB, KT, NW>), grid, dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -333,7 +333,7 @@ __device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[S::FM][S::FN], flo
 
 // ============================================================== dense GEMM
 template <typename T, int BM, int BN, bool TWO, int NS, int NW>
-__global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void k_dense_gemm(DenseGemm g) {
+__global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) void k_dense_gemm(DenseGemm g) {
   static_assert(sizeof(T) == 2 || NW == 4, "the fp32 path runs four waves");
   using S = GemmShape<T, BM, BN, NW>;
   constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS, NW>::STAGE : S::SMEM;
@@ -548,7 +548,7 @@ hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s) {
 
 // ============================================================ grouped GEMM
 template <typename T, int BM, int BN, int KIND, int NS, int NW>
-__global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void k_grouped_gemm(GroupedGemm g) {
+__global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) void k_grouped_gemm(GroupedGemm g) {
   static_assert(sizeof(T) == 2 || NW == 4, "the fp32 path runs four waves");
   using S = GemmShape<T, BM, BN, NW>;
   constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS, NW>::STAGE : S::SMEM;
