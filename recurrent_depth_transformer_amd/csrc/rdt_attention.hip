@@ -243,9 +243,12 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
         mx *= sc;  // scores stay raw; the scale (> 0) is applied inside the exponent
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(mrow[qs], mx);
+        // the reference max moves only when the tile's max exceeds it by more
+        // than 8 (probabilities stay below 2^8); otherwise alpha is exactly 1
+        const bool move = mx > mrow[qs] + 8.f;
+        const float mnew = move ? mx : mrow[qs];
         const float base = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(mrow[qs] - base);
+        const float alpha = move ? __builtin_amdgcn_exp2f(mrow[qs] - base) : 1.f;
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
         rs += __shfl_xor(rs, 32, 64);
         lrow[qs] = lrow[qs] * alpha + rs;
         mrow[qs] = mnew;
-        if (__ballot(alpha != 1.f)) {  // some row's running max moved
+        if (__ballot(move)) {  // some row's reference max moved
 #pragma unroll
           for (int ds = 0; ds < DS; ++ds) {
             oacc[ds][qs][0] *= alpha;
