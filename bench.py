@@ -270,8 +270,8 @@ def main():
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_from_profiles(args.workload),
-                "kernel": ("k_grouped_gemm<f32,128,128,0,2>" if cfg["dtype"] == "f32"
-                           else "k_grouped_gemm<bf16,192,128,0,2>") + " (expert gate/up + SwiGLU)",
+                "kernel": ("k_grouped_gemm<f32,128,128,0,2,4>" if cfg["dtype"] == "f32"
+                           else "k_grouped_gemm<bf16,192,128,0,2,4>") + " (expert gate/up + SwiGLU)",
                 "avg_launch_us": round(gu_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(gu_bytes)}
 
     calibration = None if args.no_extras else machine_calibration(stream)
