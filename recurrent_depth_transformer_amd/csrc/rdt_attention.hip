@@ -12,27 +12,31 @@
 // The scores are formed transposed, S^T = K Q^T, so that a lane holds four
 // consecutive keys of one query: that is exactly the k-slot layout the second
 // MFMA needs for P, so O^T = V^T P^T is accumulated without moving P through
-// LDS. V is written to LDS transposed (Vt[d][key]) for the same reason; in
-// bf16 the 4-key groups of each row are permuted (vswz) against LDS bank
-// conflicts of the transposing stores.
+// LDS. In bf16, V stays row-major in LDS and the V^T fragments come from the
+// LDS transpose read (ds_read_b64_tr_b16: within each 16-lane group, lane j
+// receives element j & 3 of the 8-byte chunks addressed by lanes
+// 4t + (j >> 2), t = 0..3). In fp32, V is written to LDS transposed.
 //
 // Multi-latent attention in absorbed form is the same computation with one kv
 // head whose key is [c_kv | k_rope] and whose value is the c_kv prefix of the
-// same row, shared by every query head.
+// same row, shared by every query head; in bf16 (VK) the V^T fragments are
+// then read from the K tile itself and no V tile is loaded.
 #include "rdt_device.h"
 #include "rdt_launch.h"
 
 namespace rdt {
 
 
-// slot of the 4-key group g in row d of the transposed bf16 V tile: g ^ vswz(d).
-// With rows padded by 4 keys (KT + 4), the 16-row fragment reads are conflict-free
-// and the transposing stores (8 rows 8 apart per pass) at most 2-way; vswz is
-// constant over each 16-row block, so every address stays a base plus an
-// immediate offset.
-__device__ __forceinline__ int vswz(int d) { return (d >> 4) & 3; }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-template <typename T, int DQK, int DV, int QW, int NHB, int KT, int NW>
+// Four 16-bit elements through the LDS transpose read (gfx950), as two dwords.
+__device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+template <typename T, int DQK, int DV, int QW, int NHB, int KT, int NW, bool VK>
 __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KB = KT / 16;  // 16-key blocks per tile
@@ -41,17 +45,22 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
   constexpr int QS = QW / 16;
   constexpr int DS = DV / 16;
   constexpr int VEC = ST<T>::VEC;
+  constexpr bool BF = sizeof(T) == 2;
+  static_assert(!VK || (BF && DV <= DQK), "V from the K tile needs bf16 and DV <= DQK");
   constexpr int KLD = DQKP + VEC;
-  constexpr int VLD = KT + 4;
+  // bf16: V row-major with rows padded by 16 (conflict-free transpose reads);
+  // fp32: V transposed, rows of KT + 4 keys
+  constexpr int VLD = BF ? DV + 16 : KT + 4;
+  constexpr int VSZ = VK ? 8 : (BF ? KT * VLD : DV * VLD);
   constexpr int SLICES = NW / NHB;
   constexpr int BQ = QW * SLICES;  // query rows per workgroup (per head)
   // per-thread share of one K tile and one V tile (NT threads)
   constexpr int KV_VECS = KT * (DQKP / VEC);
   constexpr int KL = (KV_VECS + NT - 1) / NT;
-  constexpr int VV = sizeof(T) == 2 ? (KT / 2) * (DV / 8) : KT * (DV / 4);
-  constexpr int VL = (VV + NT - 1) / NT;
+  constexpr int VV = VK ? 0 : (BF ? KT * (DV / 8) : KT * (DV / 4));
+  constexpr int VL = VV > 0 ? (VV + NT - 1) / NT : 1;
   __shared__ __align__(16) T Ks[2][KT * KLD];
-  __shared__ __align__(16) T Vt[2][DV * VLD];
+  __shared__ __align__(16) T Vt[2][VSZ];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lg = lane >> 4, lc = lane & 15;
@@ -129,13 +138,13 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) qlo = min(qlo, __shfl_xor(qlo, o, 64));
 
-  // ---- K/V tile: global -> registers -> LDS (V transposed); two register
-  // sets so that two tiles can be in flight
+  // ---- K/V tile: global -> registers -> LDS (fp32 V transposed); two
+  // register sets so that two tiles can be in flight
   typedef uint4 RK[KL];
   typedef uint4 RV[VL];
   RK rk0, rk1;
-  RV rv00, rv10, rv01, rv11;
-  auto gload = [&](int k0, RK& rk, RV& rv0, RV& rv1) {
+  RV rv0, rv1;
+  auto gload = [&](int k0, RK& rk, RV& rv) {
 #pragma unroll
     for (int u = 0; u < KL; ++u) {
       const int v = tid + u * NT;
@@ -145,25 +154,18 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
                   ? *reinterpret_cast<const uint4*>(Kg + (tokbase + key) * a.k_ld + (long long)kvh * a.k_hs + kc)
                   : make_uint4(0, 0, 0, 0);
     }
+    if constexpr (VK) return;
 #pragma unroll
     for (int u = 0; u < VL; ++u) {
       const int v = tid + u * NT;
-      if constexpr (sizeof(T) == 2) {
-        const int kp = v / (DV / 8), dc = (v % (DV / 8)) * 8;
-        const int key = k0 + 2 * kp;
-        const T* src = Vg + (tokbase + key) * a.v_ld + (long long)kvh * a.v_hs + dc;
-        rv0[u] = (v < VV && key < kmax) ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
-        rv1[u] = (v < VV && key + 1 < kmax) ? *reinterpret_cast<const uint4*>(src + a.v_ld) : make_uint4(0, 0, 0, 0);
-      } else {
-        const int kr = v / (DV / 4), dc = (v % (DV / 4)) * 4;
-        const int key = k0 + kr;
-        rv0[u] = (v < VV && key < kmax)
-                     ? *reinterpret_cast<const uint4*>(Vg + (tokbase + key) * a.v_ld + (long long)kvh * a.v_hs + dc)
-                     : make_uint4(0, 0, 0, 0);
-      }
+      const int kr = v / (DV / VEC), dc = (v % (DV / VEC)) * VEC;
+      const int key = k0 + kr;
+      rv[u] = (v < VV && key < kmax)
+                  ? *reinterpret_cast<const uint4*>(Vg + (tokbase + key) * a.v_ld + (long long)kvh * a.v_hs + dc)
+                  : make_uint4(0, 0, 0, 0);
     }
   };
-  auto sstore = [&](int buf, const RK& rk, const RV& rv0, const RV& rv1) {
+  auto sstore = [&](int buf, const RK& rk, const RV& rv) {
 #pragma unroll
     for (int u = 0; u < KL; ++u) {
       const int v = tid + u * NT;
@@ -172,27 +174,17 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
         *reinterpret_cast<uint4*>(&Ks[buf][kr * KLD + kc]) = rk[u];
       }
     }
+    if constexpr (VK) return;
 #pragma unroll
     for (int u = 0; u < VL; ++u) {
       const int v = tid + u * NT;
       if (v >= VV) continue;
-      if constexpr (sizeof(T) == 2) {
-        // keys 2kp, 2kp+1 of rows dc..dc+7: one dword per row, at 4-key
-        // group kp/2 (slot (kp/2) ^ vswz(row)), half kp%2
-        const int kp = v / (DV / 8), dc = (v % (DV / 8)) * 8;
-        const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&rv0[u]);
-        const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&rv1[u]);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const uint32_t lo = (p0[x] & 0xffffu) | (p1[x] << 16);
-          const uint32_t hi = (p0[x] >> 16) | (p1[x] & 0xffff0000u);
-          const int d0 = dc + 2 * x, d1 = d0 + 1;
-          *reinterpret_cast<uint32_t*>(&Vt[buf][d0 * VLD + (((kp >> 1) ^ vswz(d0)) << 2) + ((kp & 1) << 1)]) = lo;
-          *reinterpret_cast<uint32_t*>(&Vt[buf][d1 * VLD + (((kp >> 1) ^ vswz(d1)) << 2) + ((kp & 1) << 1)]) = hi;
-        }
+      if constexpr (BF) {
+        const int kr = v / (DV / 8), dc = (v % (DV / 8)) * 8;
+        *reinterpret_cast<uint4*>(&Vt[buf][kr * VLD + dc]) = rv[u];
       } else {
         const int kr = v / (DV / 4), dc = (v % (DV / 4)) * 4;
-        const float* f = reinterpret_cast<const float*>(&rv0[u]);
+        const float* f = reinterpret_cast<const float*>(&rv[u]);
 #pragma unroll
         for (int x = 0; x < 4; ++x) Vt[buf][(dc + x) * VLD + kr] = f[x];
       }
@@ -295,17 +287,18 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
         }
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-          const int vr = ds * 16 + lc;
-          const T* vrow = Vb + vr * VLD;
           Frag<T> vf;
-          if constexpr (sizeof(T) == 2) {
-            // keys 32c + 4lg.. (group 8c + lg) and 32c + 16 + 4lg.. (group 8c + 4 + lg)
-            const int sw = vswz(vr);
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((8 * c + lg) ^ sw) << 2));
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((8 * c + 4 + lg) ^ sw) << 2));
+          if constexpr (BF) {
+            // V^T rows ds*16 + lc, k-slots 0..3 = keys 32c + 4lg + 0..3 and
+            // 4..7 = keys 32c + 16 + 4lg + 0..3: lane lc of each 16-lane group
+            // addresses key row 32c + 4lg + (lc >> 2), columns ds*16 + 4(lc & 3)
+            constexpr int LDV = VK ? KLD : VLD;
+            const T* vsrc = (VK ? Kb : Vb) + (32 * c + 4 * lg + (lc >> 2)) * LDV + ds * 16 + 4 * (lc & 3);
+            const uint2 lo = lds_read_tr16(vsrc);
+            const uint2 hi = lds_read_tr16(vsrc + 16 * LDV);
             vf.v[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
           } else {
-            vrow += 32 * c + lg * 4;
+            const T* vrow = Vb + (ds * 16 + lc) * VLD + 32 * c + lg * 4;
             vf.v[0] = *reinterpret_cast<const uint4*>(vrow);
             vf.v[sizeof(T) / 2 - 1] = *reinterpret_cast<const uint4*>(vrow + 16);
           }
@@ -319,34 +312,34 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
     // tile kt sits in LDS buffer kt & 1; register set (kt & 1) receives tile
     // kt + 2 while tile kt is multiplied, and tile kt + 1 (in the other set,
     // loaded one tile earlier) is written to the other LDS buffer afterwards
-    if (kt_begin < nkt) gload(kt_begin * KT, rk0, rv00, rv10);
-    if (kt_begin + 1 < nkt) gload((kt_begin + 1) * KT, rk1, rv01, rv11);
-    if (kt_begin < nkt) sstore(0, rk0, rv00, rv10);
+    if (kt_begin < nkt) gload(kt_begin * KT, rk0, rv0);
+    if (kt_begin + 1 < nkt) gload((kt_begin + 1) * KT, rk1, rv1);
+    if (kt_begin < nkt) sstore(0, rk0, rv0);
     __syncthreads();
     for (int kt = kt_begin; kt < nkt; kt += 2) {
-      if (kt + 2 < nkt) gload((kt + 2) * KT, rk0, rv00, rv10);
+      if (kt + 2 < nkt) gload((kt + 2) * KT, rk0, rv0);
       tile(kt, 0);
-      if (kt + 1 < nkt) sstore(1, rk1, rv01, rv11);
+      if (kt + 1 < nkt) sstore(1, rk1, rv1);
       __syncthreads();
       if (kt + 1 >= nkt) break;
-      if (kt + 3 < nkt) gload((kt + 3) * KT, rk1, rv01, rv11);
+      if (kt + 3 < nkt) gload((kt + 3) * KT, rk1, rv1);
       tile(kt + 1, 1);
-      if (kt + 2 < nkt) sstore(0, rk0, rv00, rv10);
+      if (kt + 2 < nkt) sstore(0, rk0, rv0);
       __syncthreads();
     }
   } else {
     // wide query slices keep one tile in flight (fewer registers, more
     // workgroups per CU)
     if (kt_begin < nkt) {
-      gload(kt_begin * KT, rk0, rv00, rv10);
-      sstore(0, rk0, rv00, rv10);
+      gload(kt_begin * KT, rk0, rv0);
+      sstore(0, rk0, rv0);
     }
     __syncthreads();
     for (int kt = kt_begin; kt < nkt; ++kt) {
       const int buf = (kt - kt_begin) & 1;
-      if (kt + 1 < nkt) gload((kt + 1) * KT, rk0, rv00, rv10);
+      if (kt + 1 < nkt) gload((kt + 1) * KT, rk0, rv0);
       tile(kt, buf);
-      if (kt + 1 < nkt) sstore(buf ^ 1, rk0, rv00, rv10);
+      if (kt + 1 < nkt) sstore(buf ^ 1, rk0, rv0);
       __syncthreads();
     }
   }
@@ -384,14 +377,14 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
   }
 }
 
-template <typename T, int DQK, int DV, int QW, int NHB, int NW = 4>
+template <typename T, int DQK, int DV, int QW, int NHB, bool VK, int NW = 4>
 static hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
   // 128-key tiles for bf16 heads up to 64 wide (measured faster on the gqa and
   // ACT workloads); 64-key tiles otherwise (LDS and registers)
   constexpr int KT = (sizeof(T) == 2 && DQK <= 64) ? 128 : 64;
   constexpr int BQ = QW * (NW / NHB);
   dim3 grid((a.dec ? (a.nsplit > 1 ? a.nsplit : 1) : (a.S + BQ - 1) / BQ) * a.B * (a.H / NHB));
-  hipLaunchKernelGGL((k_attention<T, DQK, DV, QW, NHB, KT, NW>), grid, dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((k_attention<T, DQK, DV, QW, NHB, KT, NW, VK>), grid, dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -399,26 +392,31 @@ static hipError_t attn_launch(const AttnArgs& a, hipStream_t s) {
 // (32 rows when the launch has blocks to spare: every key and value fragment
 // read from LDS then feeds two MFMAs; measured in place, MLA forward -7 %,
 // wide_moe -4 %).
-template <typename T, int DQK, int DV>
+template <typename T, int DQK, int DV, bool VK>
 static hipError_t attn_pick(const AttnArgs& a, hipStream_t s) {
   const int G = a.H / a.KV;
   const int nhb = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
   const long long blocks16 = (long long)(a.dec ? 1 : (a.S + 63) / 64) * a.B * a.H;  // 64 rows per block per head
   const bool wide = blocks16 * 2 >= 1024;
-  if (nhb == 4) return wide ? attn_launch<T, DQK, DV, 32, 4>(a, s) : attn_launch<T, DQK, DV, 16, 4>(a, s);
-  if (nhb == 2) return wide ? attn_launch<T, DQK, DV, 32, 2>(a, s) : attn_launch<T, DQK, DV, 16, 2>(a, s);
-  return wide ? attn_launch<T, DQK, DV, 32, 1>(a, s) : attn_launch<T, DQK, DV, 16, 1>(a, s);
+  if (nhb == 4) return wide ? attn_launch<T, DQK, DV, 32, 4, VK>(a, s) : attn_launch<T, DQK, DV, 16, 4, VK>(a, s);
+  if (nhb == 2) return wide ? attn_launch<T, DQK, DV, 32, 2, VK>(a, s) : attn_launch<T, DQK, DV, 16, 2, VK>(a, s);
+  return wide ? attn_launch<T, DQK, DV, 32, 1, VK>(a, s) : attn_launch<T, DQK, DV, 16, 1, VK>(a, s);
 }
 
 template <typename T>
 static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   const int dq = a.dqk, dv = a.dv;
-  if (dq == 16 && dv == 16) return attn_pick<T, 16, 16>(a, s);
-  if (dq == 32 && dv == 32) return attn_pick<T, 32, 32>(a, s);
-  if (dq == 64 && dv == 64) return attn_pick<T, 64, 64>(a, s);
-  if (dq == 128 && dv == 128) return attn_pick<T, 128, 128>(a, s);
-  if (dq == 160 && dv == 128) return attn_pick<T, 160, 128>(a, s);
-  if (dq == 96 && dv == 64) return attn_pick<T, 96, 64>(a, s);
+  // bf16 absorbed MLA: the value is the prefix of the key row; its V^T
+  // fragments are read from the K tile
+  const bool vk = sizeof(T) == 2 && a.v == a.k && a.v_ld == a.k_ld && a.v_hs == a.k_hs && dv <= dq;
+  if (dq == 16 && dv == 16) return attn_pick<T, 16, 16, false>(a, s);
+  if (dq == 32 && dv == 32) return attn_pick<T, 32, 32, false>(a, s);
+  if (dq == 64 && dv == 64) return attn_pick<T, 64, 64, false>(a, s);
+  if (dq == 128 && dv == 128) return attn_pick<T, 128, 128, false>(a, s);
+  if (dq == 160 && dv == 128)
+    return vk ? attn_pick<T, 160, 128, sizeof(T) == 2>(a, s) : attn_pick<T, 160, 128, false>(a, s);
+  if (dq == 96 && dv == 64)
+    return vk ? attn_pick<T, 96, 64, sizeof(T) == 2>(a, s) : attn_pick<T, 96, 64, false>(a, s);
   return hipErrorInvalidValue;
 }
 
