@@ -145,6 +145,27 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
   RK rk0, rk1;
   RV rv0, rv1;
   auto gload = [&](int k0, RK& rk, RV& rv) {
+    if (k0 + KT <= kmax) {  // every key of the tile exists: loads without predicates
+      const T* kb = Kg + (tokbase + k0) * a.k_ld + (long long)kvh * a.k_hs;
+#pragma unroll
+      for (int u = 0; u < KL; ++u) {
+        const int v = tid + u * NT;
+        const int kr = v / (DQKP / VEC), kc = (v % (DQKP / VEC)) * VEC;
+        if ((KV_VECS % NT == 0 || v < KV_VECS) && (DQKP == DQK || kc < DQK))
+          rk[u] = *reinterpret_cast<const uint4*>(kb + kr * a.k_ld + kc);
+        else
+          rk[u] = make_uint4(0, 0, 0, 0);
+      }
+      if constexpr (VK) return;
+      const T* vb = Vg + (tokbase + k0) * a.v_ld + (long long)kvh * a.v_hs;
+#pragma unroll
+      for (int u = 0; u < VL; ++u) {
+        const int v = tid + u * NT;
+        const int kr = v / (DV / VEC), dc = (v % (DV / VEC)) * VEC;
+        rv[u] = (VV % NT == 0 || v < VV) ? *reinterpret_cast<const uint4*>(vb + kr * a.v_ld + dc) : make_uint4(0, 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < KL; ++u) {
       const int v = tid + u * NT;
