@@ -300,14 +300,15 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   // loop 0's expert counts are cleared by the first RMSNorm kernel; each
   // loop's combine clears the next loop's
   // Expert GEMM tiles (measured on MI355X): gate/up 192x128 with a two-stage
-  // ring (two workgroups per CU), or 64x128 with a three-stage ring when
-  // experts see under 64 rows (decode); down 192x128 with a two-stage ring
+  // ring (two workgroups per CU), or 64x64 with a three-stage ring when
+  // experts see under 64 rows (decode: narrow tiles give more workgroups;
+  // 64x128 was 2-4 % slower per step); down 192x128 with a two-stage ring
   // when experts see many rows (measured in place: 0.3-1.5 % faster forwards
-  // than 128x128), else 64x64 with a three-stage ring.
+  // than 128x128), 64x32 for decode, else 64x64 with a three-stage ring.
   const long long rows_per_expert = (long long)N * k / E;
   const bool bf = dt == DT_BF16;
   const int gu_bm = bf ? (rows_per_expert < 64 ? 64 : 192) : GU_BM;
-  const int gu_bn = GU_BN;
+  const int gu_bn = bf && rows_per_expert < 64 ? 64 : GU_BN;
   const int dn_bm = (rows_per_expert >= 256 && bf) ? 128 : 64;
   // grid bound of a grouped GEMM with bm-row tiles: sum_e ceil(c_e / bm) over
   // the routed experts is at most N*k/bm + E; each shared expert adds ceil(N/bm)
@@ -554,7 +555,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     gd.ksplit = P.ksplit; gd.part = P.ksplit > 1 ? reinterpret_cast<float*>(ybuf) : nullptr; gd.pstride = ystride;
     // many rows per expert: large tiles; few rows: small tiles, deeper ring
     if (dn_bm == 128) { gd.bm = 192; gd.bn = 128; gd.ns = 2; }
-    else { gd.bm = 64; gd.bn = 64; gd.ns = 3; }
+    else { gd.bm = 64; gd.bn = rows_per_expert < 64 && bf ? 32 : 64; gd.ns = 3; }
     gd.max_mtiles = max_mtiles(gd.bm);
     LAUNCH(RDT_STAGE_EXPERT_DOWN, launch_grouped_gemm(gd, s));
 

@@ -148,7 +148,7 @@ struct LdsRing {
 __device__ __forceinline__ void wait_vmcnt(int n) {
   switch (n) {
 #define RDT_W(N) case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
-    RDT_W(2) RDT_W(4) RDT_W(6) RDT_W(8) RDT_W(10) RDT_W(12) RDT_W(16) RDT_W(20) RDT_W(24)
+    RDT_W(1) RDT_W(2) RDT_W(3) RDT_W(4) RDT_W(5) RDT_W(6) RDT_W(8) RDT_W(10) RDT_W(12) RDT_W(16) RDT_W(20) RDT_W(24)
 #undef RDT_W
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
@@ -713,8 +713,8 @@ static hipError_t grouped_dispatch(const GroupedGemm& g, hipStream_t s) {
     // at the register budget of two workgroups per CU; 128x128 needs more tiles)
 #define RDT_G(K, BM, BN, NS) \
     if (g.kind == K && g.bm == BM && g.bn == BN && g.ns == NS) return grouped_launch<T, BM, BN, K, NS>(g, s);
-    RDT_G(0, 64, 128, 3) RDT_G(0, 128, 128, 2) RDT_G(0, 192, 128, 2)
-    RDT_G(1, 64, 64, 3) RDT_G(1, 64, 64, 4) RDT_G(1, 192, 128, 2)
+    RDT_G(0, 64, 64, 3) RDT_G(0, 128, 128, 2) RDT_G(0, 192, 128, 2)
+    RDT_G(1, 64, 32, 3) RDT_G(1, 64, 64, 3) RDT_G(1, 64, 64, 4) RDT_G(1, 192, 128, 2)
 #undef RDT_G
     return hipErrorInvalidValue;
   }
