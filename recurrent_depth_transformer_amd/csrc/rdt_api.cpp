@@ -231,13 +231,15 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   // the RoPE tables are built by the first loop's RMSNorm kernel
   int* pos_dev = f.decode ? at<int>(ws, P.pos) : nullptr;
   // decode without ACT: the cached keys are cut into P.att_split ranges, one
-  // workgroup each, merged by a second launch
+  // workgroup each; the last range of each (sequence, head group) to finish
+  // merges them (counted in P.att_cnt ints in front of the expert counts)
   auto set_split = [&](AttnArgs& aa) {
     aa.nsplit = (f.decode && !act && P.att_split > 1) ? P.att_split : 1;
     if (aa.nsplit > 1) {
       aa.part_o = at<float>(ws, P.att_po);
       aa.part_m = at<float>(ws, P.att_pm);
       aa.part_l = at<float>(ws, P.att_pl);
+      aa.split_cnt = at<int>(ws, P.cnt);
     }
   };
   // loop t's cache: GQA keys then values, or MLA latents (rows b*max_seq + p)
@@ -292,7 +294,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   int* idx = at<int>(ws, P.idx);
   float* gates = at<float>(ws, P.gates);
   float* gap = at<float>(ws, P.gap);
-  int* cnt2 = at<int>(ws, P.cnt);      // per-expert counts of even / odd loops
+  int* cnt2 = at<int>(ws, P.cnt) + P.att_cnt;  // per-expert counts of even / odd loops
   int* slot = at<int>(ws, P.slot);
   int* pcap = at<int>(ws, P.pcap);
   char* hmid = at<char>(ws, P.hmid);
@@ -339,7 +341,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       n1a.rope_cos[0] = cosb; n1a.rope_sin[0] = sinb; n1a.rope_S[0] = P.rope_len; n1a.rope_dr[0] = P.dr;
       if (P.da) { n1a.rope_cos[1] = dcos; n1a.rope_sin[1] = dsin; n1a.rope_S[1] = f.T; n1a.rope_dr[1] = P.dd; }
       n1a.rope_base = c.rope_base;
-      n1a.zero = cnt2; n1a.zero_n = E;
+      n1a.zero = at<int>(ws, P.cnt); n1a.zero_n = P.att_cnt + E;  // split counters, loop 0's counts
       LAUNCH(RDT_STAGE_NORM1, launch_norm(n1a, s));
     }
     if (P.da) {
@@ -425,7 +427,6 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       aa.scale = 1.f / sqrtf((float)P.d);
       set_split(aa);
       LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, s));
-      if (aa.nsplit > 1) LAUNCH(RDT_STAGE_ATTN, launch_attention_merge(aa, s));
     } else {
       const int W = P.kvl + P.nr, qw = P.nope + P.nr;
       char* cq_raw = at<char>(ws, P.cq_raw);
@@ -485,7 +486,6 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       aa.scale = 1.f / sqrtf((float)(P.nope + P.nr));
       set_split(aa);
       LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, s));
-      if (aa.nsplit > 1) LAUNCH(RDT_STAGE_ATTN, launch_attention_merge(aa, s));
       // value up-projection per head: o[h] = o_lat[h] . Wuv[h]^T
       DenseGemm g4{};
       g4.dtype = dt; g4.A = olat; g4.lda = P.H * P.kvl; g4.a_bstride = P.kvl; g4.K = P.kvl; g4.epi = EPI_STORE;

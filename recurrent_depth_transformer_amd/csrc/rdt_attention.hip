@@ -365,20 +365,62 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
     }
   }
 
-  if (split) {  // partial result of this key range, unnormalised
+  if (split) {
+    // Partial result of this key range, unnormalised. The ranges of one
+    // (sequence, head group) may run on different XCDs (separate L2s), so the
+    // partials are written and read with device-coherent accesses (agent-scope
+    // atomic stores and loads) and counted with a device atomic; the range
+    // that finishes last forms o.
+    constexpr int SC = __HIP_MEMORY_SCOPE_AGENT;
 #pragma unroll
     for (int qs = 0; qs < QS; ++qs) {
       const int qq = qs * 16 + lc;
       if (qq >= nq) continue;
       const long long pr = ((long long)outer * a.B + (qfirst + qq)) * a.H + h;
       if (lg == 0) {
-        a.part_m[pr] = mrow[qs];
-        a.part_l[pr] = lrow[qs];
+        __hip_atomic_store(a.part_m + pr, mrow[qs], __ATOMIC_RELAXED, SC);
+        __hip_atomic_store(a.part_l + pr, lrow[qs], __ATOMIC_RELAXED, SC);
       }
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds)
-        *reinterpret_cast<float4*>(a.part_o + pr * DV + ds * 16 + lg * 4) =
-            make_float4(oacc[ds][qs][0], oacc[ds][qs][1], oacc[ds][qs][2], oacc[ds][qs][3]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __hip_atomic_store(a.part_o + pr * DV + ds * 16 + lg * 4 + r, oacc[ds][qs][r], __ATOMIC_RELAXED, SC);
+    }
+    __shared__ int s_last;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this range's partials landed before it is counted
+    __syncthreads();
+    const int grp = (int)(blockIdx.x % bz);             // (sequence b, head group)
+    if (tid == 0) s_last = __hip_atomic_fetch_add(a.split_cnt + grp, 1, __ATOMIC_RELAXED, SC) == a.nsplit - 1;
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) __hip_atomic_store(a.split_cnt + grp, 0, __ATOMIC_RELAXED, SC);  // ready for the next launch
+    // merge: one wave per head of the group, lane l owns columns 2l, 2l+1 of
+    // the sequence's query row (row b: one query per sequence in decode)
+    if (wave >= NHB) return;
+    const int hh = (int)(blockIdx.x % nhg) * NHB + wave;
+    const long long i = b;
+    float M = -INFINITY;
+    for (int r = 0; r < a.nsplit; ++r)
+      M = fmaxf(M, __hip_atomic_load(a.part_m + ((long long)r * a.B + i) * a.H + hh, __ATOMIC_RELAXED, SC));
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+    const int d = 2 * lane;
+    for (int r = 0; r < a.nsplit; ++r) {
+      const long long pr = ((long long)r * a.B + i) * a.H + hh;
+      const float m = __hip_atomic_load(a.part_m + pr, __ATOMIC_RELAXED, SC);
+      if (m == -INFINITY) continue;                 // an empty key range
+      const float wgt = exp2f(m - M);
+      L += wgt * __hip_atomic_load(a.part_l + pr, __ATOMIC_RELAXED, SC);
+      if (d < DV) {
+        o0 += wgt * __hip_atomic_load(a.part_o + pr * DV + d, __ATOMIC_RELAXED, SC);
+        o1 += wgt * __hip_atomic_load(a.part_o + pr * DV + d + 1, __ATOMIC_RELAXED, SC);
+      }
+    }
+    if (d < DV) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      T* Om = reinterpret_cast<T*>(a.o) + i * a.o_ld + (long long)hh * a.o_hs + d;
+      Om[0] = ST<T>::from_f(o0 * inv);
+      Om[1] = ST<T>::from_f(o1 * inv);
     }
     return;
   }
@@ -443,47 +485,9 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.H % a.KV) return hipErrorInvalidValue;
-  if (a.dec && a.nsplit > 1 && (!a.part_o || !a.part_m || !a.part_l || a.rows || a.seg)) return hipErrorInvalidValue;
+  if (a.dec && a.nsplit > 1 && (!a.part_o || !a.part_m || !a.part_l || !a.split_cnt || a.rows || a.seg || a.dv > 128))
+    return hipErrorInvalidValue;
   return a.dtype == DT_F32 ? attn_dispatch<float>(a, s) : attn_dispatch<bf16_t>(a, s);
-}
-
-// One wave per (query row i, head h); lane l owns output columns 2l, 2l+1.
-template <typename T>
-__global__ __launch_bounds__(256) void k_attention_merge(AttnArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int w = blockIdx.x * 4 + wave;
-  if (w >= a.B * a.H) return;
-  const int i = w / a.H, h = w % a.H;
-  float M = -INFINITY;
-  for (int r = 0; r < a.nsplit; ++r) M = fmaxf(M, a.part_m[((long long)r * a.B + i) * a.H + h]);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  const int d = 2 * lane;
-  for (int r = 0; r < a.nsplit; ++r) {
-    const long long pr = ((long long)r * a.B + i) * a.H + h;
-    const float m = a.part_m[pr];
-    if (m == -INFINITY) continue;                 // an empty key range
-    const float wgt = exp2f(m - M);
-    L += wgt * a.part_l[pr];
-    if (d < a.dv) {
-      o0 += wgt * a.part_o[pr * a.dv + d];
-      o1 += wgt * a.part_o[pr * a.dv + d + 1];
-    }
-  }
-  if (d < a.dv) {
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    T* O = reinterpret_cast<T*>(a.o) + (long long)i * a.o_ld + (long long)h * a.o_hs + d;
-    O[0] = ST<T>::from_f(o0 * inv);
-    O[1] = ST<T>::from_f(o1 * inv);
-  }
-}
-
-hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s) {
-  if (!a.dec || a.nsplit <= 1) return hipSuccess;
-  if (a.dv > 128 || a.dv % 2) return hipErrorInvalidValue;
-  dim3 grid((a.B * a.H + 3) / 4);
-  if (a.dtype == DT_F32) hipLaunchKernelGGL(k_attention_merge<float>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_attention_merge<bf16_t>, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
 }
 
 }  // namespace rdt

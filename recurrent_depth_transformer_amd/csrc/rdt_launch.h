@@ -116,12 +116,12 @@ struct AttnArgs {
   // tiles, one workgroup each; range r writes its unnormalised output and its
   // running max / sum (exp2 domain) for query row i, head h to
   // part_o[((r * nq + i) * H + h) * dv + d], part_m / part_l[(r * nq + i) * H + h]
-  // (nq = B query rows), and launch_attention_merge forms o from them
-  int nsplit; float* part_o; float* part_m; float* part_l;
+  // (nq = B query rows). split_cnt[b * (H / heads per workgroup) + group]
+  // (zero on entry, left zero) counts the finished ranges; the last one
+  // forms o from all of them
+  int nsplit; float* part_o; float* part_m; float* part_l; int* split_cnt;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
-// o[i, h] = sum_r 2^(m_r - M) part_o_r / sum_r 2^(m_r - M) l_r over the ranges
-hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- row kernels
 struct NormArgs {

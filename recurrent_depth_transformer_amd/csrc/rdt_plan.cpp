@@ -71,7 +71,7 @@ rdt_status validate_config(const rdt_config& c, std::string* why) {
 
 static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Plan make_plan(const rdt_config& c, int T) {
+Plan make_plan(const rdt_config& c, int T, int counters) {
   Plan p{};
   p.B = c.batch; p.S = c.seq; p.N = c.batch * c.seq; p.D = c.dim;
   p.H = c.n_heads; p.E = c.n_experts; p.Se = c.n_shared_experts; p.k = c.top_k;
@@ -114,7 +114,8 @@ Plan make_plan(const rdt_config& c, int T) {
   p.idx = take(N * p.k * 4);
   p.gates = take(N * p.k * 4);
   p.gap = take(N * 4);
-  p.cnt = take((size_t)2 * p.E * 4);          // two loops' counts, used alternately
+  p.att_cnt = counters;
+  p.cnt = take((size_t)(counters + 2 * p.E) * 4);  // counters, then two loops' counts (alternate loops)
   p.slot = take(N * p.k * 4);
   p.pcap = take((size_t)p.E * N * 4);
   p.hmid = take(N * (p.k + p.Se) * p.F * e);
@@ -152,7 +153,8 @@ Plan make_plan(const rdt_config& c, int T) {
 Plan make_decode_plan(const rdt_config& c, int T, int max_seq) {
   rdt_config d = c;
   d.seq = 1;
-  Plan p = make_plan(d, T);
+  const int att_split = max_seq / 128 < 1 ? 1 : (max_seq / 128 > 8 ? 8 : max_seq / 128);
+  Plan p = make_plan(d, T, att_split > 1 ? c.batch * c.n_heads : 0);
   size_t off = p.total;
   auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
   p.cosb = take((size_t)max_seq * (p.dr / 2) * 4);
@@ -160,7 +162,7 @@ Plan make_decode_plan(const rdt_config& c, int T, int max_seq) {
   p.rope_len = max_seq;
   // one workgroup per 128 cached positions, at most 8, per sequence and head
   // group (measured in place: 4 ranges for the gqa decode, 8 for the MLA one)
-  p.att_split = max_seq / 128 < 1 ? 1 : (max_seq / 128 > 8 ? 8 : max_seq / 128);
+  p.att_split = att_split;
   if (p.att_split > 1) {
     const size_t rows = (size_t)p.att_split * p.B * p.H;
     p.att_po = take(rows * p.dv * 4);

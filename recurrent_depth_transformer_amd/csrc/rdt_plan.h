@@ -36,6 +36,10 @@ struct Plan {
   // decode attention: key ranges per step and their partial results
   int att_split;
   size_t att_po, att_pm, att_pl;
+  // ints in front of the expert counts (cnt), cleared with them by the first
+  // RMSNorm of a call: decode attention counts finished key ranges per
+  // (sequence, head group) there, so the last range merges the partials
+  int att_cnt;
   size_t total;
 };
 
@@ -43,7 +47,7 @@ struct Plan {
 rdt_status validate_config(const rdt_config& c, std::string* why);
 
 // Layout for loop counts up to T (T >= 0). Requires a validated config.
-Plan make_plan(const rdt_config& c, int T);
+Plan make_plan(const rdt_config& c, int T, int counters = 0);
 // Plan of one decoding step: batch slots of one token each, RoPE tables for
 // max_seq positions.
 Plan make_decode_plan(const rdt_config& c, int T, int max_seq);
