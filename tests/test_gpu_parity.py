@@ -84,6 +84,32 @@ def test_end_to_end_forced(name):
         assert 0 < res["loops"].min() <= res["loops"].max() <= T
 
 
+# fp32 versions of the MLA, ACT (with depth-wise LoRA) and Dreamer workloads:
+# the fp32 attention (V transposed in LDS, no transpose reads), the fp32 GEMM
+# main loop with the LoRA second K phase, and the fp32 router and combine,
+# against the oracle at a tolerance fp32 arithmetic can meet.
+F32_VARIANTS = {
+    "mla_f32": dict(base="mla_small", dtype="f32"),
+    "act_f32": dict(base="act_small", dtype="f32"),
+    "dreamer_f32": dict(base="dreamer_small", dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(F32_VARIANTS))
+def test_fp32_variants_forced(name):
+    over = dict(F32_VARIANTS[name])
+    cfg = get_config(over.pop("base"), **over)
+    T = cfg["T"]
+    res, inp, *_ = run_gpu(cfg, T=T)
+    mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro)
+    ref = ro.forward(cfg, inp, T=T, forced_idx=res["route_idx"], forced_loops=res["loops"] if cfg["act"] else None)
+    err = np.max(np.abs(res["h"] - ref["h"]))
+    scale = rms(ref["h"])
+    _report(name, ratio=f"{err / scale:.3e}", route_mismatch=mism, near_ties=near, compared=comp)
+    assert mism == 0
+    assert err <= 1e-4 * scale
+
+
 # The limits of the block: the widest row (dim 4096: 16 float4 per lane and
 # more than one router k-chunk), the most routed experts (64) with top-8, the
 # pages' maximum of 16 loops, and a ragged sequence length. In bf16 over 16
