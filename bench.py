@@ -82,6 +82,18 @@ def flops_per_token_loop(cfg: dict) -> dict:
     return f
 
 
+def gate_up_kernel(cfg: dict) -> str:
+    """Name of the gate/up launch the library picks for this workload: fp32
+    128x128; bf16 64x64 under 64 rows per expert, 160x128 up to 128, else
+    192x128 (the tile rule of the library's host code)."""
+    if cfg["dtype"] == "f32":
+        return "k_grouped_gemm<f32,128,128,0,2,4>"
+    rows = cfg["batch"] * cfg["seq"] * cfg["top_k"] / cfg["n_experts"]
+    if rows < 64:
+        return "k_grouped_gemm<bf16,64,64,0,3,4>"
+    return "k_grouped_gemm<bf16,160,128,0,2,4>" if rows <= 128 else "k_grouped_gemm<bf16,192,128,0,2,4>"
+
+
 def gate_up_bytes(cfg: dict, counts_per_loop, elt: int) -> float:
     """Algorithmic HBM bytes of the grouped gate/up GEMM, averaged per launch:
     the gate and up matrices of every expert that received a row (and of every
@@ -270,8 +282,7 @@ def main():
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_from_profiles(args.workload),
-                "kernel": ("k_grouped_gemm<f32,128,128,0,2,4>" if cfg["dtype"] == "f32"
-                           else "k_grouped_gemm<bf16,192,128,0,2,4>") + " (expert gate/up + SwiGLU)",
+                "kernel": gate_up_kernel(cfg) + " (expert gate/up + SwiGLU)",
                 "avg_launch_us": round(gu_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(gu_bytes)}
 
     calibration = None if args.no_extras else machine_calibration(stream)

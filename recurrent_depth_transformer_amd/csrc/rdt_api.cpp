@@ -302,14 +302,18 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   // loop 0's expert counts are cleared by the first RMSNorm kernel; each
   // loop's combine clears the next loop's
   // Expert GEMM tiles (measured on MI355X): gate/up 192x128 with a two-stage
-  // ring (two workgroups per CU), or 64x64 with a three-stage ring when
+  // ring (two workgroups per CU); 160x128 when experts see 64-128 rows on
+  // average (one row tile still covers an expert 25 % above the average, and
+  // each CU that runs two tiles streams 10 % fewer bytes: gqa forward -2.4 %
+  // in place, while the large workloads were 1-2 % slower with it); or 64x64
+  // with a three-stage ring when
   // experts see under 64 rows (decode: narrow tiles give more workgroups;
   // 64x128 was 2-4 % slower per step); down 192x128 with a two-stage ring
   // when experts see many rows (measured in place: 0.3-1.5 % faster forwards
   // than 128x128), 64x32 for decode, else 64x64 with a three-stage ring.
   const long long rows_per_expert = (long long)N * k / E;
   const bool bf = dt == DT_BF16;
-  const int gu_bm = bf ? (rows_per_expert < 64 ? 64 : 192) : GU_BM;
+  const int gu_bm = bf ? (rows_per_expert < 64 ? 64 : rows_per_expert <= 128 ? 160 : 192) : GU_BM;
   const int gu_bn = bf && rows_per_expert < 64 ? 64 : GU_BN;
   const int dn_bm = (rows_per_expert >= 256 && bf) ? 128 : 64;
   // grid bound of a grouped GEMM with bm-row tiles: sum_e ceil(c_e / bm) over

@@ -713,7 +713,7 @@ static hipError_t grouped_dispatch(const GroupedGemm& g, hipStream_t s) {
     // at the register budget of two workgroups per CU; 128x128 needs more tiles)
 #define RDT_G(K, BM, BN, NS) \
     if (g.kind == K && g.bm == BM && g.bn == BN && g.ns == NS) return grouped_launch<T, BM, BN, K, NS>(g, s);
-    RDT_G(0, 64, 64, 3) RDT_G(0, 128, 128, 2) RDT_G(0, 192, 128, 2)
+    RDT_G(0, 64, 64, 3) RDT_G(0, 128, 128, 2) RDT_G(0, 160, 128, 2) RDT_G(0, 192, 128, 2)
     RDT_G(1, 64, 32, 3) RDT_G(1, 64, 64, 3) RDT_G(1, 64, 64, 4) RDT_G(1, 192, 128, 2)
 #undef RDT_G
     return hipErrorInvalidValue;
