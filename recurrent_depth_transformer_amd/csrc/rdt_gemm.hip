@@ -566,7 +566,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
   // shared: n rows) owns ceil(rows / BM) consecutive m-tiles. The grid is
   // sized for the worst case; only the first total_mt * ntn blocks have a
   // tile. Those are spread over the XCDs by dispatch order, and each XCD's
-  // share is remapped to consecutive tiles (shared A rows in L2).
+  // share is remapped to consecutive tiles (an order chosen below).
   const int lane = threadIdx.x & 63;
   auto rows_of = [&](int gg) { return gg < G ? (gg < g.E ? g.cnt[gg] : n) : 0; };
   auto scan = [&](int v) {  // inclusive prefix sum over the wave
@@ -582,24 +582,39 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
   const int nb = total_mt * ntn;
   if ((int)blockIdx.x >= nb) return;
   const int L = xcd_remap(blockIdx.x, nb);
-  const int mt = L / ntn, nt = L % ntn;  // consecutive tiles share the A rows
+  const int q = L / ntn;  // expert of tile L: the one whose m-tiles hold q
   // this tile's expert, its first tile and the first output row of its rows
-  int grp = -1, tstart = 0, rbase = 0;
+  int grp = -1, tstart = 0, rbase = 0, tlg = 1;
   for (int b0 = 0, ct = 0, cr = 0; b0 < G && grp < 0; b0 += 64) {
     const int gg = b0 + lane, rows = rows_of(gg), tl = (rows + BM - 1) / BM;
     const int it = scan(tl), ir = scan(gg < g.E ? rows : 0);
     const int end = ct + it;
-    const unsigned long long hit = __ballot(gg < G && mt >= end - tl && mt < end);
+    const unsigned long long hit = __ballot(gg < G && q >= end - tl && q < end);
     if (hit) {
       const int w = __ffsll((long long)hit) - 1;
       grp = b0 + w;
       tstart = __shfl(end - tl, w, 64);
+      tlg = __shfl(tl, w, 64);
       rbase = cr + __shfl(ir - (gg < g.E ? rows : 0), w, 64);
     }
     ct += __shfl(it, 63, 64);
     cr += __shfl(ir, 63, 64);
   }
   grp = __builtin_amdgcn_readfirstlane(grp);
+  // Order of an expert's tiles [tstart * ntn, (tstart + tlg) * ntn) in L.
+  // 64-row down tiles (an expert has few rows, hence few m-tiles): m-tiles
+  // innermost, so the m-tiles that stream one weight slab run side by side on
+  // one XCD and share it in L2. Otherwise n-tiles innermost: consecutive tiles
+  // share the A rows.
+  int mt, nt;
+  if constexpr (KIND == 1 && BM == 64) {
+    const int r = L - tstart * ntn;
+    nt = r / tlg;
+    mt = tstart + r % tlg;
+  } else {
+    mt = q;
+    nt = L % ntn;
+  }
   const bool routed = grp < g.E;
   const int rows_g = routed ? g.cnt[grp] : n;
   const int pbase = routed ? rbase : n * g.k + (grp - g.E) * n;
