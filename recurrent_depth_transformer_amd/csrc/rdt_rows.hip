@@ -101,15 +101,58 @@ hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
 // ---------------------------------------------------------- combine + inject
 // m = sum_j gate_j * Y[inv_j] + sum_s Y_shared_s;  h = A*h + B*e + a + m
 // ACT: cum += sigmoid(w . h); loops = t + 1.
-// All column vectors of a row are handled at once (NV float4 per lane), so the
-// expert-output gathers of every column are in flight together; the next
-// loop's RMSNorm works from the registers that hold h' + e.
-template <typename T, int NV>
+// One wave per row, all column vectors of the row at once (NV float4 per
+// lane), so the expert-output gathers of every column are in flight together;
+// the next loop's RMSNorm works from the registers that hold h' + e.
+// LAT (launches of a few hundred rows, where latency and not bandwidth sets
+// the time): the loads that need no expert offsets (routing entries; h, e, a
+// for rows of up to 1024 columns) are issued before the count scan, the
+// routed outputs are gathered two experts at a time, and lanes past D load
+// column 0 (never stored) so that no load sits behind a per-column branch.
+// This takes 2-3 times the registers, which costs occupancy on long launches.
+// Both forms add the same terms in the same order.
+template <typename T, int NV, bool LAT>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  constexpr bool PRE = LAT && NV <= 4;  // h, e, a ahead of the scan (registers)
+  constexpr int KP = LAT ? 8 : 0;       // routing entries fetched ahead
+  constexpr int KA = KP > 0 ? KP : 1;
   __shared__ int s_off[MAX_EXPERTS];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave;
   const int n = a.ndev ? *a.ndev : a.n;
+  const bool live = i < n;
+  const int D = a.D, k = a.k;
+  int colc[NV];
+  bool okc[NV];
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    const int col = (c * 64 + lane) * 4;
+    okc[c] = col < D;
+    colc[c] = okc[c] ? col : 0;
+  }
+  const int tok = live ? (a.rows ? a.rows[i] : i) : 0;
+  int eidx[KA], eslot[KA];
+  float egt[KA];
+  float4 hv[NV], ev[NV], av[NV];
+#pragma unroll
+  for (int j = 0; j < KA; ++j) { eidx[j] = 0; eslot[j] = 0; egt[j] = 0.f; }
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < KP; ++j)
+      if (j < k) {
+        eidx[j] = a.idx[(long long)i * k + j];
+        eslot[j] = a.slot[(long long)i * k + j];
+        egt[j] = a.gates[(long long)i * k + j];
+      }
+    if constexpr (PRE) {
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        hv[c] = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + colc[c]);
+        ev[c] = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + colc[c]);
+        av[c] = *reinterpret_cast<const float4*>(a.a + (long long)i * D + colc[c]);
+      }
+    }
+  }
   // exclusive prefix of the per-expert counts (wave 0, one lane per expert)
   if (wave == 0) {
     const int c = lane < a.E ? a.cnt[lane] : 0;
@@ -126,9 +169,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     }
   }
   __syncthreads();
-  if (i >= n) return;
-  const int tok = a.rows ? a.rows[i] : i;
-  const int D = a.D, k = a.k;
+  if (!live) return;
   const T* Y = reinterpret_cast<const T*>(a.Y);
   // expert output row p, columns col..col+3: stored values, or the sum of the
   // K-slice partials in slice order
@@ -147,15 +188,56 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   float m[NV][4];
 #pragma unroll
   for (int c = 0; c < NV; ++c) m[c][0] = m[c][1] = m[c][2] = m[c][3] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int p = s_off[a.idx[(long long)i * k + j]] + a.slot[(long long)i * k + j];
+  // routed experts in pairs (the second of a pair may repeat the first row
+  // and is then not added); each element adds its experts in choice order
+#pragma unroll
+  for (int j0 = 0; j0 < KP; j0 += 2) {
+    if (j0 >= k) break;
+    const bool two = j0 + 1 < k;
+    const long long p0 = s_off[eidx[j0]] + eslot[j0];
+    const long long p1 = two ? s_off[eidx[j0 + 1]] + eslot[j0 + 1] : p0;
+    float y0[NV][4], y1[NV][4];
+    if (a.ksplit == 2) {
+      float4 u0[NV], u1[NV], w0[NV], w1[NV];
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        u0[c] = *reinterpret_cast<const float4*>(a.Yp + p0 * D + colc[c]);
+        u1[c] = *reinterpret_cast<const float4*>(a.Yp + a.ystride + p0 * D + colc[c]);
+        w0[c] = *reinterpret_cast<const float4*>(a.Yp + p1 * D + colc[c]);
+        w1[c] = *reinterpret_cast<const float4*>(a.Yp + a.ystride + p1 * D + colc[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        y0[c][0] = u0[c].x + u1[c].x; y0[c][1] = u0[c].y + u1[c].y;
+        y0[c][2] = u0[c].z + u1[c].z; y0[c][3] = u0[c].w + u1[c].w;
+        y1[c][0] = w0[c].x + w1[c].x; y1[c][1] = w0[c].y + w1[c].y;
+        y1[c][2] = w0[c].z + w1[c].z; y1[c][3] = w0[c].w + w1[c].w;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        yrow(p0, colc[c], y0[c]);
+        yrow(p1, colc[c], y1[c]);
+      }
+    }
+    const float g0 = egt[j0], g1 = egt[j0 + 1 < KA ? j0 + 1 : j0];
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      m[c][0] += g0 * y0[c][0]; m[c][1] += g0 * y0[c][1]; m[c][2] += g0 * y0[c][2]; m[c][3] += g0 * y0[c][3];
+      if (two) {
+        m[c][0] += g1 * y1[c][0]; m[c][1] += g1 * y1[c][1]; m[c][2] += g1 * y1[c][2]; m[c][3] += g1 * y1[c][3];
+      }
+    }
+  }
+  // (outside LAT, loads stay behind per-column guards: fewer registers live)
+  for (int j = KP; j < k; ++j) {
+    const long long p = s_off[a.idx[(long long)i * k + j]] + a.slot[(long long)i * k + j];
     const float gt = a.gates[(long long)i * k + j];
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
-      const int col = (c * 64 + lane) * 4;
-      if (col < D) {
+      if (LAT || okc[c]) {
         float y[4];
-        yrow(p, col, y);
+        yrow(p, colc[c], y);
         m[c][0] += gt * y[0]; m[c][1] += gt * y[1]; m[c][2] += gt * y[2]; m[c][3] += gt * y[3];
       }
     }
@@ -165,10 +247,9 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     const long long p = (long long)n * k + (long long)s * n + i;
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
-      const int col = (c * 64 + lane) * 4;
-      if (col < D) {
+      if (LAT || okc[c]) {
         float y[4];
-        yrow(p, col, y);
+        yrow(p, colc[c], y);
         m[c][0] += sw * y[0]; m[c][1] += sw * y[1]; m[c][2] += sw * y[2]; m[c][3] += sw * y[3];
       }
     }
@@ -176,31 +257,32 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   float z = 0.f, ss = 0.f;
 #pragma unroll
   for (int c = 0; c < NV; ++c) {
-    const int col = (c * 64 + lane) * 4;
-    if (col >= D) continue;
+    if (!okc[c]) continue;
+    const int col = colc[c];
+    if constexpr (!PRE) {
+      hv[c] = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + col);
+      ev[c] = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
+      av[c] = *reinterpret_cast<const float4*>(a.a + (long long)i * D + col);
+    }
     if (a.d) {
       const float4 dv = *reinterpret_cast<const float4*>(a.d + (long long)i * D + col);
       m[c][0] += dv.x; m[c][1] += dv.y; m[c][2] += dv.z; m[c][3] += dv.w;
     }
-    float* hp = a.h + (long long)tok * D + col;
-    const float4 hv = *reinterpret_cast<const float4*>(hp);
-    const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
-    const float4 av = *reinterpret_cast<const float4*>(a.a + (long long)i * D + col);
     const float4 Av = *reinterpret_cast<const float4*>(a.A + col);
     const float4 Bv = *reinterpret_cast<const float4*>(a.B + col);
     float4 hn;
-    hn.x = Av.x * hv.x + Bv.x * ev.x + av.x + m[c][0];
-    hn.y = Av.y * hv.y + Bv.y * ev.y + av.y + m[c][1];
-    hn.z = Av.z * hv.z + Bv.z * ev.z + av.z + m[c][2];
-    hn.w = Av.w * hv.w + Bv.w * ev.w + av.w + m[c][3];
-    *reinterpret_cast<float4*>(hp) = hn;
-    if (a.a_dump) *reinterpret_cast<float4*>(a.a_dump + (long long)tok * D + col) = av;
+    hn.x = Av.x * hv[c].x + Bv.x * ev[c].x + av[c].x + m[c][0];
+    hn.y = Av.y * hv[c].y + Bv.y * ev[c].y + av[c].y + m[c][1];
+    hn.z = Av.z * hv[c].z + Bv.z * ev[c].z + av[c].z + m[c][2];
+    hn.w = Av.w * hv[c].w + Bv.w * ev[c].w + av[c].w + m[c][3];
+    *reinterpret_cast<float4*>(a.h + (long long)tok * D + col) = hn;
+    if (a.a_dump) *reinterpret_cast<float4*>(a.a_dump + (long long)tok * D + col) = av[c];
     if (a.act) {
       const float4 wv = *reinterpret_cast<const float4*>(a.w_halt + col);
       z += wv.x * hn.x + wv.y * hn.y + wv.z * hn.z + wv.w * hn.w;
     }
     // u = h' + e for the next loop's first RMSNorm
-    m[c][0] = hn.x + ev.x; m[c][1] = hn.y + ev.y; m[c][2] = hn.z + ev.z; m[c][3] = hn.w + ev.w;
+    m[c][0] = hn.x + ev[c].x; m[c][1] = hn.y + ev[c].y; m[c][2] = hn.z + ev[c].z; m[c][3] = hn.w + ev[c].w;
     ss += m[c][0] * m[c][0] + m[c][1] * m[c][1] + m[c][2] * m[c][2] + m[c][3] * m[c][3];
   }
   if (a.n1_out) {
@@ -209,8 +291,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     T* dst = reinterpret_cast<T*>(a.n1_out) + (long long)tok * D;
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
-      const int col = (c * 64 + lane) * 4;
-      if (col >= D) continue;
+      if (!okc[c]) continue;
+      const int col = colc[c];
       const float4 gv = *reinterpret_cast<const float4*>(a.g1 + col);
       float y[4] = {m[c][0] * inv * gv.x, m[c][1] * inv * gv.y, m[c][2] * inv * gv.z, m[c][3] * inv * gv.w};
       store4<T>(dst + col, y);
@@ -228,16 +310,22 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   if (lane == 0 && a.loops) a.loops[tok] = a.t + 1;
 }
 
-template <typename T>
-static hipError_t combine_t(const CombineArgs& a, hipStream_t s) {
+template <typename T, bool LAT>
+static hipError_t combine_nv(const CombineArgs& a, hipStream_t s) {
   dim3 grid((a.n + 3) / 4);
   const int nv = (a.D + 255) / 256;
-  if (nv <= 1) hipLaunchKernelGGL((k_combine<T, 1>), grid, dim3(256), 0, s, a);
-  else if (nv <= 2) hipLaunchKernelGGL((k_combine<T, 2>), grid, dim3(256), 0, s, a);
-  else if (nv <= 4) hipLaunchKernelGGL((k_combine<T, 4>), grid, dim3(256), 0, s, a);
-  else if (nv <= 8) hipLaunchKernelGGL((k_combine<T, 8>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_combine<T, 16>), grid, dim3(256), 0, s, a);
+  if (nv <= 1) hipLaunchKernelGGL((k_combine<T, 1, LAT>), grid, dim3(256), 0, s, a);
+  else if (nv <= 2) hipLaunchKernelGGL((k_combine<T, 2, LAT>), grid, dim3(256), 0, s, a);
+  else if (nv <= 4) hipLaunchKernelGGL((k_combine<T, 4, LAT>), grid, dim3(256), 0, s, a);
+  else if (nv <= 8) hipLaunchKernelGGL((k_combine<T, 8, LAT>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_combine<T, 16, LAT>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t combine_t(const CombineArgs& a, hipStream_t s) {
+  // up to 2048 rows (512 workgroups, one round on the chip at LAT's occupancy)
+  return a.n <= 2048 ? combine_nv<T, true>(a, s) : combine_nv<T, false>(a, s);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
