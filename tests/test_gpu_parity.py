@@ -195,6 +195,21 @@ def test_k_sliced_down_projection():
     assert err <= TOL * rms(ref["h"])
 
 
+def test_combine_odd_and_long_top_k():
+    """Top-11 of 16 experts with two K slices: the combine gathers the first
+    eight choices in pairs and the rest one at a time, and the last pair has
+    one member (odd k). End to end against the oracle."""
+    cfg = get_config("gqa_small", n_experts=16, top_k=11, expert_dim=2112)
+    T = cfg["T"]
+    res, inp, *_ = run_gpu(cfg, T=T)
+    mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro)
+    ref = ro.forward(cfg, inp, T=T, forced_idx=res["route_idx"])
+    err = np.max(np.abs(res["h"] - ref["h"]))
+    _report("top11_of_16", ratio=f"{err / rms(ref['h']):.3e}", route_mismatch=mism, near_ties=near)
+    assert mism == 0
+    assert err <= TOL * rms(ref["h"])
+
+
 def test_act_zero_halting_vector_halts_after_two_loops():
     """w = 0 gives p = 1/2 every loop: the cumulative sum reaches 1.0 >= 0.99
     at the second loop, so every token runs exactly two loops whatever T."""
