@@ -196,10 +196,11 @@ def test_k_sliced_down_projection():
 
 
 def test_combine_odd_and_long_top_k():
-    """Top-11 of 16 experts with two K slices: the combine gathers the first
-    eight choices in pairs and the rest one at a time, and the last pair has
-    one member (odd k). End to end against the oracle."""
-    cfg = get_config("gqa_small", n_experts=16, top_k=11, expert_dim=2112)
+    """Top-11 of 16 experts plus a shared expert, with two K slices: the
+    combine gathers the first eight choices in pairs and the rest one at a
+    time, the last pair has one member (odd k), and the shared expert's two
+    slices are added after them. End to end against the oracle."""
+    cfg = get_config("gqa_small", n_experts=16, top_k=11, expert_dim=2112, n_shared_experts=1)
     T = cfg["T"]
     res, inp, *_ = run_gpu(cfg, T=T)
     mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro)
