@@ -6,15 +6,17 @@ One step = one rdt_recurrent_forward: the whole T-loop of the recurrent block
 combine + LTI injection) over one batch of seeded synthetic inputs that are
 already resident in HBM, replayed as a captured HIP graph.
 
-Default workload: the GQA recurrent block -- batch 1, seq 512, dim 1024, 16/4
-heads of 64, 8 experts top-2 with SwiGLU hidden 2816, T = 3, bf16 weights and
-activations with fp32 accumulation and fp32 state.
+Default workload (the largest recurrent-block configuration that fits one GPU):
+wide_moe -- batch 2, seq 4096, dim 2048, GQA 16/4 heads of 128, 64 routed
+experts top-8 plus one shared expert with SwiGLU hidden 1024, T = 16, bf16
+weights and activations with fp32 accumulation and fp32 state.
 
-Prints one JSON line. `value` is token-loops per second (batch*seq*T tokens
-through one loop each, per forward); `roofline` describes the dominant kernel
-(the grouped gate/up expert GEMM), timed with HIP events around its launches on
-the stream they run on; `cpu_baseline` times the float64 CPU oracle on the
-host's cores.
+Prints one JSON line. `value` is token-loops per second (tokens through one
+loop each, per forward); `roofline` describes the dominant kernel (the grouped
+gate/up expert GEMM, MFMA-bound), timed with HIP events around its launches on
+the stream they run on; `kernels` gives the same for the other kernels (the
+router and the combine against HBM bandwidth); `extras` measures the other
+workloads; `cpu_baseline` times the float64 CPU oracle on the host's cores.
 """
 from __future__ import annotations
 
@@ -155,40 +157,295 @@ def traffic_from_profiles(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg: dict, inputs: dict, T: int, budget_s: float):
-    """Time the float64 CPU oracle on this host (repeats of the full forward
-    until the budget is used, at least one)."""
-    import numpy as np  # noqa: F401
-    from oracle import rdt_oracle
+def gate_up_flops(cfg: dict, counts_per_loop) -> float:
+    """Algorithmic FLOPs of the grouped gate/up GEMM, averaged per launch: every
+    routed row and every shared-expert row costs gate and up projections,
+    2 * 2 * D * F."""
+    D, F = cfg["dim"], cfg["expert_dim"]
+    tot = 0.0
+    for counts in counts_per_loop:
+        rows = int(sum(counts))
+        tot += 4.0 * D * F * (rows + cfg["n_shared_experts"] * (rows // cfg["top_k"]))
+    return tot / max(1, len(counts_per_loop))
+
+
+def down_flops(cfg: dict, counts_per_loop) -> float:
+    """Algorithmic FLOPs of the grouped down projection per launch (2 * D * F per row)."""
+    return gate_up_flops(cfg, counts_per_loop) / 2.0
+
+
+def active_rows(cfg: dict, counts_per_loop):
+    """Tokens that ran each loop (routed rows / top-k)."""
+    return [int(sum(c)) // cfg["top_k"] for c in counts_per_loop]
+
+
+def router_bytes(cfg: dict, counts_per_loop, elt: int) -> float:
+    """Algorithmic HBM bytes of the fused second RMSNorm + router launch per
+    loop, averaged: per running token it reads h, e and the attention-branch
+    output a (float32), writes n2 (storage type), and writes k expert indices,
+    gates and slots (int32/float32) plus the top-k gap (float32); the router
+    weights E x D are read once."""
+    D, E, k = cfg["dim"], cfg["n_experts"], cfg["top_k"]
+    extra = 4 * D if cfg.get("da_heads") and not cfg.get("parallel") else 0   # depth-attention output
+    tot = 0.0
+    for n in active_rows(cfg, counts_per_loop):
+        tot += n * (12 * D + extra + elt * D + 12 * k + 4) + E * D * elt
+    return tot / max(1, len(counts_per_loop))
+
+
+def combine_bytes(cfg: dict, counts_per_loop, elt: int, ksplit: int = 1) -> float:
+    """Algorithmic HBM bytes of the combine + injection launch per loop,
+    averaged: per running token it reads h, e, a (float32), its k routed
+    expert outputs and the shared experts' outputs (storage type, or float32
+    partial sums per K slice), and its k indices, slots and gates; it writes h'
+    (float32) and the next loop's RMSNorm(h' + e) (storage type; not after the
+    last loop); with ACT it reads and writes the halting sum."""
+    D, k, Se, T = cfg["dim"], cfg["top_k"], cfg["n_shared_experts"], len(counts_per_loop)
+    ybytes = D * (k + Se) * (4 * ksplit if ksplit > 1 else elt)
+    tot = 0.0
+    for t, n in enumerate(active_rows(cfg, counts_per_loop)):
+        per = 12 * D + ybytes + 12 * k + 4 * D + (elt * D if t + 1 < T else 0) + (8 if cfg["act"] else 0)
+        if cfg.get("da_heads"):
+            per += 4 * D
+        tot += n * per
+    return tot / max(1, T)
+
+
+def source_hash(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "recurrent_depth_transformer_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """Per-launch HBM bytes of the dominant kernel from committed rocprofv3
+    counter runs, or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"expert_gate_up_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != source_hash(DOMINANT_SOURCES):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def host_info() -> dict:
+    """Threads the BLAS pools use, the CPU model and the BLAS library."""
+    info = {"cpu_count": os.cpu_count(), "cpu_model": None, "blas": None, "threads": os.cpu_count() or 1}
     try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        import numpy as np
         from threadpoolctl import threadpool_info
-        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    runs, t_used = 0, 0.0
-    while runs == 0 or (t_used < budget_s and runs < 50):
-        t0 = time.perf_counter()
-        rdt_oracle.forward(cfg, inputs, T=T)
-        t_used += time.perf_counter() - t0
-        runs += 1
+        np.ones((2, 2)) @ np.ones((2, 2))
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            info["threads"] = max(int(p.get("num_threads", 1)) for p in pools)
+            info["blas"] = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in pools)
+    except Exception:
+        pass
+    return info
+
+
+def cpu_baseline(cfg: dict, inputs: dict) -> dict:
+    """Time the float64 CPU oracle on this host: one loop (T = 1) of the
+    workload over every token (a bounded sample of the T-loop; token-loops per
+    second do not depend on the loop index)."""
+    from oracle import rdt_oracle
+    hi = host_info()
     N = cfg["batch"] * cfg["seq"]
-    return {"value": N * T * runs / t_used, "unit": "token-loops/s", "cores": threads, "kind": "oracle",
-            "sample": f"{runs} full forward(s) of the {cfg['name']} workload (T={T}, {N} tokens) in float64 "
-                      f"NumPy, {t_used:.1f} s"}
+    t0 = time.perf_counter()
+    rdt_oracle.forward(cfg, inputs, T=1)
+    dt = time.perf_counter() - t0
+    return {"value": round(N / dt, 1), "unit": "token-loops/s", "cores": hi["threads"], "kind": "oracle",
+            "sample": f"one loop (T=1) of the {cfg['name']} workload over all {N} tokens in float64 NumPy, "
+                      f"{dt:.1f} s",
+            "cpu_model": hi["cpu_model"], "cpu_count": hi["cpu_count"], "blas": hi["blas"]}
+
+
+def unforced_routing(cfg: dict, inputs: dict, route_idx, h_gpu, P: int = 64) -> dict:
+    """For information: the float64 oracle run unforced on the first P
+    positions of sequence 0 (causal, so they do not depend on later ones)
+    against the GPU's routing of the same tokens: the share of (token, loop)
+    pairs whose expert set differs, and max|dh_T| / RMS over the tokens whose
+    routing never differed."""
+    import numpy as np
+    from oracle import rdt_oracle
+    T = route_idx.shape[0]
+    sub = dict(inputs)
+    sub["e"], sub["h0"] = inputs["e"][:P], inputs["h0"][:P]
+    ref = rdt_oracle.forward(dict(cfg, batch=1, seq=P), sub, T=T, record=True)
+    flips = np.zeros(P, bool)
+    pairs = 0
+    for t in range(T):
+        go, gg = ref["idx"][t], route_idx[t][:P]
+        run = (go[:, 0] >= 0) & (gg[:, 0] >= 0)
+        diff = run & ~np.all(np.sort(go, 1) == np.sort(gg, 1), axis=1)
+        flips |= diff
+        pairs += int(np.sum(diff))
+    hT = ref["h"][-1]
+    keep = ~flips
+    scale = float(np.sqrt(np.mean(hT ** 2)))
+    dev = float(np.max(np.abs(h_gpu[:P][keep] - hT[keep]))) / scale if keep.any() else None
+    return {"tokens": P, "loops": T, "flip_rate": round(pairs / (P * T), 5),
+            "tokens_ever_flipped": int(flips.sum()),
+            "max_dh_over_rms_unflipped": None if dev is None else round(dev, 6)}
+
+
+def _time(fn, steps: int, warmup: int, stream) -> float:
+    """Mean milliseconds of fn() over `steps` calls after `warmup` calls,
+    HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+class Run:
+    """One workload on the device: weights, a graph-mode block, its workspace,
+    and one forward with the per-loop counts (and routing dumps) recorded."""
+
+    def __init__(self, name: str, routing_dumps: bool = False):
+        import torch
+
+        import recurrent_depth_transformer_amd as rdt
+        from rdt_inputs import get_config, make_inputs
+        self.cfg = cfg = get_config(name)
+        self.T, self.N = cfg["T"], cfg["batch"] * cfg["seq"]
+        self.inputs = make_inputs(cfg)
+        self.W = rdt.device_weights(self.inputs, cfg, "cuda")
+        self.blk = rdt.RecurrentBlock(cfg, graph=True)
+        self.out = torch.empty_like(self.W["h0"])
+        self.ws = self.blk.workspace(self.T)
+        self.stream = torch.cuda.current_stream()
+        T, N = self.T, self.N
+        aux = {"loops": torch.empty(N, dtype=torch.int32, device="cuda"),
+               "expert_counts": torch.empty(T, cfg["n_experts"], dtype=torch.int32, device="cuda")}
+        if routing_dumps:
+            aux["route_idx"] = torch.empty(T, N, cfg["top_k"], dtype=torch.int32, device="cuda")
+            aux["route_gap"] = torch.empty(T, N, dtype=torch.float32, device="cuda")
+        self.blk.forward(self.W["h0"], self.W["e"], self.W, T=T, out=self.out, workspace=self.ws, aux=aux)
+        torch.cuda.synchronize()
+        self.executed = int(aux["loops"].sum().item())
+        self.counts = aux["expert_counts"].cpu().numpy()
+        self.route_idx = aux["route_idx"].cpu().numpy() if routing_dumps else None
+        self.route_gap = aux["route_gap"].cpu().numpy() if routing_dumps else None
+        self.h = self.out.cpu().numpy() if routing_dumps else None
+
+    def step(self):
+        self.blk.forward(self.W["h0"], self.W["e"], self.W, T=self.T, out=self.out, workspace=self.ws)
+
+    def stages(self, n: int) -> dict:
+        """{stage: (mean device ms per launch, launches per forward)} from n
+        kernel-by-kernel forwards with HIP events around every launch."""
+        acc = {}
+        for _ in range(max(1, n)):
+            _, st = self.blk.profile_forward(self.W["h0"], self.W["e"], self.W, T=self.T, out=self.out,
+                                             workspace=self.ws)
+            for k, (t_ms, c) in st.items():
+                a = acc.setdefault(k, [0.0, 0])
+                a[0] += t_ms
+                a[1] += c
+        return {k: (v[0] / v[1] if v[1] else 0.0, v[1] // max(1, n)) for k, v in acc.items()}
+
+
+def kernel_figures(cfg: dict, counts, stage_avg: dict, elt: int, peak_tf: float) -> dict:
+    """Per-kernel roofline figures from the per-stage launch times: the GEMMs
+    and attention against the MFMA peak, the router and combine against HBM."""
+    fl = flops_per_token_loop(cfg)
+    rows = active_rows(cfg, counts)
+    mean_rows = sum(rows) / max(1, len(rows))
+    out = {}
+
+    def mfma(stage, flops):
+        us = stage_avg.get(stage, (0.0, 0))[0] * 1e3
+        if us <= 0:
+            return
+        out[stage] = {"bound": "mfma", "avg_launch_us": round(us, 2), "algorithmic_flops_per_launch": int(flops),
+                      "achieved_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+                      "frac": round(flops / (us * 1e-6) / 1e12 / peak_tf, 4)}
+
+    def hbm(stage, nbytes):
+        us = stage_avg.get(stage, (0.0, 0))[0] * 1e3
+        if us <= 0:
+            return
+        out[stage] = {"bound": "hbm", "avg_launch_us": round(us, 2), "algorithmic_bytes_per_launch": int(nbytes),
+                      "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    mfma("expert_gate_up", gate_up_flops(cfg, counts))
+    mfma("expert_down", down_flops(cfg, counts))
+    n_qkv = max(1, stage_avg.get("qkv", (0, 1))[1] // max(1, len(counts)))
+    mfma("qkv", fl["qkv"] * mean_rows / n_qkv)
+    mfma("attention", fl["attention"] * mean_rows)
+    mfma("out_proj", fl["out_proj"] * mean_rows)
+    hbm("router", router_bytes(cfg, counts, elt))
+    hbm("combine", combine_bytes(cfg, counts, elt, ksplit_of(cfg)))
+    return out
+
+
+def ksplit_of(cfg: dict) -> int:
+    """K slices of the down projection the library picks (bf16: at most 32
+    64-wide stages per slice; fp32 does not slice)."""
+    if cfg["dtype"] == "f32":
+        return 1
+    stages = (cfg["expert_dim"] + 63) // 64
+    return (stages + 31) // 32
+
+
+def measure_extra(name: str, steps: int, stream) -> dict:
+    """Forward throughput of another workload and its per-kernel figures."""
+    r = Run(name)
+    ms = _time(r.step, steps, 3, r.stream)
+    st = r.stages(2)
+    elt = 4 if r.cfg["dtype"] == "f32" else 2
+    peak = PEAK_F32_TFLOPS if r.cfg["dtype"] == "f32" else PEAK_BF16_TFLOPS
+    flops = sum(flops_per_token_loop(r.cfg).values()) * r.executed
+    res = {"workload": describe(r.cfg), "ms_per_step": round(ms, 4), "value": round(r.executed / (ms * 1e-3), 1),
+           "unit": "token-loops/s", "token_loops_per_step": r.executed,
+           "mfma_peak_frac": round(flops / (ms * 1e-3) / (peak * 1e12), 5),
+           "kernels": kernel_figures(r.cfg, r.counts, st, elt, peak),
+           "stages_us": {k: round(v[0] * 1e3, 2) for k, v in st.items() if v[1]}}
+    if r.cfg["act"]:
+        res["nominal_token_loops_per_step"] = r.N * r.T
+    if r.cfg.get("da_heads"):
+        da_us = st["depth_attention"][0] * 1e3
+        nbytes = depth_attention_bytes(r.cfg, elt)
+        achieved = nbytes / (da_us * 1e-6) / 1e9
+        res["depth_attention"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                                  "avg_launch_us": round(da_us, 2), "algorithmic_bytes_per_launch": int(nbytes)}
+    del r
+    return res
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gqa")
-    ap.add_argument("--profile-steps", type=int, default=10, help="eager forwards timed per stage")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wide_moe")
+    ap.add_argument("--profile-steps", type=int, default=4, help="eager forwards timed per stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also print the per-stage breakdown to stderr")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the decode-step and depth-attention (dreamer workload) measurements")
+                    help="skip the other workloads, the decode step and the machine calibration")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (calibrates HBM counters) and exit")
     args = ap.parse_args()
@@ -209,50 +466,34 @@ def main():
     import numpy as np
     import torch
 
-    import recurrent_depth_transformer_amd as rdt
-    from rdt_inputs import get_config, make_inputs
-
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    cfg = get_config(args.workload)
-    T, N = cfg["T"], cfg["batch"] * cfg["seq"]
-    inputs = make_inputs(cfg)
-    W = rdt.device_weights(inputs, cfg, "cuda")
-    blk = rdt.RecurrentBlock(cfg, graph=True)
-    out = torch.empty_like(W["h0"])
-    ws = blk.workspace(T)
-    stream = torch.cuda.current_stream()
+    run = Run(args.workload, routing_dumps=True)
+    cfg, T, N = run.cfg, run.T, run.N
+    stream = run.stream
     print(f"[bench] {describe(cfg)}; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
 
-    # executed token-loops (ACT halts tokens early) and per-loop expert counts
-    loops = torch.empty(N, dtype=torch.int32, device="cuda")
-    counts = torch.empty(T, cfg["n_experts"], dtype=torch.int32, device="cuda")
-    blk.forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws, aux={"loops": loops, "expert_counts": counts})
-    torch.cuda.synchronize()
-    executed = int(loops.sum().item())
-    counts_np = counts.cpu().numpy()
-
     for _ in range(args.warmup):
-        blk.forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws)
+        run.step()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        blk.forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws)
+        run.step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
-    value = executed / (ms * 1e-3)
+    value = run.executed / (ms * 1e-3)
     print(f"[bench] {ms:.4f} ms per forward (wall {wall * 1e3 / args.steps:.4f} ms)", file=sys.stderr, flush=True)
     # spread of single steps (an event pair around each forward, after the timed run)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a_, b_ in evs:
         a_.record(stream)
-        blk.forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws)
+        run.step()
         b_.record(stream)
     torch.cuda.synchronize()
     single = np.array([a_.elapsed_time(b_) for a_, b_ in evs])
@@ -261,40 +502,44 @@ def main():
 
     # per-stage device time: kernels launched one by one with HIP events around
     # each launch on the launch stream
-    acc = {}
-    for _ in range(max(1, args.profile_steps)):
-        _, st = blk.profile_forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws)
-        for k, (t_ms, n) in st.items():
-            a = acc.setdefault(k, [0.0, 0])
-            a[0] += t_ms
-            a[1] += n
-    stage_avg = {k: (v[0] / v[1] if v[1] else 0.0, v[1] // max(1, args.profile_steps)) for k, v in acc.items()}
+    stage_avg = run.stages(args.profile_steps)
     if args.stages:
         for k, (avg, n) in stage_avg.items():
             print(f"[stage] {k:16s} {avg * 1e3:9.2f} us/launch x {n}", file=sys.stderr)
 
     elt = 4 if cfg["dtype"] == "f32" else 2
     fl = flops_per_token_loop(cfg)
-    flops = sum(fl.values()) * executed
+    flops = sum(fl.values()) * run.executed
     peak_tf = PEAK_F32_TFLOPS if cfg["dtype"] == "f32" else PEAK_BF16_TFLOPS
-    gu_ms = stage_avg[DOMINANT_STAGE][0]
-    gu_bytes = gate_up_bytes(cfg, counts_np, elt)
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_from_profiles(args.workload),
+    kernels = kernel_figures(cfg, run.counts, stage_avg, elt, peak_tf)
+    gu = kernels[DOMINANT_STAGE]
+    roofline = {"bound": "mfma", "achieved": gu["achieved_TFLOPs"], "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": gu["frac"], "traffic": traffic_from_profiles(args.workload),
                 "kernel": gate_up_kernel(cfg) + " (expert gate/up + SwiGLU)",
-                "avg_launch_us": round(gu_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(gu_bytes)}
+                "avg_launch_us": gu["avg_launch_us"], "algorithmic_flops_per_launch": gu["algorithmic_flops_per_launch"],
+                "algorithmic_bytes_per_launch": int(gate_up_bytes(cfg, run.counts, elt))}
+    gaps = run.route_gap
+    routing = {"near_ties_per_loop": [int(np.sum(gaps[t][np.isfinite(gaps[t])] < 1e-3)) for t in range(T)],
+               "routed_tokens_per_loop": [int(x) for x in active_rows(cfg, run.counts)]}
 
-    calibration = None if args.no_extras else machine_calibration(stream)
-
-    extras = None
+    calibration = extras = None
     if not args.no_extras:
-        extras = {"decode": bench_decode(args, cfg, W, stream), "dreamer": bench_dreamer(args)}
+        calibration = machine_calibration(stream)
+        extras = {}
+        for name in ["gqa", "mla", "act", "dreamer"]:
+            if name == args.workload:
+                continue
+            print(f"[bench] extra workload {name}", file=sys.stderr, flush=True)
+            extras[name] = measure_extra(name, max(5, args.steps // 3), stream)
+        print("[bench] decode step (gqa)", file=sys.stderr, flush=True)
+        extras["decode"] = bench_decode(args, "gqa")
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, inputs, T, args.cpu_budget)
+        cpu = cpu_baseline(cfg, run.inputs)
+        print("[bench] unforced routing on a causal prefix (oracle)", file=sys.stderr, flush=True)
+        routing["unforced"] = unforced_routing(cfg, run.inputs, run.route_idx, run.h)
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "token-loops/s", "n_gpus": 1,
@@ -302,33 +547,19 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
         "data": "synthetic (seeded PCG64 draws, random-init weights)",
         "config": {"workload": describe(cfg), "batch": cfg["batch"], "seq": cfg["seq"], "dim": cfg["dim"],
-                   "T": T, "token_loops_per_step": executed, "parallelism": "single GPU"},
+                   "T": T, "token_loops_per_step": run.executed, "parallelism": "single GPU"},
         "mfma_peak_frac": round(flops / (ms * 1e-3) / (peak_tf * 1e12), 5),
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "roofline": roofline,
+        "kernels": kernels,
         "cpu_baseline": cpu,
+        "routing": routing,
         "stages_us": {k: round(v[0] * 1e3, 2) for k, v in stage_avg.items() if v[1]},
         "step_ms": step_ms,
         "calibration": calibration,
         "extras": extras,
     }
     print(json.dumps(res), flush=True)
-
-
-def _time(fn, steps: int, warmup: int, stream) -> float:
-    """Mean milliseconds of fn() over `steps` calls after `warmup` calls,
-    HIP events on `stream`."""
-    import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        fn()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
 
 
 def machine_calibration(stream) -> dict:
@@ -350,13 +581,17 @@ def machine_calibration(stream) -> dict:
             "library_bf16_gemm_TFLOPs": round(2 * 8192 ** 3 / (mm_ms * 1e-3) / 1e12, 1)}
 
 
-def bench_decode(args, cfg: dict, W: dict, stream) -> dict:
-    """One-token decode step on the bench workload: prefill seq-1 positions,
-    then time steps at the last position (each step rewrites the same cache
-    row, so every step does the same work)."""
+def bench_decode(args, name: str) -> dict:
+    """One-token decode step: prefill seq-1 positions, then time steps at the
+    last position (each step rewrites the same cache row, so every step does
+    the same work)."""
     import torch
 
     import recurrent_depth_transformer_amd as rdt
+    from rdt_inputs import get_config, make_inputs
+    cfg = get_config(name)
+    W = rdt.device_weights(make_inputs(cfg), cfg, "cuda")
+    stream = torch.cuda.current_stream()
     B, S, D, T = cfg["batch"], cfg["seq"], cfg["dim"], cfg["T"]
     blk = rdt.RecurrentBlock(dict(cfg, seq=S - 1), graph=True)
     cache = blk.new_cache(T, S)
@@ -379,37 +614,6 @@ def bench_decode(args, cfg: dict, W: dict, stream) -> dict:
                          "kernel": "whole decode step (weights, chosen experts, cache)",
                          "algorithmic_bytes_per_step": int(nbytes)},
             "cache_bytes": blk.cache_size(T, S)}
-
-
-def bench_dreamer(args) -> dict:
-    """Forward throughput of the full-size Dreamer workload (depth attention,
-    max-score shared expert) and the roofline of the depth-attention kernel."""
-    import torch
-
-    import recurrent_depth_transformer_amd as rdt
-    from rdt_inputs import get_config, make_inputs
-    cfg = get_config("dreamer")
-    T, N = cfg["T"], cfg["batch"] * cfg["seq"]
-    W = rdt.device_weights(make_inputs(cfg), cfg, "cuda")
-    blk = rdt.RecurrentBlock(cfg, graph=True)
-    out = torch.empty_like(W["h0"])
-    ws = blk.workspace(T)
-    stream = torch.cuda.current_stream()
-    steps = max(3, args.steps // 10)
-    ms = _time(lambda: blk.forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws), steps, 2, stream)
-    _, st = blk.profile_forward(W["h0"], W["e"], W, T=T, out=out, workspace=ws)
-    da_ms, da_n = st["depth_attention"]
-    da_us = da_ms / max(1, da_n) * 1e3
-    elt = 2
-    nbytes = depth_attention_bytes(cfg, elt)
-    achieved = nbytes / (da_us * 1e-6) / 1e9
-    return {"workload": describe(cfg), "ms_per_step": round(ms, 4),
-            "value": round(N * T / (ms * 1e-3), 1), "unit": "token-loops/s",
-            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                         "kernel": "k_depth_attention (Dreamer depth attention)", "avg_launch_us": round(da_us, 2),
-                         "algorithmic_bytes_per_launch": int(nbytes)},
-            "stages_us": {k: round(v[0] / v[1] * 1e3, 2) for k, v in st.items() if v[1]}}
 
 
 if __name__ == "__main__":

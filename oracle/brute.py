@@ -8,10 +8,20 @@ then the per-head value up-projection) where the NumPy oracle reconstructs K and
 V explicitly. Agreement of the two to float64 rounding pins the oracle's
 indexing, head mapping, rope pairing and associativity.
 
-It follows the same readings R1-R9 as rdt_oracle (listed there).
+It follows the same readings R1-R9 as rdt_oracle (listed there), and for the
+Dreamer block variants (gist.science summary of "Depth-Recurrent Attention
+Mixtures", Metodologia) the same readings of depth attention (every token
+attends over its own states of loops 0..t; rotary encoding of the depth with
+one half of the pairs at the reversed depth), of the sublayer order (depth
+attention, then sequence attention, then experts, each behind an RMSNorm of
+the running residual, or all three on RMSNorm(h + e) in the parallel variant)
+and of the shared expert scaled by the token's largest router probability.
+Here the depth rotation is written with complex numbers and the depth history
+is kept per token as lists, where the NumPy oracle stacks per-loop arrays.
 """
 from __future__ import annotations
 
+import cmath
 import math
 
 
@@ -56,6 +66,21 @@ def _silu(z):
     return z / (1.0 + math.exp(-z))
 
 
+def _depth_rot(x, p_lo, p_hi, base):
+    """Depth rotation of one head vector as complex multiplication: element i
+    and element i + d/2 form the complex number x_i + 1j*x_{i+d/2}, rotated by
+    the angle p * base^(-2i/d), with p = p_lo for the first d/4 pairs and
+    p = p_hi (the reversed depth) for the others."""
+    d = len(x)
+    half = d // 2
+    out = [0.0] * d
+    for i in range(half):
+        p = p_lo if i < half // 2 else p_hi
+        z = complex(x[i], x[i + half]) * cmath.exp(1j * p * base ** (-2.0 * i / d))
+        out[i], out[i + half] = z.real, z.imag
+    return out
+
+
 def forward(cfg, W, T):
     """Brute-force T-loop. Returns (h as nested lists, loops list)."""
     B, S, D = cfg["batch"], cfg["seq"], cfg["dim"]
@@ -82,6 +107,16 @@ def forward(cfg, W, T):
         Wdq, Wuq, Wdkv = _rows(W["Wdq"]), _rows(W["Wuq"]), _rows(W["Wdkv"])
         Wuk, Wuv = _rows(W["Wuk"]), _rows(W["Wuv"])
         gq, gkv = list(map(float, W["gq"])), list(map(float, W["gkv"]))
+    Hd = cfg.get("da_heads", 0)
+    par = bool(cfg.get("parallel", 0))
+    smax_shared = bool(cfg.get("shared_scale", 0))
+    if Hd:
+        KVd, dd = cfg["da_kv_heads"], cfg["da_head_dim"]
+        Wq_da, Wk_da, Wv_da = _rows(W["Wq_da"]), _rows(W["Wk_da"]), _rows(W["Wv_da"])
+        Wo_da = _rows(W["Wo_da"])
+        g_da = list(map(float, W["g_da"]))
+        keys_of = [[] for _ in range(N)]      # per token: its depth keys of loops 0..t
+        vals_of = [[] for _ in range(N)]
     active = [True] * N
     loops = [0] * N
     cum = [0.0] * N
@@ -89,7 +124,32 @@ def forward(cfg, W, T):
 
     for t in range(T):
         u = [[h[n][c] + e[n][c] for c in range(D)] for n in range(N)]
-        n1 = [_rms(u[n], g1, eps) for n in range(N)]
+        dep = [[0.0] * D for _ in range(N)]
+        if Hd:
+            # depth attention: the token's own states over the loops so far
+            for n in range(N):
+                x = _rms(u[n], g_da, eps)
+                qv, kv, vv_ = _matvec(Wq_da, x), _matvec(Wk_da, x), _matvec(Wv_da, x)
+                q_heads = [_depth_rot(qv[i * dd:(i + 1) * dd], t, T - 1 - t, base) for i in range(Hd)]
+                keys_of[n].append([_depth_rot(kv[j * dd:(j + 1) * dd], t, T - 1 - t, base)
+                                   for j in range(KVd)])
+                vals_of[n].append([vv_[j * dd:(j + 1) * dd] for j in range(KVd)])
+                cat = []
+                for i in range(Hd):
+                    j = (i * KVd) // Hd
+                    sc = [_dot(q_heads[i], keys_of[n][tau][j]) / math.sqrt(dd) for tau in range(t + 1)]
+                    mx = max(sc)
+                    wts = [math.exp(s_ - mx) for s_ in sc]
+                    z = sum(wts)
+                    acc = [0.0] * dd
+                    for tau in range(t + 1):
+                        for c in range(dd):
+                            acc[c] += wts[tau] / z * vals_of[n][tau][j][c]
+                    cat += acc
+                dep[n] = _matvec(Wo_da, cat)
+        # the sequence attention reads RMSNorm(u + d), or RMSNorm(u) in parallel
+        u1 = u if par else [[u[n][c] + dep[n][c] for c in range(D)] for n in range(N)]
+        n1 = [_rms(u1[n], g1, eps) for n in range(N)]
         o = [[0.0] * 0 for _ in range(N)]
         if cfg["attn"] == "gqa":
             q = [_matvec(Wq, n1[n]) for n in range(N)]
@@ -162,7 +222,8 @@ def forward(cfg, W, T):
         for n in range(N):
             if not active[n]:
                 continue
-            x = [u[n][c] + a[n][c] for c in range(D)]
+            # the experts read RMSNorm(u + d + a), or RMSNorm(u) in parallel
+            x = list(u[n]) if par else [u1[n][c] + a[n][c] for c in range(D)]
             n2 = _rms(x, g2, eps)
             logits = _matvec(Wr, n2)
             mx = max(logits)
@@ -182,12 +243,13 @@ def forward(cfg, W, T):
                 y = _matvec(wd, hid)
                 for c in range(D):
                     m[c] += prob[ee] * y[c]
+            sw = max(prob) if smax_shared else 1.0
             for (wg, wu, wd) in shared:
                 hid = [_silu(_dot(wg[f], n2)) * _dot(wu[f], n2) for f in range(len(wg))]
                 y = _matvec(wd, hid)
                 for c in range(D):
-                    m[c] += y[c]
-            h[n] = [A[c] * h[n][c] + Bv[c] * e[n][c] + a[n][c] + m[c] for c in range(D)]
+                    m[c] += sw * y[c]
+            h[n] = [A[c] * h[n][c] + Bv[c] * e[n][c] + dep[n][c] + a[n][c] + m[c] for c in range(D)]
             loops[n] += 1
         if cfg["act"]:
             import numpy as _np  # only for float32 accumulation of the halting sum

@@ -388,12 +388,17 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
           __hip_atomic_store(a.part_o + pr * DV + ds * 16 + lg * 4 + r, oacc[ds][qs][r], __ATOMIC_RELAXED, SC);
     }
     __shared__ int s_last;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this range's partials landed before it is counted
+    // Release: every thread's partial stores happen before the count that
+    // publishes them (an agent-scope release fence in each thread, then the
+    // workgroup barrier, then one relaxed increment). Acquire in the range
+    // that counts last, before it reads the other ranges' partials.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     const int grp = (int)(blockIdx.x % bz);             // (sequence b, head group)
     if (tid == 0) s_last = __hip_atomic_fetch_add(a.split_cnt + grp, 1, __ATOMIC_RELAXED, SC) == a.nsplit - 1;
     __syncthreads();
     if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (tid == 0) __hip_atomic_store(a.split_cnt + grp, 0, __ATOMIC_RELAXED, SC);  // ready for the next launch
     // merge: one wave per head of the group, lane l owns columns 2l, 2l+1 of
     // the sequence's query row (row b: one query per sequence in decode)

@@ -544,15 +544,15 @@ __global__ __launch_bounds__(1024) void k_compact(CompactArgs a) {
   if (tid == 0) *a.n_out = running;
   __syncthreads();
   // seg[b] = first list position whose token belongs to sequence >= b
-  if (tid <= a.B) {
-    const int target = tid * a.S;
+  for (int b = tid; b <= a.B; b += 1024) {
+    const int target = b * a.S;
     int lo = 0, hi = running;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (a.rows_out[mid] < target) lo = mid + 1;
       else hi = mid;
     }
-    a.seg_out[tid] = lo;
+    a.seg_out[b] = lo;
   }
 }
 

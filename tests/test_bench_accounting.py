@@ -75,3 +75,22 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_wide_moe_kernel_accounting():
+    """wide_moe: 8192 tokens, D 2048, 64 experts top-8 + 1 shared, F 1024, T 16,
+    bf16, every expert receiving 1024 rows in every loop.
+    gate/up: 4 * D * F FLOPs for each of the 8192 * 8 routed and 8192 shared rows;
+    router: per token h, e, a read (3 * 4 * D), n2 written (2 * D), 8 indices,
+    gates and slots (12 * 8) and a gap (4), plus the 64 x 2048 router weights;
+    combine: per token h, e, a (12 * D), nine bf16 expert rows (9 * 2 * D),
+    routing entries (12 * 8), h' (4 * D) and, except after the last loop, the
+    next RMSNorm output (2 * D)."""
+    cfg = get_config("wide_moe")
+    counts = [np.full(64, 1024)] * 16
+    assert bench.gate_up_flops(cfg, counts) == 4 * 2048 * 1024 * (65536 + 8192)
+    assert bench.down_flops(cfg, counts) == 2 * 2048 * 1024 * (65536 + 8192)
+    assert bench.router_bytes(cfg, counts, 2) == 8192 * (24576 + 4096 + 96 + 4) + 64 * 2048 * 2
+    per = 24576 + 9 * 2 * 2048 + 96 + 8192
+    assert bench.combine_bytes(cfg, counts, 2, 1) == 8192 * (15 * (per + 4096) + per) / 16
+    assert bench.ksplit_of(cfg) == 1 and bench.ksplit_of(get_config("gqa")) == 2

@@ -5,7 +5,7 @@ import pytest
 from oracle import rdt_oracle as ro
 from rdt_inputs import get_config, make_inputs, n_tokens
 
-from rdt_gpu_run import check_routing_teacher_forced, rms, run_gpu
+from rdt_gpu_run import check_halting, check_routing_teacher_forced, rms, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -66,20 +66,7 @@ def test_end_to_end_forced(name):
     assert err <= TOL * scale
     if cfg["act"]:
         # halting decisions from the GPU's own states, loop by loop
-        thr = np.float32(cfg["act_threshold"])
-        cum = np.zeros(n_tokens(cfg), np.float32)
-        bad = 0
-        for t in range(T):
-            act_rows = np.nonzero(res["loops"] > t)[0]
-            z = res["h_dump"][t + 1][act_rows].astype(np.float64) @ inp["w_halt"].astype(np.float64)
-            cum[act_rows] = (cum[act_rows] + (1 / (1 + np.exp(-z))).astype(np.float32)).astype(np.float32)
-            halt_o = cum[act_rows] >= thr
-            halt_g = res["loops"][act_rows] == t + 1
-            if t == T - 1:  # loops == T also means the token ran out of loops
-                halt_g = halt_g & (res["act_cum"][t][act_rows] >= thr)
-            clear = np.abs(cum[act_rows] - thr) >= 1e-3
-            bad += int(np.sum((halt_o != halt_g) & clear))
-            np.testing.assert_allclose(res["act_cum"][t][act_rows], cum[act_rows], rtol=1e-4, atol=1e-4)
+        bad, _ = check_halting(cfg, inp, res, T)
         assert bad == 0
         assert 0 < res["loops"].min() <= res["loops"].max() <= T
 

@@ -305,6 +305,29 @@ def test_brute_force_matches_oracle(which):
         assert 0 < res["loops"].min() and res["loops"].min() < T  # some tokens halted
 
 
+@pytest.mark.parametrize("name", ["act_small", "mla_small", "wide_small"])
+def test_causal_prefix_equals_full_forward(name):
+    """The full-size end-to-end check runs the oracle on a causal prefix of one
+    sequence: with routing and halting forced, the first P positions of any
+    sequence come out of the whole forward as from the prefix alone (up to
+    float64 summation order)."""
+    from rdt_gpu_run import prefix_inputs
+    cfg = get_config(name)
+    W = make_inputs(cfg)
+    T, P, S = cfg["T"], 23, cfg["seq"]
+    full = oracle.forward(cfg, W, T=T, record=True)
+    forced = np.stack(full["idx"])
+    loops = full["loops"] if cfg["act"] else None
+    for b in (0, cfg["batch"] - 1):
+        rows = b * S + np.arange(P)
+        cp, sub = prefix_inputs(W, cfg, b, P)
+        ref = oracle.forward(cp, sub, T=T, forced_idx=forced[:, rows],
+                             forced_loops=None if loops is None else loops[rows])
+        # (record=True keeps h per loop; BLAS blocking differs with the row count)
+        np.testing.assert_allclose(ref["h"], full["h"][-1][rows], rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(ref["loops"], full["loops"][rows])
+
+
 # ---------------------------------------------------------------------------
 # invariants of the loop
 # ---------------------------------------------------------------------------
@@ -639,6 +662,36 @@ def test_depth_attention_relative_in_both_halves():
         hist = {"k": [], "v": []}
         outs.append([oracle.depth_attention(cfg, W, states[t], t, T, hist) for t in range(5)])
     np.testing.assert_allclose(np.array(outs[0]), np.array(outs[1]), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", ["sequential", "parallel", "parallel_no_depth", "plain_shared_weight"])
+def test_brute_force_matches_oracle_dreamer(variant):
+    """The Dreamer block composition inside the loop, against the scalar brute
+    force: depth attention -> sequence attention -> experts on the running
+    residual, the parallel variant (every sublayer reads RMSNorm(h + e)), and
+    the shared expert weighted by the largest router probability. All weights
+    are nonzero, so a sublayer that reads the wrong residual, a dropped depth
+    term or a wrong shared weight changes h_T by far more than the tolerance."""
+    # weights ~N(0, 0.15): every sublayer moves the state by tens of percent
+    over = dict(batch=1, seq=12, T=4, w_std=0.15)
+    if variant == "parallel":
+        over["parallel"] = 1
+    elif variant == "parallel_no_depth":
+        over.update(parallel=1, da_heads=0, da_kv_heads=0, da_head_dim=0)
+    elif variant == "plain_shared_weight":
+        over["shared_scale"] = 0
+    cfg = get_config("dreamer_tiny", **over)
+    W = make_inputs(cfg)
+    T = cfg["T"]
+    res = oracle.forward(cfg, W, T=T)
+    hb, loops = brute.forward(cfg, W, T)
+    hb = np.array(hb)
+    np.testing.assert_allclose(res["h"], hb, rtol=1e-10, atol=1e-11)
+    assert np.all(res["loops"] == T) and np.all(np.array(loops) == T)
+    # the pin is sensitive to the composition: the other sublayer wiring moves h_T
+    other = dict(cfg, parallel=0 if cfg.get("parallel", 0) else 1)
+    hb_other = np.array(brute.forward(other, W, T)[0])
+    assert np.max(np.abs(hb_other - hb)) > 1e-2 * np.max(np.abs(hb))
 
 
 def test_parallel_equals_sequential_without_attention_output():
