@@ -367,32 +367,41 @@ class Run:
 
 def kernel_figures(cfg: dict, counts, stage_avg: dict, elt: int, peak_tf: float) -> dict:
     """Per-kernel roofline figures from the per-stage launch times: the GEMMs
-    and attention against the MFMA peak, the router and combine against HBM."""
+    and attention against the MFMA peak, the router and combine against HBM.
+    A stage's time per loop is its mean launch time times its launches per
+    loop (the MLA attention stage also holds the value up-projection; its
+    FLOPs are counted with it)."""
     fl = flops_per_token_loop(cfg)
     rows = active_rows(cfg, counts)
     mean_rows = sum(rows) / max(1, len(rows))
+    T = max(1, len(counts))
     out = {}
 
+    def per_loop_us(stage):
+        avg_ms, n = stage_avg.get(stage, (0.0, 0))
+        return avg_ms * 1e3 * n / T, n / T
+
     def mfma(stage, flops):
-        us = stage_avg.get(stage, (0.0, 0))[0] * 1e3
+        us, lpl = per_loop_us(stage)
         if us <= 0:
             return
-        out[stage] = {"bound": "mfma", "avg_launch_us": round(us, 2), "algorithmic_flops_per_launch": int(flops),
+        out[stage] = {"bound": "mfma", "us_per_loop": round(us, 2), "launches_per_loop": round(lpl, 3),
+                      "algorithmic_flops_per_loop": int(flops),
                       "achieved_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
                       "frac": round(flops / (us * 1e-6) / 1e12 / peak_tf, 4)}
 
     def hbm(stage, nbytes):
-        us = stage_avg.get(stage, (0.0, 0))[0] * 1e3
+        us, lpl = per_loop_us(stage)
         if us <= 0:
             return
-        out[stage] = {"bound": "hbm", "avg_launch_us": round(us, 2), "algorithmic_bytes_per_launch": int(nbytes),
+        out[stage] = {"bound": "hbm", "us_per_loop": round(us, 2), "launches_per_loop": round(lpl, 3),
+                      "algorithmic_bytes_per_loop": int(nbytes),
                       "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                       "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
     mfma("expert_gate_up", gate_up_flops(cfg, counts))
     mfma("expert_down", down_flops(cfg, counts))
-    n_qkv = max(1, stage_avg.get("qkv", (0, 1))[1] // max(1, len(counts)))
-    mfma("qkv", fl["qkv"] * mean_rows / n_qkv)
+    mfma("qkv", fl["qkv"] * mean_rows)
     mfma("attention", fl["attention"] * mean_rows)
     mfma("out_proj", fl["out_proj"] * mean_rows)
     hbm("router", router_bytes(cfg, counts, elt))
@@ -512,11 +521,11 @@ def main():
     flops = sum(fl.values()) * run.executed
     peak_tf = PEAK_F32_TFLOPS if cfg["dtype"] == "f32" else PEAK_BF16_TFLOPS
     kernels = kernel_figures(cfg, run.counts, stage_avg, elt, peak_tf)
-    gu = kernels[DOMINANT_STAGE]
+    gu = kernels[DOMINANT_STAGE]   # one launch per loop
     roofline = {"bound": "mfma", "achieved": gu["achieved_TFLOPs"], "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": gu["frac"], "traffic": traffic_from_profiles(args.workload),
                 "kernel": gate_up_kernel(cfg) + " (expert gate/up + SwiGLU)",
-                "avg_launch_us": gu["avg_launch_us"], "algorithmic_flops_per_launch": gu["algorithmic_flops_per_launch"],
+                "avg_launch_us": gu["us_per_loop"], "algorithmic_flops_per_launch": gu["algorithmic_flops_per_loop"],
                 "algorithmic_bytes_per_launch": int(gate_up_bytes(cfg, run.counts, elt))}
     gaps = run.route_gap
     routing = {"near_ties_per_loop": [int(np.sum(gaps[t][np.isfinite(gaps[t])] < 1e-3)) for t in range(T)],
