@@ -202,7 +202,9 @@ rdt_status rdt_config_validate(const rdt_config* cfg);
 
 /* Create a handle for one config on the current HIP device. The handle owns a
  * private capture stream and the cache of captured graphs; it allocates no
- * device memory. *out is set to null on failure. */
+ * device memory. The first handle on a device also looks up the device address
+ * of that device's static scratch (rdt_recurrent_forward_noalloc); RDT_E_HIP if
+ * that fails. *out is set to null on failure. */
 rdt_status rdt_create(const rdt_config* cfg, rdt_handle** out);
 
 /* Destroy a handle (null is a no-op). Work it enqueued must have finished. */
@@ -236,13 +238,42 @@ rdt_status rdt_set_graph_mode(rdt_handle* h, int32_t enabled);
  * The work is enqueued asynchronously; the call returns without waiting, except
  * that the first call with a given A pointer copies A to the host once to check
  * rho(A) < 1 (RDT_E_UNSTABLE otherwise; the weights are never clipped,
- * openclawapi troubleshooting item 3). Kernel faults surface at the caller's
+ * openclawapi troubleshooting item 3). The check is made once per A pointer
+ * (the handle remembers the last 8): values rewritten in place under a pointer
+ * already checked are not checked again. Kernel faults surface at the caller's
  * next synchronisation. Not thread-safe for one handle.
  */
 rdt_status rdt_recurrent_forward(rdt_handle* h, const float* h0, const float* e,
                                  const rdt_weights* w, int32_t T, float* out,
                                  const rdt_aux* aux, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/* Bytes of the static scratch behind rdt_recurrent_forward_noalloc (one copy
+ * per device, 32 MiB). */
+#define RDT_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * rdt_recurrent_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The workspace is a static device array of
+ * RDT_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends; this call allocates nothing (no hipMalloc, no graph
+ * instantiation: the kernels are launched one by one on `stream`).
+ *   Arguments, layouts and results as for rdt_recurrent_forward; the handle's
+ *   device must be current.
+ *   RDT_E_WORKSPACE when the config's workspace for T loops
+ *   (rdt_workspace_size) exceeds RDT_NOALLOC_SCRATCH_BYTES, before anything is
+ *   enqueued; the other errors as for rdt_recurrent_forward.
+ * Every call on one device shares that device's scratch: calls whose work
+ * overlaps on a device (other streams, other threads, other handles) race and
+ * must be serialised by the caller. The scratch keeps the last call's contents;
+ * the forward clears what it needs before use. As for rdt_recurrent_forward,
+ * the first call with a new A pointer waits for a copy of A to check rho(A),
+ * so a caller that captures graphs makes one call before capture.
+ */
+rdt_status rdt_recurrent_forward_noalloc(rdt_handle* h, const float* h0, const float* e,
+                                         const rdt_weights* w, int32_t T, float* out,
+                                         const rdt_aux* aux, void* stream);
 
 /*
  * Per-loop key/value cache for incremental decoding. Generation keeps one cache

@@ -25,8 +25,9 @@ EXPORTED_SYMBOLS = [
     "rdt_workspace_size", "rdt_spectral_radius", "rdt_set_graph_mode",
     "rdt_recurrent_forward", "rdt_profile_forward", "rdt_stage_name", "rdt_last_error", "rdt_version",
     "rdt_cache_size", "rdt_prefill", "rdt_decode_workspace_size", "rdt_decode_step",
-    "rdt_router_bias_update", "rdt_expert_depths",
+    "rdt_router_bias_update", "rdt_expert_depths", "rdt_recurrent_forward_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 32 << 20   # RDT_NOALLOC_SCRATCH_BYTES
 N_STAGES = 13
 
 RDT_OK, RDT_E_INVALID, RDT_E_UNSUPPORTED, RDT_E_UNSTABLE, RDT_E_WORKSPACE, RDT_E_HIP = 0, -1, -2, -3, -4, -5
@@ -92,6 +93,8 @@ def load_library(path: str = LIB_PATH):
     lib.rdt_set_graph_mode.argtypes = [_vp, _i32]
     lib.rdt_recurrent_forward.argtypes = [_vp, _vp, _vp, ctypes.POINTER(RdtWeights), _i32, _vp,
                                           ctypes.POINTER(RdtAux), _vp, ctypes.c_size_t, _vp]
+    lib.rdt_recurrent_forward_noalloc.argtypes = [_vp, _vp, _vp, ctypes.POINTER(RdtWeights), _i32, _vp,
+                                                  ctypes.POINTER(RdtAux), _vp]
     lib.rdt_profile_forward.argtypes = [_vp, _vp, _vp, ctypes.POINTER(RdtWeights), _i32, _vp,
                                         ctypes.POINTER(RdtAux), _vp, ctypes.c_size_t, _vp,
                                         ctypes.POINTER(_f32), ctypes.POINTER(_i32), _i32]
@@ -111,7 +114,8 @@ def load_library(path: str = LIB_PATH):
     lib.rdt_version.restype = ctypes.c_char_p
     for name in ["rdt_config_default", "rdt_config_validate", "rdt_create", "rdt_spectral_radius",
                  "rdt_set_graph_mode", "rdt_recurrent_forward", "rdt_profile_forward", "rdt_prefill",
-                 "rdt_decode_step", "rdt_router_bias_update", "rdt_expert_depths"]:
+                 "rdt_decode_step", "rdt_router_bias_update", "rdt_expert_depths",
+                 "rdt_recurrent_forward_noalloc"]:
         getattr(lib, name).restype = _i32
     _lib = lib
     return lib
@@ -220,6 +224,22 @@ class RecurrentBlock:
         """out = h_T. Tensors live on the GPU; aux maps rdt_aux field names to
         preallocated device tensors."""
         return self._run(False, h0, e, weights, T, out, aux, workspace, stream)[0]
+
+    def forward_noalloc(self, h0, e, weights: dict, T: int | None = None, out=None, aux: dict | None = None,
+                        stream=None):
+        """forward through rdt_recurrent_forward_noalloc: the library's static
+        per-device scratch instead of a workspace; kernels launched one by one.
+        `out` must be preallocated by the caller when nothing may allocate."""
+        import torch
+        T = int(self.cfg.get("T", 1) if T is None else T)
+        if out is None:
+            out = torch.empty_like(h0)
+        w, a = self._structs(weights, aux)
+        if stream is None:
+            stream = torch.cuda.current_stream(h0.device).cuda_stream
+        _check(self.lib.rdt_recurrent_forward_noalloc(self.h, _ptr(h0), _ptr(e), ctypes.byref(w), T, _ptr(out),
+                                                      ctypes.byref(a), stream))
+        return out
 
     def profile_forward(self, h0, e, weights: dict, T: int | None = None, out=None, aux: dict | None = None,
                         workspace=None, stream=None):

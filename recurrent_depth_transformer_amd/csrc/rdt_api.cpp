@@ -55,14 +55,48 @@ struct GraphEntry {
   hipGraphExec_t exec;
 };
 
+// A pointers whose rho(A) < 1 was confirmed (the newest kRhoSlots, fixed
+// storage so that checking allocates nothing).
+constexpr int kRhoSlots = 8;
+
 struct rdt_handle {
   rdt_config cfg;
   int device;
   hipStream_t cap;
   int graph_mode;
-  std::vector<const float*> checked_A;
+  const float* checked_A[kRhoSlots];
+  int n_checked;
   std::vector<GraphEntry> graphs;
 };
+
+// Scratch of rdt_recurrent_forward_noalloc: one copy of this array on every
+// device the library runs on, held until the process ends. Host code never
+// passes the array's name to a kernel (on the host it stands for a host-side
+// shadow, not a device address); it uses the device address that
+// hipGetSymbolAddress returned for the device, looked up once per device when
+// the first handle on that device is created.
+static __device__ __align__(256) char scratch[RDT_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static hipError_t scratch_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));   // the current device's copy
+  if (e != hipSuccess) return e;
+  if (!ptr) return hipErrorInvalidSymbol;
+  g_scratch_ptr[device] = ptr;
+  return hipSuccess;
+}
+
+static void* scratch_of(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
 
 extern "C" const char* rdt_last_error(void) { return g_err.c_str(); }
 extern "C" const char* rdt_version(void) { return "librdt 0.1 gfx950"; }
@@ -108,10 +142,18 @@ extern "C" rdt_status rdt_create(const rdt_config* c, rdt_handle** out) {
   if (!h) return set_err(RDT_E_INVALID, "out of host memory");
   h->cfg = *c;
   h->graph_mode = 1;
+  h->n_checked = 0;
   if (hipGetDevice(&h->device) != hipSuccess ||
       hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking) != hipSuccess) {
     delete h;
     return set_err(RDT_E_HIP, "rdt_create: cannot create the capture stream");
+  }
+  // the device address of this device's scratch array (first handle only)
+  hipError_t se = scratch_setup(h->device);
+  if (se != hipSuccess) {
+    (void)hipStreamDestroy(h->cap);
+    delete h;
+    return set_err(RDT_E_HIP, std::string("rdt_create: scratch address lookup failed: ") + hipGetErrorString(se));
   }
   *out = h;
   return RDT_OK;
@@ -621,20 +663,27 @@ static rdt_status check_weights(const rdt_config& c, const rdt_weights* w) {
   return RDT_OK;
 }
 
+// rho(A) < 1 for the per-channel A, checked once per A pointer: the first call
+// with a pointer copies A to the host (a stack buffer; dim <= 4096 is
+// validated) and waits for it. A rewritten in place under the same pointer is
+// not checked again.
 static rdt_status check_rho(rdt_handle* h, const float* A, hipStream_t s) {
-  for (const float* p : h->checked_A)
-    if (p == A) return RDT_OK;
-  std::vector<float> host((size_t)h->cfg.dim);
-  HIPCHK(hipMemcpyAsync(host.data(), A, host.size() * 4, hipMemcpyDeviceToHost, s));
+  for (int i = 0; i < h->n_checked && i < kRhoSlots; ++i)
+    if (h->checked_A[i] == A) return RDT_OK;
+  float host[4096];
+  const int dim = h->cfg.dim;
+  if (dim > 4096) return set_err(RDT_E_UNSUPPORTED, "dim above 4096");
+  HIPCHK(hipMemcpyAsync(host, A, (size_t)dim * 4, hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
   float rho = 0.f;
-  rdt_spectral_radius(host.data(), h->cfg.dim, &rho);
+  rdt_spectral_radius(host, dim, &rho);
   if (!(rho < 1.f)) {
     char buf[96];
     snprintf(buf, sizeof buf, "unstable injection: rho(A) = %.6g >= 1", (double)rho);
     return set_err(RDT_E_UNSTABLE, buf);
   }
-  h->checked_A.push_back(A);
+  h->checked_A[h->n_checked % kRhoSlots] = A;
+  h->n_checked += 1;
   return RDT_OK;
 }
 
@@ -767,6 +816,34 @@ extern "C" rdt_status rdt_recurrent_forward(rdt_handle* h, const float* h0, cons
   st = check_rho(h, w->A, s);
   if (st != RDT_OK) return st;
   return launch(h, f, s);
+}
+
+extern "C" rdt_status rdt_recurrent_forward_noalloc(rdt_handle* h, const float* h0, const float* e,
+                                                    const rdt_weights* w, int32_t T, float* out,
+                                                    const rdt_aux* aux, void* stream) {
+  if (!h) return set_err(RDT_E_INVALID, "null handle");
+  void* ws = scratch_of(h->device);
+  if (!ws) return set_err(RDT_E_HIP, "no scratch address for this handle's device");
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != h->device)
+    return set_err(RDT_E_INVALID, "the handle's device must be current");
+  if (T >= 0 && T <= h->cfg.max_T) {
+    const size_t need = make_plan(h->cfg, T).total;
+    if (need > (size_t)RDT_NOALLOC_SCRATCH_BYTES) {
+      char buf[160];
+      snprintf(buf, sizeof buf, "rdt_recurrent_forward_noalloc: this config needs %zu workspace bytes; the static "
+               "scratch holds %zu (use rdt_recurrent_forward with a workspace)", need,
+               (size_t)RDT_NOALLOC_SCRATCH_BYTES);
+      return set_err(RDT_E_WORKSPACE, buf);
+    }
+  }
+  Fwd f;
+  rdt_status st = prepare(h, h0, e, w, T, out, aux, ws, (size_t)RDT_NOALLOC_SCRATCH_BYTES, f);
+  if (st != RDT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  st = check_rho(h, w->A, s);
+  if (st != RDT_OK) return st;
+  return enqueue(f, s);   // launched one by one: instantiating a graph would allocate
 }
 
 extern "C" size_t rdt_cache_size(const rdt_config* cfg, int32_t T, int32_t max_seq) {
