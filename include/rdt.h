@@ -370,8 +370,8 @@ typedef enum rdt_stage {
   RDT_STAGE_PERMUTE = 6,  /* per-expert counts, offsets, stable permutation */
   RDT_STAGE_EXPERT_GU = 7,   /* grouped gate/up GEMM + SwiGLU */
   RDT_STAGE_EXPERT_DOWN = 8, /* grouped down GEMM */
-  RDT_STAGE_COMBINE = 9,  /* MoE combine + LTI injection (+ ACT) */
-  RDT_STAGE_COMPACT = 10, /* ACT active-list compaction */
+  RDT_STAGE_COMBINE = 9,  /* MoE combine + LTI injection (+ ACT halting and compaction) */
+  RDT_STAGE_COMPACT = 10, /* reserved: the ACT active-list compaction runs inside the combine */
   RDT_STAGE_OTHER = 11,   /* per-forward set-up, fills and dump copies */
   RDT_STAGE_DEPTH_ATTN = 12, /* Dreamer depth attention over a token's own loop states */
   RDT_N_STAGES = 13

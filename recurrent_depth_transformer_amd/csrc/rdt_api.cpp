@@ -7,8 +7,8 @@
 //   causal flash attention -> output projection (+ depth-wise LoRA as a second
 //   K phase) -> one kernel for RMSNorm, router softmax/top-k and the stable
 //   expert permutation -> grouped SwiGLU gate/up -> grouped down -> combine +
-//   injection (+ ACT, + the next loop's first RMSNorm) -> (ACT) active-list
-//   compaction.
+//   injection (+ ACT halting and the stable compaction of the active list, +
+//   the next loop's first RMSNorm).
 // Data-dependent sizes (active tokens, rows per expert) stay on the device;
 // grids are sized for the worst case and idle workgroups exit at once, so the
 // whole T-loop is a static graph.
@@ -304,6 +304,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   if (act) {
     LAUNCH(RDT_STAGE_OTHER, launch_iota(lists, N, ncount, N, segs, P.B, P.S, s));
     LAUNCH(RDT_STAGE_OTHER, launch_fill_f32(cum, 0.f, N, s));
+    LAUNCH(RDT_STAGE_OTHER, launch_fill_i32(at<int>(ws, P.wgmask), 0, (N + 3) / 4, s));
   }
   const int k = P.k, E = P.E;
   if (f.aux.loops) LAUNCH(RDT_STAGE_OTHER, launch_fill_i32(f.aux.loops, 0, N, s));
@@ -336,7 +337,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   int* idx = at<int>(ws, P.idx);
   float* gates = at<float>(ws, P.gates);
   float* gap = at<float>(ws, P.gap);
-  int* cnt2 = at<int>(ws, P.cnt) + P.att_cnt;  // per-expert counts of even / odd loops
+  int* cnt2 = at<int>(ws, P.cnt) + P.att_cnt + kCompactCounters;  // per-expert counts of even / odd loops
   int* slot = at<int>(ws, P.slot);
   int* pcap = at<int>(ws, P.pcap);
   char* hmid = at<char>(ws, P.hmid);
@@ -387,7 +388,8 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       n1a.rope_cos[0] = cosb; n1a.rope_sin[0] = sinb; n1a.rope_S[0] = P.rope_len; n1a.rope_dr[0] = P.dr;
       if (P.da) { n1a.rope_cos[1] = dcos; n1a.rope_sin[1] = dsin; n1a.rope_S[1] = f.T; n1a.rope_dr[1] = P.dd; }
       n1a.rope_base = c.rope_base;
-      n1a.zero = at<int>(ws, P.cnt); n1a.zero_n = P.att_cnt + E;  // split counters, loop 0's counts
+      // split counters, the compaction arrival counters, loop 0's counts
+      n1a.zero = at<int>(ws, P.cnt); n1a.zero_n = P.att_cnt + kCompactCounters + E;
       LAUNCH(RDT_STAGE_NORM1, launch_norm(n1a, s));
     }
     if (P.da) {
@@ -619,14 +621,12 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     ca.a_dump = f.aux.a_dump ? f.aux.a_dump + (size_t)t * N * D : nullptr;
     ca.n1_out = t + 1 < f.T ? (P.da ? nd : n1) : nullptr; ca.g1 = P.da ? w.g_da : w.g1; ca.eps = c.norm_eps;
     ca.d = P.da ? dbuf : nullptr; ca.smax = smax;
-    LAUNCH(RDT_STAGE_COMBINE, launch_combine(ca, s));
-    if (act) {
-      CompactArgs cp{};
-      cp.rows_in = cur; cp.n_in = ncur; cp.cum = cum; cp.thr = c.act_threshold;
-      cp.rows_out = lists + (size_t)(t + 1) * N; cp.n_out = ncount + t + 1;
-      cp.seg_out = segs + (size_t)(t + 1) * (P.B + 1); cp.B = P.B; cp.S = P.S;
-      LAUNCH(RDT_STAGE_COMPACT, launch_compact(cp, s));
+    if (act) {   // the stable compaction of the active list runs inside the combine launch
+      ca.seg_in = seg; ca.rows_out = lists + (size_t)(t + 1) * N; ca.n_out = ncount + t + 1;
+      ca.seg_out = segs + (size_t)(t + 1) * (P.B + 1); ca.nseq = P.B;
+      ca.wg_mask = at<int>(ws, P.wgmask); ca.wg_tmp = at<int>(ws, P.wgtmp); ca.done = at<int>(ws, P.cnt) + P.att_cnt;
     }
+    LAUNCH(RDT_STAGE_COMBINE, launch_combine(ca, s));
     if (f.aux.h_dump) LAUNCH(RDT_STAGE_OTHER, launch_copy_f32(f.aux.h_dump + (size_t)(t + 1) * N * D, f.out, (long long)N * D, s));
   }
   return RDT_OK;

@@ -427,7 +427,28 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
         float v[8];
 #pragma unroll
         for (int x = 0; x < 8; ++x) v[x] = crow[c8 + x];
-        if (sg.rope) {
+        const int rhalf = g.rope_dim >> 1;
+        // whole-vector RoPE: the 8 columns lie in one half of one head and
+        // share one rotation position, so their angle entries are 8
+        // consecutive table floats (same arithmetic as the per-element form)
+        const bool rope_vec = sg.rope && (rhalf & 7) == 0 && (!g.drope || ((rhalf >> 1) & 7) == 0);
+        if (rope_vec) {
+          const int hd0 = lc % g.rope_dim, jj0 = hd0 % rhalf;
+          const int pp = g.drope ? (jj0 < (rhalf >> 1) ? g.dpos0 : g.dpos1) : (g.pos_dev ? *g.pos_dev : tok % g.seq);
+          const float4 c0 = *reinterpret_cast<const float4*>(g.cosb + pp * rhalf + jj0);
+          const float4 c1 = *reinterpret_cast<const float4*>(g.cosb + pp * rhalf + jj0 + 4);
+          const float4 s0 = *reinterpret_cast<const float4*>(g.sinb + pp * rhalf + jj0);
+          const float4 s1 = *reinterpret_cast<const float4*>(g.sinb + pp * rhalf + jj0 + 4);
+          const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+          if (hd0 < rhalf) {
+#pragma unroll
+            for (int x = 0; x < 8; ++x) v[x] = crow[c8 + x] * cs[x] - crow[c8 + x + rhalf] * sn[x];
+          } else {
+#pragma unroll
+            for (int x = 0; x < 8; ++x) v[x] = crow[c8 + x - rhalf] * sn[x] + crow[c8 + x] * cs[x];
+          }
+        } else if (sg.rope) {
           const int rd = g.rope_dim, half = rd >> 1;
           const int pos = g.pos_dev ? *g.pos_dev : tok % g.seq;
 #pragma unroll

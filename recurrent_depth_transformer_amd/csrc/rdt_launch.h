@@ -162,6 +162,14 @@ struct CombineArgs {
   // ksplit > 1: the expert outputs are ksplit float partial sums at
   // Yp + s * ystride (row-major, D), added in slice order; Y is unused
   int ksplit; const float* Yp; long long ystride;
+  // ACT compaction (act and rows_out set): the tokens of this launch's list
+  // (rows, *ndev of them, in token order) whose halting sum stays below thr
+  // go, in the same order, to rows_out (count to *n_out); seg_out[b] is the
+  // first position in rows_out of sequence b's tokens (seg_in: the same for
+  // the input list), b = 0..nseq. Scratch: wg_mask [grid] (zero on entry,
+  // left zero), wg_tmp [grid], done [65] (zero on entry, left zero).
+  const int* seg_in; int* rows_out; int* n_out; int* seg_out; int nseq;
+  int* wg_mask; int* wg_tmp; int* done;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
@@ -179,11 +187,6 @@ struct NormRouteArgs {
 };
 hipError_t launch_norm_route(const NormRouteArgs& a, hipStream_t s);
 
-struct CompactArgs {
-  const int* rows_in; const int* n_in; const float* cum; float thr;
-  int* rows_out; int* n_out; int* seg_out; int B, S;
-};
-hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 
 // -------------------------------------------------------- depth attention
 // Row i (token tok = i) and query head h attend over the token's own keys and

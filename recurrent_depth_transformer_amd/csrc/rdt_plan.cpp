@@ -115,7 +115,9 @@ Plan make_plan(const rdt_config& c, int T, int counters) {
   p.gates = take(N * p.k * 4);
   p.gap = take(N * 4);
   p.att_cnt = counters;
-  p.cnt = take((size_t)(counters + 2 * p.E) * 4);  // counters, then two loops' counts (alternate loops)
+  // decode key-range counters, the ACT compaction arrival counters, then two
+  // loops' expert counts (alternate loops)
+  p.cnt = take((size_t)(counters + kCompactCounters + 2 * p.E) * 4);
   p.slot = take(N * p.k * 4);
   p.pcap = take((size_t)p.E * N * 4);
   p.hmid = take(N * (p.k + p.Se) * p.F * e);
@@ -131,6 +133,8 @@ Plan make_plan(const rdt_config& c, int T, int counters) {
   p.ncount = take(Tp * 4);
   p.seg = take(Tp * (p.B + 1) * 4);
   p.cum = take(N * 4);
+  p.wgmask = take((size_t)((N + 3) / 4) * 4);   // ACT compaction: one mask per combine workgroup
+  p.wgtmp = take((size_t)((N + 3) / 4) * 4);
   p.pos = take(4);
   p.smax = take(N * 4);
   p.da = c.da_heads > 0;

@@ -8,6 +8,10 @@
 
 namespace rdt {
 
+// Arrival counters of the ACT compaction inside the combine launch (one
+// counter of finished sub-counters, then 64 sub-counters).
+constexpr int kCompactCounters = 65;
+
 struct Plan {
   // shapes
   int B, S, N, D, H, KV, d, E, Se, k, F, r, L, T;
@@ -26,6 +30,7 @@ struct Plan {
   int ksplit;                // K slices of the expert down projection (y then holds
                             // ksplit float partial sums, [ksplit][N*(k+Se)][D])
   size_t lists, ncount, seg, cum;
+  size_t wgmask, wgtmp;     // ACT compaction inside the combine: [ceil(N/4)] ints each
   size_t pos;               // decode position (one int, written before each step)
   int rope_len;             // positions in the RoPE tables
   size_t smax;              // [N] float: maximum router probability per row
@@ -38,7 +43,9 @@ struct Plan {
   size_t att_po, att_pm, att_pl;
   // ints in front of the expert counts (cnt), cleared with them by the first
   // RMSNorm of a call: decode attention counts finished key ranges per
-  // (sequence, head group) there, so the last range merges the partials
+  // (sequence, head group) there, so the last range merges the partials;
+  // ints att_cnt .. att_cnt + kCompactCounters - 1 of the region are the ACT
+  // compaction's arrival counters, and the two loops' counts follow them
   int att_cnt;
   size_t total;
 };

@@ -1,7 +1,7 @@
 // Bandwidth-bound row kernels of the recurrent block: the two RMSNorms (the
 // second fused with the router and the expert slot assignment), the MoE
-// combine fused with the LTI injection and ACT halting, depth attention, the
-// active-list compaction, and small utilities.
+// combine fused with the LTI injection, ACT halting and the active-list
+// compaction, depth attention, and small utilities.
 //
 // Row kernels give one wave64 to one token row; each lane moves 16-byte
 // vectors, so a row of D floats is read in D/256 fully coalesced passes.
@@ -98,6 +98,118 @@ hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------- ACT active-list compaction
+// Runs at the end of every combine workgroup, inside the combine launch. Each
+// workgroup holds 4 consecutive rows of the input list (in token order) and
+// knows which of them keep running (halting sum still below the threshold).
+// It publishes that 4-bit mask with an arrival bit through a device-coherent
+// store, then counts itself on `done`; the workgroup that counts last (no
+// workgroup ever waits for another before that) builds the stable compacted
+// list: an exclusive scan of the masks, then every kept token in order, the
+// per-sequence offsets, and it clears the masks and the counter for the next
+// launch. A mask whose store is not yet visible to it is re-read (its store
+// was issued before its workgroup counted itself, so it arrives; the re-read
+// is bounded all the same). Only workgroups holding rows count themselves,
+// on CMP_SUB sub-counters and one counter of finished sub-counters, because
+// atomics on one address serialise (one counter for 4096 workgroups cost
+// about 75 us per launch).
+constexpr int CMP_ARRIVED = 0x100;
+
+constexpr int CMP_SUB = 64;   // arrival sub-counters (same-address atomics serialise)
+
+__device__ __forceinline__ void act_compact_tail(const CombineArgs& a, int n, int keep_bits) {
+  constexpr int SC = __HIP_MEMORY_SCOPE_AGENT;
+  __shared__ int s_last;
+  __shared__ int s_ws[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwg = (n + 3) / 4;     // workgroups holding rows of the list
+  const int w = blockIdx.x;
+  if (nwg == 0) {                  // nothing ran: an empty list
+    if (w == 0) {
+      if (tid == 0) *a.n_out = 0;
+      for (int b = tid; b <= a.nseq; b += 256) a.seg_out[b] = 0;
+    }
+    return;
+  }
+  if (w >= nwg) return;
+  // done[0] counts finished sub-counters, done[1 + j] the workgroups w with
+  // w % CMP_SUB == j; the one completing the last sub-counter goes on
+  if (tid == 0) {
+    __hip_atomic_store(a.wg_mask + w, keep_bits | CMP_ARRIVED, __ATOMIC_RELAXED, SC);
+    asm volatile("" ::: "memory");
+    const int j = w % CMP_SUB;
+    const int tgt = (nwg - 1 - j) / CMP_SUB + 1;
+    int last = 0;
+    if (__hip_atomic_fetch_add(a.done + 1 + j, 1, __ATOMIC_RELAXED, SC) == tgt - 1) {
+      __hip_atomic_store(a.done + 1 + j, 0, __ATOMIC_RELAXED, SC);          // zero for the next launch
+      const int nsub = nwg < CMP_SUB ? nwg : CMP_SUB;
+      last = __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, SC) == nsub - 1;
+    }
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // the last workgroup: thread tid takes the input workgroups [w0, w1)
+  const int chunk = (nwg + 255) / 256;
+  const int w0 = tid * chunk < nwg ? tid * chunk : nwg;
+  const int w1 = w0 + chunk < nwg ? w0 + chunk : nwg;
+  int cntl = 0;
+  for (int b0 = w0; b0 < w1; b0 += 16) {
+    int mm[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      mm[u] = b0 + u < w1 ? __hip_atomic_load(a.wg_mask + b0 + u, __ATOMIC_RELAXED, SC) : CMP_ARRIVED;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (b0 + u >= w1) break;
+      int m = mm[u];
+      for (int spin = 0; !(m & CMP_ARRIVED) && spin < (1 << 20); ++spin) {
+        __builtin_amdgcn_s_sleep(2);
+        m = __hip_atomic_load(a.wg_mask + b0 + u, __ATOMIC_RELAXED, SC);
+      }
+      a.wg_tmp[b0 + u] = m & 15;
+      cntl += __popc(m & 15);
+      __hip_atomic_store(a.wg_mask + b0 + u, 0, __ATOMIC_RELAXED, SC);   // zero for the next launch
+    }
+  }
+  // exclusive scan of the per-thread counts over the workgroup
+  int inc = cntl;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) s_ws[wave] = inc;
+  __syncthreads();
+  int run = inc - cntl;
+  for (int q = 0; q < wave; ++q) run += s_ws[q];
+  const int total = s_ws[0] + s_ws[1] + s_ws[2] + s_ws[3];
+  for (int w = w0; w < w1; ++w) {
+    const int m = a.wg_tmp[w];
+    a.wg_tmp[w] = (run << 4) | m;             // base of input workgroup w, and its mask
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if ((m >> r) & 1) a.rows_out[run++] = a.rows ? a.rows[4 * w + r] : 4 * w + r;
+  }
+  if (tid == 0) {
+    *a.n_out = total;
+    __hip_atomic_store(a.done, 0, __ATOMIC_RELAXED, SC);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // seg_out[b]: kept rows before input position seg_in[b]
+  for (int b = tid; b <= a.nseq; b += 256) {
+    const int j = a.seg_in[b];
+    int v = total;
+    if (j < n) {
+      const int x = a.wg_tmp[j >> 2];
+      v = (x >> 4) + __popc((x & 15) & ((1 << (j & 3)) - 1));
+    }
+    a.seg_out[b] = v;
+  }
+}
+
 // ---------------------------------------------------------- combine + inject
 // m = sum_j gate_j * Y[inv_j] + sum_s Y_shared_s;  h = A*h + B*e + a + m
 // ACT: cum += sigmoid(w . h); loops = t + 1.
@@ -117,11 +229,13 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   constexpr int KP = LAT ? 8 : 0;       // routing entries fetched ahead
   constexpr int KA = KP > 0 ? KP : 1;
   __shared__ int s_off[MAX_EXPERTS];
+  __shared__ int s_keep;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave;
   const int n = a.ndev ? *a.ndev : a.n;
   const bool live = i < n;
   const int D = a.D, k = a.k;
+  if (threadIdx.x == 0) s_keep = 0;
   int colc[NV];
   bool okc[NV];
 #pragma unroll
@@ -169,7 +283,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     }
   }
   __syncthreads();
-  if (!live) return;
+  if (live) {
   const T* Y = reinterpret_cast<const T*>(a.Y);
   // expert output row p, columns col..col+3: stored values, or the sum of the
   // K-slice partials in slice order
@@ -305,9 +419,156 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       const float c = a.cum[tok] + p;
       a.cum[tok] = c;
       if (a.cum_dump) a.cum_dump[tok] = c;
+      if (c < a.thr) atomicOr(&s_keep, 1 << wave);
     }
   }
   if (lane == 0 && a.loops) a.loops[tok] = a.t + 1;
+  }  // live
+  if (a.act && a.rows_out) {
+    __syncthreads();
+    act_compact_tail(a, n, s_keep);
+  }
+}
+
+// The combine with 8 consecutive columns per lane (bf16 expert outputs as one
+// 16-byte load, float rows as two): the bandwidth form for rows that are a
+// multiple of 512 wide. Expert outputs are gathered EB rows at a time (all
+// their loads in flight). Every element adds the same terms in the same order
+// as k_combine; the per-lane partial sums of the halting dot product and of
+// the next RMSNorm run over the lane's own columns.
+template <int NV8, int EB>
+__global__ __launch_bounds__(256) void k_combine8(CombineArgs a) {
+  __shared__ int s_off[MAX_EXPERTS];
+  __shared__ int s_keep;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave;
+  const int n = a.ndev ? *a.ndev : a.n;
+  const bool live = i < n;
+  const int D = a.D, k = a.k;
+  if (threadIdx.x == 0) s_keep = 0;
+  if (wave == 0) {   // exclusive prefix of the per-expert counts
+    const int c = lane < a.E ? a.cnt[lane] : 0;
+    int inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane < a.E) s_off[lane] = inc - c;
+    if (blockIdx.x == 0 && lane < a.E) {
+      if (a.counts_dump) a.counts_dump[lane] = c;
+      a.cnt_next[lane] = 0;
+    }
+  }
+  __syncthreads();
+  if (live) {
+    const int tok = a.rows ? a.rows[i] : i;
+    const bf16_t* Y = reinterpret_cast<const bf16_t*>(a.Y);
+    float m[NV8][8];
+#pragma unroll
+    for (int c = 0; c < NV8; ++c)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) m[c][x] = 0.f;
+    const float sw = a.smax ? a.smax[i] : 1.f;   // shared-expert weight
+    const int KT = k + a.Se;                     // routed choices in order, then the shared experts
+    for (int j0 = 0; j0 < KT; j0 += EB) {
+      long long p[EB];
+      float gt[EB];
+#pragma unroll
+      for (int u = 0; u < EB; ++u) {
+        const int j = j0 + u < KT ? j0 + u : j0;
+        if (j < k) {
+          p[u] = s_off[a.idx[(long long)i * k + j]] + a.slot[(long long)i * k + j];
+          gt[u] = a.gates[(long long)i * k + j];
+        } else {
+          p[u] = (long long)n * k + (long long)(j - k) * n + i;
+          gt[u] = sw;
+        }
+      }
+      uint4 yv[EB][NV8];
+#pragma unroll
+      for (int u = 0; u < EB; ++u)
+#pragma unroll
+        for (int c = 0; c < NV8; ++c)
+          yv[u][c] = *reinterpret_cast<const uint4*>(Y + p[u] * D + (c * 64 + lane) * 8);
+#pragma unroll
+      for (int u = 0; u < EB; ++u) {
+        if (j0 + u >= KT) break;
+#pragma unroll
+        for (int c = 0; c < NV8; ++c) {
+          const uint32_t w4[4] = {yv[u][c].x, yv[u][c].y, yv[u][c].z, yv[u][c].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            m[c][2 * q] += gt[u] * __uint_as_float(w4[q] << 16);
+            m[c][2 * q + 1] += gt[u] * __uint_as_float(w4[q] & 0xffff0000u);
+          }
+        }
+      }
+    }
+    float z = 0.f, ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NV8; ++c) {
+      const int col0 = (c * 64 + lane) * 8;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int col = col0 + 4 * hh;
+        float* mm = m[c] + 4 * hh;
+        const float4 hv = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + col);
+        const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
+        const float4 av = *reinterpret_cast<const float4*>(a.a + (long long)i * D + col);
+        if (a.d) {
+          const float4 dv = *reinterpret_cast<const float4*>(a.d + (long long)i * D + col);
+          mm[0] += dv.x; mm[1] += dv.y; mm[2] += dv.z; mm[3] += dv.w;
+        }
+        const float4 Av = *reinterpret_cast<const float4*>(a.A + col);
+        const float4 Bv = *reinterpret_cast<const float4*>(a.B + col);
+        float4 hn;
+        hn.x = Av.x * hv.x + Bv.x * ev.x + av.x + mm[0];
+        hn.y = Av.y * hv.y + Bv.y * ev.y + av.y + mm[1];
+        hn.z = Av.z * hv.z + Bv.z * ev.z + av.z + mm[2];
+        hn.w = Av.w * hv.w + Bv.w * ev.w + av.w + mm[3];
+        *reinterpret_cast<float4*>(a.h + (long long)tok * D + col) = hn;
+        if (a.a_dump) *reinterpret_cast<float4*>(a.a_dump + (long long)tok * D + col) = av;
+        if (a.act) {
+          const float4 wv = *reinterpret_cast<const float4*>(a.w_halt + col);
+          z += wv.x * hn.x + wv.y * hn.y + wv.z * hn.z + wv.w * hn.w;
+        }
+        mm[0] = hn.x + ev.x; mm[1] = hn.y + ev.y; mm[2] = hn.z + ev.z; mm[3] = hn.w + ev.w;
+        ss += mm[0] * mm[0] + mm[1] * mm[1] + mm[2] * mm[2] + mm[3] * mm[3];
+      }
+    }
+    if (a.n1_out) {
+      ss = wave_sum(ss);
+      const float inv = 1.f / sqrtf(ss / (float)D + a.eps);
+      bf16_t* dst = reinterpret_cast<bf16_t*>(a.n1_out) + (long long)tok * D;
+#pragma unroll
+      for (int c = 0; c < NV8; ++c) {
+        const int col = (c * 64 + lane) * 8;
+        const float4 g0 = *reinterpret_cast<const float4*>(a.g1 + col);
+        const float4 g1 = *reinterpret_cast<const float4*>(a.g1 + col + 4);
+        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        float y[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) y[x] = m[c][x] * inv * gg[x];
+        store8<bf16_t>(dst + col, y);
+      }
+    }
+    if (a.act) {
+      z = wave_sum(z);
+      if (lane == 0) {
+        const float p = 1.f / (1.f + expf(-z));
+        const float c = a.cum[tok] + p;
+        a.cum[tok] = c;
+        if (a.cum_dump) a.cum_dump[tok] = c;
+        if (c < a.thr) atomicOr(&s_keep, 1 << wave);
+      }
+    }
+    if (lane == 0 && a.loops) a.loops[tok] = a.t + 1;
+  }
+  if (a.act && a.rows_out) {
+    __syncthreads();
+    act_compact_tail(a, n, s_keep);
+  }
 }
 
 template <typename T, bool LAT>
@@ -325,7 +586,20 @@ static hipError_t combine_nv(const CombineArgs& a, hipStream_t s) {
 template <typename T>
 static hipError_t combine_t(const CombineArgs& a, hipStream_t s) {
   // up to 2048 rows (512 workgroups, one round on the chip at LAT's occupancy)
-  return a.n <= 2048 ? combine_nv<T, true>(a, s) : combine_nv<T, false>(a, s);
+  if (a.n <= 2048) return combine_nv<T, true>(a, s);
+  // long bf16 launches with whole 512-column vectors per row: 8 columns per
+  // lane (measured on 8192 rows of 2048: 153 -> 137 us)
+  if (sizeof(T) == 2 && a.ksplit <= 1 && a.D % 512 == 0 && a.D <= 4096) {
+    dim3 grid((a.n + 3) / 4);
+    switch (a.D / 512) {
+      case 1: hipLaunchKernelGGL((k_combine8<1, 5>), grid, dim3(256), 0, s, a); return hipGetLastError();
+      case 2: hipLaunchKernelGGL((k_combine8<2, 5>), grid, dim3(256), 0, s, a); return hipGetLastError();
+      case 4: hipLaunchKernelGGL((k_combine8<4, 5>), grid, dim3(256), 0, s, a); return hipGetLastError();
+      case 8: hipLaunchKernelGGL((k_combine8<8, 3>), grid, dim3(256), 0, s, a); return hipGetLastError();
+      default: break;
+    }
+  }
+  return combine_nv<T, false>(a, s);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
@@ -346,8 +620,11 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
 // expert with one atomic add on cnt, and hands the slots out; the slot order
 // inside an expert is arbitrary (each row's expert output does not depend on
 // which rows share its GEMM tile).
+// Up to 2048-wide rows the kernel is held to 64 VGPRs (8 waves per SIMD), so
+// two 16-wave workgroups share a CU and all of a 8192-row launch is resident
+// at once (measured on 8192 x 2048: 75 -> 67 us).
 template <typename T, int NV>
-__global__ __launch_bounds__(1024) void k_norm_route(NormRouteArgs a) {
+__global__ __launch_bounds__(1024, NV <= 8 ? 8 : 1) void k_norm_route(NormRouteArgs a) {
   constexpr int KC = 4096 / (int)sizeof(T);        // columns per LDS chunk
   constexpr int LDA = KC + 16 / (int)sizeof(T);    // padded row stride
   __shared__ __align__(16) T As[16 * LDA];
@@ -505,61 +782,6 @@ hipError_t launch_norm_route(const NormRouteArgs& a, hipStream_t s) {
   return a.norm.dtype == DT_F32 ? norm_route_t<float>(a, s) : norm_route_t<bf16_t>(a, s);
 }
 
-
-// -------------------------------------------------------- ACT compaction
-// Stable filter of the active list (tokens whose cumulative halting sum is
-// still below the threshold) plus the start of every sequence in the new list.
-__global__ __launch_bounds__(1024) void k_compact(CompactArgs a) {
-  __shared__ int wtot[16];
-  __shared__ int woff[16];
-  __shared__ int total_s;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n = *a.n_in;
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  int running = 0;
-  for (int c0 = 0; c0 < n; c0 += 1024) {
-    const int i = c0 + tid;
-    int tok = -1;
-    bool keep = false;
-    if (i < n) {
-      tok = a.rows_in[i];
-      keep = a.cum[tok] < a.thr;
-    }
-    const unsigned long long m = __ballot(keep);
-    if (lane == 0) wtot[wave] = __popcll(m);
-    __syncthreads();
-    if (tid == 0) {
-      int acc = 0;
-      for (int w = 0; w < 16; ++w) {
-        woff[w] = acc;
-        acc += wtot[w];
-      }
-      total_s = acc;
-    }
-    __syncthreads();
-    if (keep) a.rows_out[running + woff[wave] + __popcll(m & lt)] = tok;
-    running += total_s;
-    __syncthreads();
-  }
-  if (tid == 0) *a.n_out = running;
-  __syncthreads();
-  // seg[b] = first list position whose token belongs to sequence >= b
-  for (int b = tid; b <= a.B; b += 1024) {
-    const int target = b * a.S;
-    int lo = 0, hi = running;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (a.rows_out[mid] < target) lo = mid + 1;
-      else hi = mid;
-    }
-    a.seg_out[b] = lo;
-  }
-}
-
-hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, s, a);
-  return hipGetLastError();
-}
 
 // ----------------------------------------------------------- MLA latents
 // cqn = RMSNorm(c_q) * gq;  latent = [RMSNorm(c_kv) * gkv | rope(k_rope)]

@@ -269,3 +269,25 @@ def test_error_paths():
     ref = blk.forward(W["h0"], W["e"], W, T=2)
     torch.cuda.synchronize()
     assert torch.equal(h, ref)
+
+
+def test_act_many_sequences_compaction():
+    """ACT with more sequences than one compaction workgroup has threads
+    (1100 sequences of 2 tokens): every sequence's offset in the compacted
+    active list must be right, or its tokens get another sequence's keys.
+    End to end against the oracle with halting forced to the GPU's, and the
+    halting decisions from the GPU's own states."""
+    cfg = get_config("act_small", batch=1100, seq=2, dim=64, n_heads=4, n_kv_heads=2, head_dim=16,
+                     n_experts=4, top_k=2, expert_dim=32, lora_rank=8, n_lora=2, T=5, halt_std=0.3)
+    T = cfg["T"]
+    res, inp, *_ = run_gpu(cfg, T=T)
+    mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro)
+    ref = ro.forward(cfg, inp, T=T, forced_idx=res["route_idx"], forced_loops=res["loops"])
+    err = np.max(np.abs(res["h"] - ref["h"]))
+    scale = rms(ref["h"])
+    bad, _ = check_halting(cfg, inp, res, T)
+    _report("act_many_sequences", ratio=f"{err / scale:.3e}", route_mismatch=mism, near_ties=near,
+            loops=np.bincount(res["loops"], minlength=T + 1).tolist())
+    assert mism == 0 and bad == 0
+    assert res["loops"].min() < T   # some tokens halted early
+    assert err <= TOL * scale
