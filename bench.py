@@ -535,7 +535,7 @@ def main():
     if not args.no_extras:
         calibration = machine_calibration(stream)
         extras = {}
-        for name in ["gqa", "mla", "act", "dreamer"]:
+        for name in ["gqa", "mla", "act", "dreamer", "dreamer_parallel"]:
             if name == args.workload:
                 continue
             print(f"[bench] extra workload {name}", file=sys.stderr, flush=True)

@@ -21,6 +21,8 @@ gains = 1, router bias = 0):
 
   dreamer   bf16, 4x2048, D 1024, GQA 16/4 of 64, depth attention 16/4 of 64, 16 experts
             top-2 + 1 shared weighted by the max router probability, F 1408, T 8
+  dreamer_parallel  the same with parallel sublayers (every sublayer reads
+            RMSNorm(h + e)) and depth-wise LoRA of rank 16 on the attention output
 
 The ``*_small`` workloads keep each family's structure at sizes a CPU reference
 finishes in seconds, with sequence lengths and widths that leave ragged tiles.
@@ -112,6 +114,17 @@ WORKLOADS = {
                            da_heads=4, da_kv_heads=4, da_head_dim=64, parallel=1,
                            n_experts=16, n_shared_experts=1, shared_scale=1, top_k=4,
                            expert_dim=160, T=4, dtype="bf16"),
+    "dreamer_parallel": _cfg(batch=4, seq=2048, dim=1024, n_heads=16, n_kv_heads=4, head_dim=64,
+                             da_heads=16, da_kv_heads=4, da_head_dim=64, parallel=1, n_experts=16,
+                             n_shared_experts=1, shared_scale=1, top_k=2, expert_dim=1408, T=8,
+                             lora_rank=16, n_lora=8, dtype="bf16"),
+    "parallel_lora_small": _cfg(batch=2, seq=66, dim=256, n_heads=8, n_kv_heads=2, head_dim=32,
+                                da_heads=4, da_kv_heads=2, da_head_dim=32, parallel=1, n_experts=8,
+                                n_shared_experts=1, shared_scale=1, top_k=2, expert_dim=160, T=5,
+                                lora_rank=16, n_lora=3, dtype="bf16"),
+    "parallel_act_small": _cfg(batch=3, seq=70, dim=256, n_heads=4, n_kv_heads=2, head_dim=64,
+                               parallel=1, n_experts=8, top_k=2, expert_dim=192, T=8,
+                               lora_rank=8, n_lora=4, act=True, dtype="bf16"),
     "dreamer_tiny": _cfg(batch=1, seq=32, dim=64, n_heads=4, n_kv_heads=2, head_dim=16,
                          da_heads=2, da_kv_heads=1, da_head_dim=16, n_experts=4,
                          n_shared_experts=1, shared_scale=1, top_k=2, expert_dim=128, T=5,

@@ -63,6 +63,8 @@ struct rdt_handle {
   rdt_config cfg;
   int device;
   hipStream_t cap;
+  hipStream_t side;          // the parallel block's attention branch
+  hipEvent_t ev_fork, ev_join;
   int graph_mode;
   const float* checked_A[kRhoSlots];
   int n_checked;
@@ -148,6 +150,17 @@ extern "C" rdt_status rdt_create(const rdt_config* c, rdt_handle** out) {
     delete h;
     return set_err(RDT_E_HIP, "rdt_create: cannot create the capture stream");
   }
+  h->side = nullptr; h->ev_fork = nullptr; h->ev_join = nullptr;
+  if (c->parallel_block &&
+      (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+       hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+       hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess)) {
+    if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+    if (h->side) (void)hipStreamDestroy(h->side);
+    (void)hipStreamDestroy(h->cap);
+    delete h;
+    return set_err(RDT_E_HIP, "rdt_create: cannot create the branch stream");
+  }
   // the device address of this device's scratch array (first handle only)
   hipError_t se = scratch_setup(h->device);
   if (se != hipSuccess) {
@@ -165,6 +178,9 @@ extern "C" void rdt_destroy(rdt_handle* h) {
     (void)hipGraphExecDestroy(g.exec);
     (void)hipGraphDestroy(g.graph);
   }
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->side) (void)hipStreamDestroy(h->side);
   (void)hipStreamDestroy(h->cap);
   delete h;
 }
@@ -196,6 +212,10 @@ struct Fwd {
   char* cache = nullptr;
   int max_seq = 0;
   int decode = 0;
+  // second stream and fork / join events for the parallel block's branches
+  // (null: one stream)
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
 
 // Event pairs around launches (rdt_profile_forward only).
@@ -289,11 +309,11 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   const size_t cplane = (size_t)P.B * f.max_seq * crow * elt;                 // bytes per array per loop
   auto cache_at = [&](int t, int which) { return f.cache + ((size_t)t * (P.mla ? 1 : 2) + which) * cplane; };
   // rows of this call's K/V (or latent) buffer -> cache rows
-  auto append = [&](int t, int which, const char* src) -> hipError_t {
+  auto append = [&](int t, int which, const char* src, hipStream_t st) -> hipError_t {
     if (!f.cache) return hipSuccess;
     const int s_in = f.decode ? 1 : P.S;
     return launch_rows_scatter(cache_at(t, which), (long long)crow * elt, src, (long long)crow * elt,
-                               (int)(crow * elt), N, s_in, f.max_seq, pos_dev, s);
+                               (int)(crow * elt), N, s_in, f.max_seq, pos_dev, st);
   };
   if (P.mla) LAUNCH(RDT_STAGE_OTHER, launch_head_transpose(dt, at<char>(ws, P.wukT), w.Wuk, P.H, P.nope, P.kvl, s));
 
@@ -320,6 +340,11 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   char* n1 = at<char>(ws, P.n1);
   // Dreamer variants: depth attention buffers, parallel sublayers, shared scale
   const bool par = c.parallel_block != 0;
+  // concurrent branches need the handle's second stream; the profiling
+  // forward keeps one stream so that its events time single launches
+  const bool fork = par && f.side && !prof;
+  hipStream_t sa = fork ? f.side : s;
+  const bool lora_in_combine = par && P.r > 0 && P.r <= 32;
   float* smax = (c.shared_scale && P.Se > 0) ? at<float>(ws, P.smax) : nullptr;
   char* nd = P.da ? at<char>(ws, P.da_nd) : nullptr;
   char* dq = P.da ? at<char>(ws, P.da_q) : nullptr;
@@ -392,6 +417,13 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       n1a.zero = at<int>(ws, P.cnt); n1a.zero_n = P.att_cnt + kCompactCounters + E;
       LAUNCH(RDT_STAGE_NORM1, launch_norm(n1a, s));
     }
+    // Parallel block (every sublayer reads RMSNorm(h + e)): the sequence-
+    // attention branch runs on a second stream, forked here and joined before
+    // the combine, beside the depth-attention and MoE branches on `s`.
+    if (fork) {
+      HIPCHK(hipEventRecord(f.ev_fork, s));
+      HIPCHK(hipStreamWaitEvent(f.side, f.ev_fork, 0));
+    }
     if (P.da) {
       // Dreamer depth attention: q, k, v of this loop (depth RoPE at t and at
       // the reversed depth T-1-t), keys/values kept per loop, attention over
@@ -423,7 +455,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       NormArgs n1a{};
       n1a.dtype = dt; n1a.h = f.out; n1a.e = f.e; n1a.a = par ? nullptr : dbuf; n1a.g = w.g1; n1a.eps = c.norm_eps;
       n1a.D = D; n1a.rows = nullptr; n1a.ndev = nullptr; n1a.n = N; n1a.out = n1; n1a.out_scatter = 1;
-      LAUNCH(RDT_STAGE_NORM1, launch_norm(n1a, s));
+      LAUNCH(RDT_STAGE_NORM1, launch_norm(n1a, sa));
     }
 
     // a2-a4: attention
@@ -449,20 +481,20 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
         g.rows = nullptr; g.gather = 0; g.Mdev = nullptr;
         g.nseg = 3; g.seg[0] = sq; g.seg[1] = sk; g.seg[2] = sv;
         pick_tile(N, Hd + 2 * KVd, P.d, &g.bm, &g.bn);
-        LAUNCH(RDT_STAGE_QKV, dense_gemm(g, s));
+        LAUNCH(RDT_STAGE_QKV, dense_gemm(g, sa));
       } else {
         DenseGemm gq = g;
         gq.rows = cur; gq.gather = 1; gq.Mdev = ncur; gq.nseg = 1; gq.seg[0] = sq;
         pick_tile(N, Hd, P.d, &gq.bm, &gq.bn);
-        LAUNCH(RDT_STAGE_QKV, dense_gemm(gq, s));
+        LAUNCH(RDT_STAGE_QKV, dense_gemm(gq, sa));
         DenseGemm gkv = g;
         gkv.rows = prev; gkv.gather = 1; gkv.Mdev = nprev; gkv.nseg = 2; gkv.seg[0] = sk; gkv.seg[1] = sv;
         pick_tile(N, 2 * KVd, P.d, &gkv.bm, &gkv.bn);
-        LAUNCH(RDT_STAGE_QKV, dense_gemm(gkv, s));
+        LAUNCH(RDT_STAGE_QKV, dense_gemm(gkv, sa));
       }
       if (f.cache && !direct) {
-        LAUNCH(RDT_STAGE_QKV, append(t, 0, kb));
-        LAUNCH(RDT_STAGE_QKV, append(t, 1, vb));
+        LAUNCH(RDT_STAGE_QKV, append(t, 0, kb, sa));
+        LAUNCH(RDT_STAGE_QKV, append(t, 1, vb, sa));
       }
       AttnArgs aa{};
       aa.dtype = dt; aa.dqk = P.d; aa.dv = P.d;
@@ -474,7 +506,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       aa.S = f.decode ? f.max_seq : P.S; aa.dec = f.decode; aa.dec_pos = pos_dev;
       aa.scale = 1.f / sqrtf((float)P.d);
       set_split(aa);
-      LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, s));
+      LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, sa));
     } else {
       const int W = P.kvl + P.nr, qw = P.nope + P.nr;
       char* cq_raw = at<char>(ws, P.cq_raw);
@@ -493,21 +525,21 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g1.seg[0] = GemmSeg{w.Wdq, P.ql, cq_raw, P.ql, 1, 0, 1};
       g1.seg[1] = GemmSeg{w.Wdkv, W, lat_raw, W, 1, 0, 1};
       pick_tile(N, P.ql + W, 16, &g1.bm, &g1.bn);
-      LAUNCH(RDT_STAGE_QKV, dense_gemm(g1, s));
+      LAUNCH(RDT_STAGE_QKV, dense_gemm(g1, sa));
       MlaNormArgs mn{};
       mn.dtype = dt; mn.cq_raw = (const float*)cq_raw; mn.ql = P.ql; mn.lat_raw = (const float*)lat_raw;
       mn.kvl = P.kvl; mn.nr = P.nr; mn.gq = w.gq; mn.gkv = w.gkv; mn.eps = c.norm_eps;
       mn.rows = prev; mn.ndev = nprev; mn.n = N; mn.cqn = cqn; mn.latent = latent;
       mn.cosb = cosb; mn.sinb = sinb; mn.S = P.S; mn.pos_dev = pos_dev;
-      LAUNCH(RDT_STAGE_QKV, launch_mla_norm(mn, s));
-      if (f.cache) LAUNCH(RDT_STAGE_QKV, append(t, 0, latent));
+      LAUNCH(RDT_STAGE_QKV, launch_mla_norm(mn, sa));
+      if (f.cache) LAUNCH(RDT_STAGE_QKV, append(t, 0, latent, sa));
       // query up-projection (compacted rows)
       DenseGemm g2{};
       g2.dtype = dt; g2.A = cqn; g2.lda = P.ql; g2.K = P.ql; g2.batch = 1; g2.epi = EPI_STORE;
       g2.rows = cur; g2.gather = act ? 1 : 0; g2.M = N; g2.Mdev = ncur;
       g2.nseg = 1; g2.seg[0] = GemmSeg{w.Wuq, P.H * qw, qfull, P.H * qw, 0, 0, 0};
       pick_tile(N, P.H * qw, 16, &g2.bm, &g2.bn);
-      LAUNCH(RDT_STAGE_QKV, dense_gemm(g2, s));
+      LAUNCH(RDT_STAGE_QKV, dense_gemm(g2, sa));
       // absorb: q_lat[h] = q_nope[h] . Wuk[h]  (per head, B = Wuk[h]^T)
       DenseGemm g3{};
       g3.dtype = dt; g3.A = qfull; g3.lda = P.H * qw; g3.a_bstride = qw; g3.K = P.nope; g3.epi = EPI_STORE;
@@ -515,13 +547,13 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g3.nseg = 1; g3.seg[0] = GemmSeg{wukT, P.kvl, qattn, P.H * W, 0, 0, 0};
       g3.b_bstride = (long long)P.kvl * P.nope; g3.c_bstride = W;
       pick_tile(N, (long long)P.kvl * P.H, 16, &g3.bm, &g3.bn);
-      LAUNCH(RDT_STAGE_QKV, dense_gemm(g3, s));
+      LAUNCH(RDT_STAGE_QKV, dense_gemm(g3, sa));
       QRopeArgs qr{};
       qr.dtype = dt; qr.src = qfull; qr.src_ld = P.H * qw; qr.src_hs = qw; qr.src_off = P.nope;
       qr.dst = qattn; qr.dst_ld = P.H * W; qr.dst_hs = W; qr.dst_off = P.kvl;
       qr.H = P.H; qr.nr = P.nr; qr.rows = cur; qr.ndev = ncur; qr.n = N;
       qr.cosb = cosb; qr.sinb = sinb; qr.S = P.S; qr.pos_dev = pos_dev;
-      LAUNCH(RDT_STAGE_QKV, launch_qrope(qr, s));
+      LAUNCH(RDT_STAGE_QKV, launch_qrope(qr, sa));
       AttnArgs aa{};
       aa.dtype = dt; aa.dqk = W; aa.dv = P.kvl;
       aa.q = qattn; aa.q_ld = P.H * W; aa.q_hs = W;
@@ -533,7 +565,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       aa.S = f.decode ? f.max_seq : P.S; aa.dec = f.decode; aa.dec_pos = pos_dev;
       aa.scale = 1.f / sqrtf((float)(P.nope + P.nr));
       set_split(aa);
-      LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, s));
+      LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, sa));
       // value up-projection per head: o[h] = o_lat[h] . Wuv[h]^T
       DenseGemm g4{};
       g4.dtype = dt; g4.A = olat; g4.lda = P.H * P.kvl; g4.a_bstride = P.kvl; g4.K = P.kvl; g4.epi = EPI_STORE;
@@ -541,12 +573,13 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g4.nseg = 1; g4.seg[0] = GemmSeg{w.Wuv, P.vd, o, P.hv, 0, 0, 0};
       g4.b_bstride = (long long)P.vd * P.kvl; g4.c_bstride = P.vd;
       pick_tile(N, (long long)P.vd * P.H, 16, &g4.bm, &g4.bn);
-      LAUNCH(RDT_STAGE_ATTN, dense_gemm(g4, s));
+      LAUNCH(RDT_STAGE_ATTN, dense_gemm(g4, sa));
     }
 
-    // a5: output projection (+ depth-wise LoRA as a second K phase)
+    // a5: output projection (+ depth-wise LoRA as a second K phase; in the
+    // parallel block the combine adds the LoRA term instead)
     const int tl = P.r > 0 ? (t < P.L - 1 ? t : P.L - 1) : 0;
-    if (P.r > 0) {
+    if (P.r > 0 && !lora_in_combine) {
       DenseGemm gz{};
       gz.dtype = dt; gz.A = o; gz.lda = P.hv; gz.K = P.hv; gz.batch = 1; gz.epi = EPI_STORE;
       gz.rows = cur; gz.gather = 0; gz.M = N; gz.Mdev = ncur;
@@ -554,17 +587,18 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       gz.seg[0] = GemmSeg{elt_ptr(w.lora_down, (long long)tl * P.r * P.hv, elt), P.r, z, P.r, 0, 0, 0};
       gz.bm = 128; gz.bn = 64;
       if ((N + 127) / 128 < 256) gz.bm = 64;
-      LAUNCH(RDT_STAGE_OPROJ, dense_gemm(gz, s));
+      LAUNCH(RDT_STAGE_OPROJ, dense_gemm(gz, sa));
     }
     DenseGemm go{};
     go.dtype = dt; go.A = o; go.lda = P.hv; go.K = P.hv; go.batch = 1; go.epi = EPI_STORE;
     go.rows = cur; go.gather = 0; go.M = N; go.Mdev = ncur;
     go.nseg = 1; go.seg[0] = GemmSeg{w.Wo, D, abuf, D, 0, 0, 1};
-    if (P.r > 0) {
+    if (P.r > 0 && !lora_in_combine) {
       go.A2 = z; go.lda2 = P.r; go.B2 = elt_ptr(w.lora_up, (long long)tl * D * P.r, elt); go.K2 = P.r;
     }
     pick_tile(N, D, 16, &go.bm, &go.bn);
-    LAUNCH(RDT_STAGE_OPROJ, dense_gemm(go, s));
+    LAUNCH(RDT_STAGE_OPROJ, dense_gemm(go, sa));
+    if (fork) HIPCHK(hipEventRecord(f.ev_join, sa));
 
     // a5-a6: x = u + a, n2 = RMSNorm(x) * g2 (compacted rows), router softmax /
     // top-k, and the stable expert permutation, in one kernel
@@ -626,6 +660,12 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       ca.seg_out = segs + (size_t)(t + 1) * (P.B + 1); ca.nseq = P.B;
       ca.wg_mask = at<int>(ws, P.wgmask); ca.wg_tmp = at<int>(ws, P.wgtmp); ca.done = at<int>(ws, P.cnt) + P.att_cnt;
     }
+    if (lora_in_combine) {
+      ca.lora_o = o; ca.lora_r = P.r; ca.lora_hv = P.hv;
+      ca.lora_A = elt_ptr(w.lora_down, (long long)tl * P.r * P.hv, elt);
+      ca.lora_B = elt_ptr(w.lora_up, (long long)tl * D * P.r, elt);
+    }
+    if (fork) HIPCHK(hipStreamWaitEvent(s, f.ev_join, 0));   // the attention branch has written a
     LAUNCH(RDT_STAGE_COMBINE, launch_combine(ca, s));
     if (f.aux.h_dump) LAUNCH(RDT_STAGE_OTHER, launch_copy_f32(f.aux.h_dump + (size_t)(t + 1) * N * D, f.out, (long long)N * D, s));
   }
@@ -714,6 +754,7 @@ static rdt_status prepare(rdt_handle* h, const float* h0, const float* e, const 
   if (!ws || ws_bytes < f.P.total) return set_err(RDT_E_WORKSPACE, "workspace missing or too small");
   if (misaligned(ws, 256)) return set_err(RDT_E_INVALID, "workspace must be 256-byte aligned");
   f.h0 = h0; f.e = e; f.w = w; f.T = T; f.out = out; f.ws = (char*)ws;
+  f.side = h->side; f.ev_fork = h->ev_fork; f.ev_join = h->ev_join;
   f.decode = decode ? 1 : 0;
   f.max_seq = max_seq;
   if (aux) f.aux = *aux;

@@ -105,18 +105,21 @@ def test_fullsize(name):
         assert end_to_end_prefix(name, cfg, inp, res, T) <= TOL
 
 
-def test_fullsize_dreamer():
-    """The Dreamer workload at the size bench.py times: routing of every row
+@pytest.mark.parametrize("name", ["dreamer", "dreamer_parallel"])
+def test_fullsize_dreamer(name):
+    """The Dreamer workloads at the size bench.py times (sequential sublayers;
+    parallel sublayers with depth-wise LoRA, whose branches run on two
+    streams and whose LoRA term the combine adds): routing of every row
     teacher-forced each loop, and on sampled rows of the first sequence the
     loop update from the GPU's own states (depth attention over the token's
     loops 0..t, sequence attention over its sequence)."""
-    cfg = get_config("dreamer")
+    cfg = get_config(name)
     T, S = cfg["T"], cfg["seq"]
-    print("[fullsize] dreamer: running the GPU forward with dumps", flush=True)
+    print(f"[fullsize] {name}: running the GPU forward with dumps", flush=True)
     res, inp, *_ = run_gpu(cfg, T=T)
     assert np.all(np.isfinite(res["h"]))
     mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro)
-    print(f"[fullsize] dreamer: routing mismatches={mism} near_ties={near} compared={comp}", flush=True)
+    print(f"[fullsize] {name}: routing mismatches={mism} near_ties={near} compared={comp}", flush=True)
     assert mism == 0
     rng = np.random.default_rng(321)
     tables = ro.rope_tables(S, cfg["head_dim"], cfg["rope_base"])
@@ -126,7 +129,7 @@ def test_fullsize_dreamer():
                                          res["route_idx"][t][rows], tables=tables)
         err = np.max(np.abs(res["h_dump"][t + 1][rows] - hn))
         scale = rms(res["h_dump"][t + 1])
-        print(f"[fullsize] dreamer loop {t}: rows={rows.size} max|dh|/rms={err / scale:.3e}", flush=True)
+        print(f"[fullsize] {name} loop {t}: rows={rows.size} max|dh|/rms={err / scale:.3e}", flush=True)
         assert err <= TOL * scale
 
 

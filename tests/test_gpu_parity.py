@@ -49,7 +49,8 @@ def test_closed_form_injection(name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_bf16", "gqa_small", "wide_small", "act_small", "mla_small",
-                                  "dreamer_tiny", "dreamer_small", "parallel_small"])
+                                  "dreamer_tiny", "dreamer_small", "parallel_small", "parallel_lora_small",
+                                  "parallel_act_small"])
 def test_end_to_end_forced(name):
     cfg = get_config(name)
     T = cfg["T"]
@@ -212,12 +213,22 @@ def test_act_zero_halting_vector_halts_after_two_loops():
     assert np.max(np.abs(res["h"] - ref["h"])) <= TOL * rms(ref["h"])
 
 
-@pytest.mark.parametrize("name", ["gqa_small", "act_small", "dreamer_small"])
+@pytest.mark.parametrize("name", ["gqa_small", "act_small", "dreamer_small", "parallel_lora_small",
+                                  "parallel_act_small"])
 def test_graph_matches_eager_bitwise(name):
+    """Graph replay against kernels launched one by one; for the parallel
+    block both run the attention branch on the second stream, and the
+    profiling forward (one stream) gives the same bits as well."""
     cfg = get_config(name)
-    r1, inp, _, W = run_gpu(cfg, dumps=False, graph=True)
+    r1, inp, blk, W = run_gpu(cfg, dumps=False, graph=True)
     r2, *_ = run_gpu(cfg, inp, dumps=False, graph=False, weights=W)
     assert np.array_equal(r1["h"], r2["h"])
+    if cfg.get("parallel"):
+        out, stages = blk.profile_forward(W["h0"], W["e"], W, T=cfg["T"])
+        assert np.array_equal(out.cpu().numpy(), r1["h"])
+        for _ in range(3):   # replays with the host synchronising in between
+            r3, *_ = run_gpu(cfg, inp, dumps=False, weights=W, block=blk)
+            assert np.array_equal(r3["h"], r1["h"])
 
 
 def test_repeat_runs_bitwise():

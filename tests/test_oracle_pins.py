@@ -664,7 +664,8 @@ def test_depth_attention_relative_in_both_halves():
     np.testing.assert_allclose(np.array(outs[0]), np.array(outs[1]), rtol=1e-10, atol=1e-12)
 
 
-@pytest.mark.parametrize("variant", ["sequential", "parallel", "parallel_no_depth", "plain_shared_weight"])
+@pytest.mark.parametrize("variant", ["sequential", "parallel", "parallel_no_depth", "plain_shared_weight",
+                                     "parallel_lora"])
 def test_brute_force_matches_oracle_dreamer(variant):
     """The Dreamer block composition inside the loop, against the scalar brute
     force: depth attention -> sequence attention -> experts on the running
@@ -680,6 +681,8 @@ def test_brute_force_matches_oracle_dreamer(variant):
         over.update(parallel=1, da_heads=0, da_kv_heads=0, da_head_dim=0)
     elif variant == "plain_shared_weight":
         over["shared_scale"] = 0
+    elif variant == "parallel_lora":
+        over.update(parallel=1, lora_rank=8, n_lora=2)
     cfg = get_config("dreamer_tiny", **over)
     W = make_inputs(cfg)
     T = cfg["T"]
