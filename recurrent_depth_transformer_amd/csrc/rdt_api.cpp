@@ -344,7 +344,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   // forward keeps one stream so that its events time single launches
   const bool fork = par && f.side && !prof;
   hipStream_t sa = fork ? f.side : s;
-  const bool lora_in_combine = par && P.r > 0 && P.r <= 32;
+
   float* smax = (c.shared_scale && P.Se > 0) ? at<float>(ws, P.smax) : nullptr;
   char* nd = P.da ? at<char>(ws, P.da_nd) : nullptr;
   char* dq = P.da ? at<char>(ws, P.da_q) : nullptr;
@@ -576,10 +576,9 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       LAUNCH(RDT_STAGE_ATTN, dense_gemm(g4, sa));
     }
 
-    // a5: output projection (+ depth-wise LoRA as a second K phase; in the
-    // parallel block the combine adds the LoRA term instead)
+    // a5: output projection (+ depth-wise LoRA as a second K phase)
     const int tl = P.r > 0 ? (t < P.L - 1 ? t : P.L - 1) : 0;
-    if (P.r > 0 && !lora_in_combine) {
+    if (P.r > 0) {
       DenseGemm gz{};
       gz.dtype = dt; gz.A = o; gz.lda = P.hv; gz.K = P.hv; gz.batch = 1; gz.epi = EPI_STORE;
       gz.rows = cur; gz.gather = 0; gz.M = N; gz.Mdev = ncur;
@@ -593,7 +592,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     go.dtype = dt; go.A = o; go.lda = P.hv; go.K = P.hv; go.batch = 1; go.epi = EPI_STORE;
     go.rows = cur; go.gather = 0; go.M = N; go.Mdev = ncur;
     go.nseg = 1; go.seg[0] = GemmSeg{w.Wo, D, abuf, D, 0, 0, 1};
-    if (P.r > 0 && !lora_in_combine) {
+    if (P.r > 0) {
       go.A2 = z; go.lda2 = P.r; go.B2 = elt_ptr(w.lora_up, (long long)tl * D * P.r, elt); go.K2 = P.r;
     }
     pick_tile(N, D, 16, &go.bm, &go.bn);
@@ -659,11 +658,6 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       ca.seg_in = seg; ca.rows_out = lists + (size_t)(t + 1) * N; ca.n_out = ncount + t + 1;
       ca.seg_out = segs + (size_t)(t + 1) * (P.B + 1); ca.nseq = P.B;
       ca.wg_mask = at<int>(ws, P.wgmask); ca.wg_tmp = at<int>(ws, P.wgtmp); ca.done = at<int>(ws, P.cnt) + P.att_cnt;
-    }
-    if (lora_in_combine) {
-      ca.lora_o = o; ca.lora_r = P.r; ca.lora_hv = P.hv;
-      ca.lora_A = elt_ptr(w.lora_down, (long long)tl * P.r * P.hv, elt);
-      ca.lora_B = elt_ptr(w.lora_up, (long long)tl * D * P.r, elt);
     }
     if (fork) HIPCHK(hipStreamWaitEvent(s, f.ev_join, 0));   // the attention branch has written a
     LAUNCH(RDT_STAGE_COMBINE, launch_combine(ca, s));

@@ -170,10 +170,6 @@ struct CombineArgs {
   // left zero), wg_tmp [grid], done [65] (zero on entry, left zero).
   const int* seg_in; int* rows_out; int* n_out; int* seg_out; int nseq;
   int* wg_mask; int* wg_tmp; int* done;
-  // depth-wise LoRA added here instead of in the output projection (parallel
-  // block, rank <= 32): a[i] += B_t (A_t o[i]), with o [n, hv] the attention
-  // output (compacted rows, storage type), A_t [r, hv], B_t [D, r]
-  const void* lora_o; const void* lora_A; const void* lora_B; int lora_r, lora_hv;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 

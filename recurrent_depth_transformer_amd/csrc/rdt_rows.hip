@@ -211,58 +211,7 @@ __device__ __forceinline__ void act_compact_tail(const CombineArgs& a, int n, in
 }
 
 // ---------------------------------------------------------- combine + inject
-// z = A_t o[i] for the wave's row i (lane-strided dot products reduced over
-// the wave; every lane ends with all r values).
-template <typename T>
-__device__ __forceinline__ void lora_down_row(const CombineArgs& a, int i, float (&z)[32]) {
-  const int lane = threadIdx.x & 63, hv = a.lora_hv, r = a.lora_r;
-  const T* o = reinterpret_cast<const T*>(a.lora_o) + (long long)i * hv;
-  const T* A = reinterpret_cast<const T*>(a.lora_A);
-#pragma unroll
-  for (int j = 0; j < 32; ++j) z[j] = 0.f;
-  for (int c0 = lane * 4; c0 < hv; c0 += 256) {
-    float ov[4];
-    load4f<T>(o + c0, ov);
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if (j >= r) break;
-      float av[4];
-      load4f<T>(A + (long long)j * hv + c0, av);
-      z[j] += av[0] * ov[0] + av[1] * ov[1] + av[2] * ov[2] + av[3] * ov[3];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 32; ++j)
-    if (j < r) z[j] = wave_sum(z[j]);
-}
-
-// (B_t z)[col] for one column
-template <typename T>
-__device__ __forceinline__ float lora_up_col(const CombineArgs& a, int col, const float (&z)[32]) {
-  const T* B = reinterpret_cast<const T*>(a.lora_B) + (long long)col * a.lora_r;
-  float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < 32; j += 4) {
-    if (j >= a.lora_r) break;
-    float bv[4];
-    load4f<T>(B + j, bv);
-    acc += bv[0] * z[j] + bv[1] * z[j + 1] + bv[2] * z[j + 2] + bv[3] * z[j + 3];
-  }
-  return acc;
-}
-// m = sum_j gate_j * Y[inv_j] + sum_s Y_shared_s;  h = A*h + B*e + a + m
-// ACT: cum += sigmoid(w . h); loops = t + 1.
-// One wave per row, all column vectors of the row at once (NV float4 per
-// lane), so the expert-output gathers of every column are in flight together;
-// the next loop's RMSNorm works from the registers that hold h' + e.
-// LAT (launches of a few hundred rows, where latency and not bandwidth sets
-// the time): the loads that need no expert offsets (routing entries; h, e, a
-// for rows of up to 1024 columns) are issued before the count scan, the
-// routed outputs are gathered two experts at a time, and lanes past D load
-// column 0 (never stored) so that no load sits behind a per-column branch.
-// This takes 2-3 times the registers, which costs occupancy on long launches.
-// Both forms add the same terms in the same order.
-template <typename T, int NV, bool LAT, bool LORA = false>
+template <typename T, int NV, bool LAT>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   constexpr bool PRE = LAT && NV <= 4;  // h, e, a ahead of the scan (registers)
   constexpr int KP = LAT ? 8 : 0;       // routing entries fetched ahead
@@ -407,8 +356,6 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       }
     }
   }
-  float lz[32];
-  if (LORA) lora_down_row<T>(a, i, lz);
   float z = 0.f, ss = 0.f;
 #pragma unroll
   for (int c = 0; c < NV; ++c) {
@@ -422,10 +369,6 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     if (a.d) {
       const float4 dv = *reinterpret_cast<const float4*>(a.d + (long long)i * D + col);
       m[c][0] += dv.x; m[c][1] += dv.y; m[c][2] += dv.z; m[c][3] += dv.w;
-    }
-    if (LORA) {
-      av[c].x += lora_up_col<T>(a, col, lz); av[c].y += lora_up_col<T>(a, col + 1, lz);
-      av[c].z += lora_up_col<T>(a, col + 2, lz); av[c].w += lora_up_col<T>(a, col + 3, lz);
     }
     const float4 Av = *reinterpret_cast<const float4*>(a.A + col);
     const float4 Bv = *reinterpret_cast<const float4*>(a.B + col);
@@ -481,7 +424,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 // their loads in flight). Every element adds the same terms in the same order
 // as k_combine; the per-lane partial sums of the halting dot product and of
 // the next RMSNorm run over the lane's own columns.
-template <int NV8, int EB, bool LORA = false>
+template <int NV8, int EB>
 __global__ __launch_bounds__(256) void k_combine8(CombineArgs a) {
   __shared__ int s_off[MAX_EXPERTS];
   __shared__ int s_keep;
@@ -550,8 +493,6 @@ __global__ __launch_bounds__(256) void k_combine8(CombineArgs a) {
         }
       }
     }
-    float lz[32];
-    if (LORA) lora_down_row<bf16_t>(a, i, lz);
     float z = 0.f, ss = 0.f;
 #pragma unroll
     for (int c = 0; c < NV8; ++c) {
@@ -562,11 +503,7 @@ __global__ __launch_bounds__(256) void k_combine8(CombineArgs a) {
         float* mm = m[c] + 4 * hh;
         const float4 hv = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + col);
         const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
-        float4 av = *reinterpret_cast<const float4*>(a.a + (long long)i * D + col);
-        if (LORA) {
-          av.x += lora_up_col<bf16_t>(a, col, lz); av.y += lora_up_col<bf16_t>(a, col + 1, lz);
-          av.z += lora_up_col<bf16_t>(a, col + 2, lz); av.w += lora_up_col<bf16_t>(a, col + 3, lz);
-        }
+        const float4 av = *reinterpret_cast<const float4*>(a.a + (long long)i * D + col);
         if (a.d) {
           const float4 dv = *reinterpret_cast<const float4*>(a.d + (long long)i * D + col);
           mm[0] += dv.x; mm[1] += dv.y; mm[2] += dv.z; mm[3] += dv.w;
@@ -622,46 +559,40 @@ __global__ __launch_bounds__(256) void k_combine8(CombineArgs a) {
   }
 }
 
-template <typename T, bool LAT, bool LORA>
+template <typename T, bool LAT>
 static hipError_t combine_nv(const CombineArgs& a, hipStream_t s) {
   dim3 grid((a.n + 3) / 4);
   const int nv = (a.D + 255) / 256;
-  if (nv <= 1) hipLaunchKernelGGL((k_combine<T, 1, LAT, LORA>), grid, dim3(256), 0, s, a);
-  else if (nv <= 2) hipLaunchKernelGGL((k_combine<T, 2, LAT, LORA>), grid, dim3(256), 0, s, a);
-  else if (nv <= 4) hipLaunchKernelGGL((k_combine<T, 4, LAT, LORA>), grid, dim3(256), 0, s, a);
-  else if (nv <= 8) hipLaunchKernelGGL((k_combine<T, 8, LAT, LORA>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_combine<T, 16, LAT, LORA>), grid, dim3(256), 0, s, a);
+  if (nv <= 1) hipLaunchKernelGGL((k_combine<T, 1, LAT>), grid, dim3(256), 0, s, a);
+  else if (nv <= 2) hipLaunchKernelGGL((k_combine<T, 2, LAT>), grid, dim3(256), 0, s, a);
+  else if (nv <= 4) hipLaunchKernelGGL((k_combine<T, 4, LAT>), grid, dim3(256), 0, s, a);
+  else if (nv <= 8) hipLaunchKernelGGL((k_combine<T, 8, LAT>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_combine<T, 16, LAT>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int NV8, int EB, bool LORA>
-static void combine8_launch(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_combine8<NV8, EB, LORA>), dim3((a.n + 3) / 4), dim3(256), 0, s, a);
-}
-
-template <typename T, bool LORA>
+template <typename T>
 static hipError_t combine_t(const CombineArgs& a, hipStream_t s) {
   // up to 2048 rows (512 workgroups, one round on the chip at LAT's occupancy)
-  if (a.n <= 2048) return combine_nv<T, true, LORA>(a, s);
+  if (a.n <= 2048) return combine_nv<T, true>(a, s);
   // long bf16 launches with whole 512-column vectors per row: 8 columns per
   // lane (measured on 8192 rows of 2048: 153 -> 137 us)
   if (sizeof(T) == 2 && a.ksplit <= 1 && a.D % 512 == 0 && a.D <= 4096) {
+    const dim3 grid((a.n + 3) / 4);
     switch (a.D / 512) {
-      case 1: combine8_launch<1, 5, LORA>(a, s); return hipGetLastError();
-      case 2: combine8_launch<2, 5, LORA>(a, s); return hipGetLastError();
-      case 4: combine8_launch<4, 5, LORA>(a, s); return hipGetLastError();
-      case 8: combine8_launch<8, 3, LORA>(a, s); return hipGetLastError();
+      case 1: hipLaunchKernelGGL((k_combine8<1, 5>), grid, dim3(256), 0, s, a); return hipGetLastError();
+      case 2: hipLaunchKernelGGL((k_combine8<2, 5>), grid, dim3(256), 0, s, a); return hipGetLastError();
+      case 4: hipLaunchKernelGGL((k_combine8<4, 5>), grid, dim3(256), 0, s, a); return hipGetLastError();
+      case 8: hipLaunchKernelGGL((k_combine8<8, 3>), grid, dim3(256), 0, s, a); return hipGetLastError();
       default: break;
     }
   }
-  return combine_nv<T, false, LORA>(a, s);
+  return combine_nv<T, false>(a, s);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
-  if (a.lora_o && (a.lora_r <= 0 || a.lora_r > 32 || a.lora_r % 4 || a.lora_hv % 4)) return hipErrorInvalidValue;
-  if (a.lora_o) return a.dtype == DT_F32 ? combine_t<float, true>(a, s) : combine_t<bf16_t, true>(a, s);
-  return a.dtype == DT_F32 ? combine_t<float, false>(a, s) : combine_t<bf16_t, false>(a, s);
+  return a.dtype == DT_F32 ? combine_t<float>(a, s) : combine_t<bf16_t>(a, s);
 }
 
 

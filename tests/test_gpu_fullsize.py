@@ -108,8 +108,8 @@ def test_fullsize(name):
 @pytest.mark.parametrize("name", ["dreamer", "dreamer_parallel"])
 def test_fullsize_dreamer(name):
     """The Dreamer workloads at the size bench.py times (sequential sublayers;
-    parallel sublayers with depth-wise LoRA, whose branches run on two
-    streams and whose LoRA term the combine adds): routing of every row
+    parallel sublayers with depth-wise LoRA, whose attention branch runs on a
+    second stream): routing of every row
     teacher-forced each loop, and on sampled rows of the first sequence the
     loop update from the GPU's own states (depth attention over the token's
     loops 0..t, sequence attention over its sequence)."""
