@@ -211,27 +211,6 @@ def combine_bytes(cfg: dict, counts_per_loop, elt: int, ksplit: int = 1) -> floa
     return tot / max(1, T)
 
 
-def source_hash(names) -> str:
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "recurrent_depth_transformer_amd", "csrc", n), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
-def traffic_from_profiles(workload: str):
-    """Per-launch HBM bytes of the dominant kernel from committed rocprofv3
-    counter runs, or None when absent or taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"expert_gate_up_{workload}_traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as fh:
-        rec = json.load(fh)
-    if rec.get("source_hash") != source_hash(DOMINANT_SOURCES):
-        return None
-    return rec.get("bytes_per_launch")
-
-
 def host_info() -> dict:
     """Threads the BLAS pools use, the CPU model and the BLAS library."""
     info = {"cpu_count": os.cpu_count(), "cpu_model": None, "blas": None, "threads": os.cpu_count() or 1}

@@ -625,13 +625,24 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
   // Order of an expert's tiles [tstart * ntn, (tstart + tlg) * ntn) in L.
   // 64-row down tiles (an expert has few rows, hence few m-tiles): m-tiles
   // innermost, so the m-tiles that stream one weight slab run side by side on
-  // one XCD and share it in L2. Otherwise n-tiles innermost: consecutive tiles
-  // share the A rows.
+  // one XCD and share it in L2. Gate/up: the n-tiles in bands of GUB, each
+  // band walked m-tile by m-tile with its n-tiles innermost. Tiles that share
+  // A rows start together, and so do (GUB tiles apart) tiles that share weight
+  // rows; L2 keeps data only for a few of the 32 k-stages of a tile, so tiles
+  // that start far apart fetch shared operands again (wide MoE shape: 2.7 ->
+  // 1.8 GB fetched per launch, 1-2 % faster). Otherwise n-tiles innermost.
   int mt, nt;
   if constexpr (KIND == 1 && BM == 64) {
     const int r = L - tstart * ntn;
     nt = r / tlg;
     mt = tstart + r % tlg;
+  } else if constexpr (KIND == 0) {
+    constexpr int GUB = 2;
+    const int r = L - tstart * ntn;
+    const int band = r / (tlg * GUB), rem = r % (tlg * GUB);
+    const int bsz = ntn - band * GUB < GUB ? ntn - band * GUB : GUB;
+    mt = tstart + rem / bsz;
+    nt = band * GUB + rem % bsz;
   } else {
     mt = q;
     nt = L % ntn;
