@@ -611,8 +611,13 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
 // Up to 2048-wide rows the kernel is held to 64 VGPRs (8 waves per SIMD), so
 // two 16-wave workgroups share a CU and all of a 8192-row launch is resident
 // at once (measured on 8192 x 2048: 75 -> 67 us).
-template <typename T, int NV>
-__global__ __launch_bounds__(1024, NV <= 8 ? 8 : 1) void k_norm_route(NormRouteArgs a) {
+// LAT (launches of up to a few thousand rows, one round of at most 256
+// workgroups): the kernel may use 128 VGPRs, and every term of a row and the
+// router weights of four k-steps are requested before any is used; the sums
+// are formed in the same order as in the bandwidth form, so both forms give
+// identical results.
+template <typename T, int NV, bool LAT>
+__global__ __launch_bounds__(1024, (NV <= 8 && !LAT) ? 8 : 1) void k_norm_route(NormRouteArgs a) {
   constexpr int KC = 4096 / (int)sizeof(T);        // columns per LDS chunk
   constexpr int LDA = KC + 16 / (int)sizeof(T);    // padded row stride
   __shared__ __align__(16) T As[16 * LDA];
@@ -627,6 +632,33 @@ __global__ __launch_bounds__(1024, NV <= 8 ? 8 : 1) void k_norm_route(NormRouteA
   const int tok = live ? (na.rows ? na.rows[i] : i) : 0;
   float x[NV][4];
   float ss = 0.f;
+  if constexpr (LAT) {
+#pragma unroll
+    for (int c = 0; c < NV; ++c) x[c][0] = x[c][1] = x[c][2] = x[c][3] = 0.f;
+    if (live) {   // one row per wave; column chunks below the last lie inside the row
+      float4 t[4][NV];
+      const float* src[4] = {na.h + (long long)tok * D, na.e + (long long)tok * D,
+                             na.a2 ? na.a2 + (long long)i * D : nullptr, na.a ? na.a + (long long)i * D : nullptr};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          const int col = (c * 64 + lane) * 4;
+          t[q][c] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (src[q] && (c < NV - 1 || col < D)) t[q][c] = *reinterpret_cast<const float4*>(src[q] + col);
+        }
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        // (h + e) + depth-attention output + attention output, as below
+        x[c][0] = t[0][c].x + t[1][c].x; x[c][1] = t[0][c].y + t[1][c].y;
+        x[c][2] = t[0][c].z + t[1][c].z; x[c][3] = t[0][c].w + t[1][c].w;
+#pragma unroll
+        for (int q = 2; q < 4; ++q)
+          if (src[q]) { x[c][0] += t[q][c].x; x[c][1] += t[q][c].y; x[c][2] += t[q][c].z; x[c][3] += t[q][c].w; }
+        ss += x[c][0] * x[c][0] + x[c][1] * x[c][1] + x[c][2] * x[c][2] + x[c][3] * x[c][3];
+      }
+    }
+  } else
 #pragma unroll
   for (int c = 0; c < NV; ++c) {
     const int col = (c * 64 + lane) * 4;
@@ -678,6 +710,32 @@ __global__ __launch_bounds__(1024, NV <= 8 ? 8 : 1) void k_norm_route(NormRouteA
     }
     __syncthreads();
     const int nstep = ck32 / 32;
+    if constexpr (LAT) {
+      // this wave's k-steps ks, ks + KS, ... four at a time: the weight
+      // fragments are fetched together (addresses clamped into the matrix,
+      // values zeroed where the expert or column does not exist), then
+      // multiplied in k-step order
+      const int my = nstep > ks ? (nstep - ks + KS - 1) / KS : 0;
+      const T* wrow = Wr + (long long)(en < E ? en : 0) * D;
+      for (int b0 = 0; b0 < my; b0 += 4) {
+        Frag<T> af[4], bf[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int kk = (ks + (b0 + u) * KS) * 32 + (lane >> 4) * 8;
+          const bool ok = en < E && b0 + u < my && kc0 + kk < D;
+          const uint4* q = reinterpret_cast<const uint4*>(wrow + (ok ? kc0 + kk : 0));
+#pragma unroll
+          for (int v = 0; v < (int)(sizeof(T) / 2); ++v) {
+            const uint4 w = q[v];
+            bf[u].v[v] = ok ? w : make_uint4(0, 0, 0, 0);
+          }
+          af[u] = frag_lds<T>(As + (lane & 15) * LDA + (b0 + u < my ? kk : 0));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (b0 + u < my) mma(acc, af[u], bf[u]);
+      }
+    } else
     for (int st = ks; st < nstep; st += KS) {
       const int kk = st * 32 + (lane >> 4) * 8;
       const Frag<T> af = frag_lds<T>(As + (lane & 15) * LDA + kk);
@@ -756,11 +814,20 @@ template <typename T>
 static hipError_t norm_route_t(const NormRouteArgs& a, hipStream_t s) {
   dim3 grid((a.norm.n + 15) / 16);
   const int nv = (a.norm.D + 255) / 256;
-  if (nv <= 1) hipLaunchKernelGGL((k_norm_route<T, 1>), grid, dim3(1024), 0, s, a);
-  else if (nv <= 2) hipLaunchKernelGGL((k_norm_route<T, 2>), grid, dim3(1024), 0, s, a);
-  else if (nv <= 4) hipLaunchKernelGGL((k_norm_route<T, 4>), grid, dim3(1024), 0, s, a);
-  else if (nv <= 8) hipLaunchKernelGGL((k_norm_route<T, 8>), grid, dim3(1024), 0, s, a);
-  else hipLaunchKernelGGL((k_norm_route<T, 16>), grid, dim3(1024), 0, s, a);
+  // up to 4096 rows of up to 1024 columns: at most 256 workgroups, one per CU,
+  // so the latency form's registers cost no occupancy that matters (wider
+  // rows would spill its four terms of NV vectors)
+  if (a.norm.n <= 4096 && nv <= 4) {
+    if (nv <= 1) hipLaunchKernelGGL((k_norm_route<T, 1, true>), grid, dim3(1024), 0, s, a);
+    else if (nv <= 2) hipLaunchKernelGGL((k_norm_route<T, 2, true>), grid, dim3(1024), 0, s, a);
+    else hipLaunchKernelGGL((k_norm_route<T, 4, true>), grid, dim3(1024), 0, s, a);
+    return hipGetLastError();
+  }
+  if (nv <= 1) hipLaunchKernelGGL((k_norm_route<T, 1, false>), grid, dim3(1024), 0, s, a);
+  else if (nv <= 2) hipLaunchKernelGGL((k_norm_route<T, 2, false>), grid, dim3(1024), 0, s, a);
+  else if (nv <= 4) hipLaunchKernelGGL((k_norm_route<T, 4, false>), grid, dim3(1024), 0, s, a);
+  else if (nv <= 8) hipLaunchKernelGGL((k_norm_route<T, 8, false>), grid, dim3(1024), 0, s, a);
+  else hipLaunchKernelGGL((k_norm_route<T, 16, false>), grid, dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 
