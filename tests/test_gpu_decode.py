@@ -58,10 +58,19 @@ def _prefill_decode(cfg, inputs, W, T):
     return h.reshape(B * S, D), loops.reshape(-1), idx.reshape(T, B * S, -1), S0
 
 
+# widths that are multiples of 8 but not of the k-stages, row chunks or tiles
+RAGGED = {"ragged_gqa": dict(base="gqa_small", dim=328, expert_dim=200),
+          "ragged_mla": dict(base="mla_small", dim=200, expert_dim=136)}
+
+
 @pytest.mark.parametrize("name", ["tiny", "tiny_bf16", "gqa_small", "mla_small", "act_small", "wide_small",
-                                  "dreamer_tiny", "dreamer_small", "parallel_small"])
+                                  "dreamer_tiny", "dreamer_small", "parallel_small"] + sorted(RAGGED))
 def test_prefill_then_decode_matches_full_forward(name):
-    cfg = get_config(name)
+    if name in RAGGED:
+        over = dict(RAGGED[name])
+        cfg = get_config(over.pop("base"), **over)
+    else:
+        cfg = get_config(name)
     T = cfg["T"]
     full, inputs, _, W = run_gpu(cfg, T=T)
     h, loops, idx, S0 = _prefill_decode(cfg, inputs, W, T)

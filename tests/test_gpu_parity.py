@@ -150,9 +150,25 @@ DEGENERATE = {
 }
 
 
+# Widths that are multiples of 8 but not of the 64-wide k-stages, the 256- and
+# 512-column row chunks or the output tiles: partial last chunks in the row
+# kernels, K tails in every GEMM, partial column tiles.
+RAGGED = {
+    "ragged_width": dict(base="gqa_small", dim=328, expert_dim=200),
+    "ragged_width_mla": dict(base="mla_small", dim=200, expert_dim=136),
+    "ragged_width_depth": dict(base="dreamer_small", dim=200, expert_dim=120),
+    "ragged_width_act": dict(base="act_small", dim=136, expert_dim=264),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RAGGED))
+def test_ragged_widths_forced(name):
+    test_degenerate_forced(name)
+
+
 @pytest.mark.parametrize("name", sorted(DEGENERATE))
 def test_degenerate_forced(name):
-    over = dict(DEGENERATE[name])
+    over = dict(DEGENERATE[name] if name in DEGENERATE else RAGGED[name])
     cfg = get_config(over.pop("base"), **over)
     T = cfg["T"]
     res, inp, *_ = run_gpu(cfg, T=T)
