@@ -1,5 +1,6 @@
 // Internal launch interface between the host orchestration (rdt_api.cpp) and
-// the HIP kernels (rdt_kernels.hip). Plain structs of device pointers and sizes.
+// the HIP kernels (rdt_gemm.hip, rdt_attention.hip, rdt_rows.hip). Plain
+// structs of device pointers and sizes.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -8,14 +9,12 @@ namespace rdt {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
-// Tile shapes the host must know to plan grids and the expert tile schedule.
-// Default tiles of the grouped expert GEMMs (rows per tile feed the schedule
-// computed by the permutation kernel; gate/up columns hold gate and up halves).
+// Tiles of the fp32 grouped expert GEMMs (the bf16 tiles are chosen per
+// launch from the rows per expert; gate/up columns hold gate and up halves).
 constexpr int GU_BM = 128;
 constexpr int GU_BN = 128;
 constexpr int DN_BM = 64;
 constexpr int DN_BN = 128;
-constexpr int ROUTER_BM = 64;
 constexpr int MAX_EXPERTS = 64;
 
 // ---------------------------------------------------------------- dense GEMM
