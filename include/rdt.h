@@ -365,9 +365,9 @@ typedef enum rdt_stage {
   RDT_STAGE_QKV = 1,      /* q/k/v projections (+RoPE); MLA latent projections and norms */
   RDT_STAGE_ATTN = 2,     /* causal flash attention (+ MLA value up-projection) */
   RDT_STAGE_OPROJ = 3,    /* output projection (+ depth-wise LoRA) */
-  RDT_STAGE_NORM2 = 4,    /* x = u + a, RMSNorm */
-  RDT_STAGE_ROUTER = 5,   /* router logits, softmax, top-k */
-  RDT_STAGE_PERMUTE = 6,  /* per-expert counts, offsets, stable permutation */
+  RDT_STAGE_NORM2 = 4,    /* reserved: x = u + a and its RMSNorm run inside the router launch */
+  RDT_STAGE_ROUTER = 5,   /* x = u + a, RMSNorm, router logits, softmax, top-k, expert slots */
+  RDT_STAGE_PERMUTE = 6,  /* reserved: per-expert counts and slots are taken inside the router launch */
   RDT_STAGE_EXPERT_GU = 7,   /* grouped gate/up GEMM + SwiGLU */
   RDT_STAGE_EXPERT_DOWN = 8, /* grouped down GEMM */
   RDT_STAGE_COMBINE = 9,  /* MoE combine + LTI injection (+ ACT halting and compaction) */
