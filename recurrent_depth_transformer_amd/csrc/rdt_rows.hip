@@ -627,6 +627,10 @@ __global__ __launch_bounds__(1024, (NV <= 8 && !LAT) ? 8 : 1) void k_norm_route(
   const NormArgs& na = a.norm;
   const int i = blockIdx.x * 16 + wave;
   const int n = na.ndev ? *na.ndev : na.n;
+  // the grid covers the static row count; under ACT fewer rows run, and a
+  // workgroup without any has nothing to do (uniform across the workgroup,
+  // before any barrier)
+  if ((int)blockIdx.x * 16 >= n) return;
   const int D = na.D, E = a.E, k = a.k;
   const bool live = i < n;
   const int tok = live ? (na.rows ? na.rows[i] : i) : 0;
