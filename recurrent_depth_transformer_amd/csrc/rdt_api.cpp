@@ -515,6 +515,10 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       aa.H = P.H; aa.KV = P.KV; aa.rows = cur; aa.seg = seg; aa.B = P.B;
       aa.S = f.decode ? f.max_seq : P.S; aa.dec = f.decode; aa.dec_pos = pos_dev;
       aa.scale = 1.f / sqrtf((float)P.d);
+      // ACT late loops: the running tokens of a sequence are spread over its
+      // positions, so a 32-row query slice walks the keys of its last token
+      // for all 32; 16-row slices halve that (act attention 66 -> 60 us per loop)
+      aa.narrow = act && t >= kActSmallTilesFrom;
       set_split(aa);
       LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, sa));
     } else {
@@ -574,6 +578,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       aa.H = P.H; aa.KV = 1; aa.rows = cur; aa.seg = seg; aa.B = P.B;
       aa.S = f.decode ? f.max_seq : P.S; aa.dec = f.decode; aa.dec_pos = pos_dev;
       aa.scale = 1.f / sqrtf((float)(P.nope + P.nr));
+      aa.narrow = act && t >= kActSmallTilesFrom;
       set_split(aa);
       LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, sa));
       // value up-projection per head: o[h] = o_lat[h] . Wuv[h]^T

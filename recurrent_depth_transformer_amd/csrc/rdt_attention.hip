@@ -465,7 +465,7 @@ static hipError_t attn_pick(const AttnArgs& a, hipStream_t s) {
   const int G = a.H / a.KV;
   const int nhb = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
   const long long blocks16 = (long long)(a.dec ? 1 : (a.S + 63) / 64) * a.B * a.H;  // 64 rows per block per head
-  const bool wide = blocks16 * 2 >= 1024;
+  const bool wide = blocks16 * 2 >= 1024 && !a.narrow;
   if (nhb == 4) return wide ? attn_launch<T, DQK, DV, 32, 4, VK>(a, s) : attn_launch<T, DQK, DV, 16, 4, VK>(a, s);
   if (nhb == 2) return wide ? attn_launch<T, DQK, DV, 32, 2, VK>(a, s) : attn_launch<T, DQK, DV, 16, 2, VK>(a, s);
   return wide ? attn_launch<T, DQK, DV, 32, 1, VK>(a, s) : attn_launch<T, DQK, DV, 16, 1, VK>(a, s);

@@ -119,6 +119,7 @@ struct AttnArgs {
   // (zero on entry, left zero) counts the finished ranges; the last one
   // forms o from all of them
   int nsplit; float* part_o; float* part_m; float* part_l; int* split_cnt;
+  int narrow;            // 16-row query slices even where the launch has blocks to spare
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
