@@ -221,6 +221,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave;
   const int n = a.ndev ? *a.ndev : a.n;
+  if (blockIdx.x > 0 && (int)blockIdx.x * 4 >= n) return;   // as in k_combine8
   const bool live = i < n;
   const int D = a.D, k = a.k;
   if (threadIdx.x == 0) s_keep = 0;
@@ -431,6 +432,10 @@ __global__ __launch_bounds__(256) void k_combine8(CombineArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave;
   const int n = a.ndev ? *a.ndev : a.n;
+  // the grid covers the static row count: past the running rows only
+  // workgroup 0 has work (clearing the next loop's counts); the ACT
+  // compaction involves only the workgroups that hold rows
+  if (blockIdx.x > 0 && (int)blockIdx.x * 4 >= n) return;
   const bool live = i < n;
   const int D = a.D, k = a.k;
   if (threadIdx.x == 0) s_keep = 0;
