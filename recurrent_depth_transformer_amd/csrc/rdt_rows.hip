@@ -1016,21 +1016,38 @@ __global__ __launch_bounds__(256) void k_depth_attention(DepthAttnArgs a) {
   float q[4] = {0.f, 0.f, 0.f, 0.f}, o[4] = {0.f, 0.f, 0.f, 0.f};
   if (on) load4f<T>(reinterpret_cast<const T*>(a.q) + (long long)i * a.H * dd + (long long)h * dd + e0, q);
   float mrun = -INFINITY, lrun = 0.f;
-  for (int tau = 0; tau <= a.t; ++tau) {
-    float k[4] = {0.f, 0.f, 0.f, 0.f}, v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (on) {
-      load4f<T>(reinterpret_cast<const T*>(a.k) + tau * a.lstride + kvoff, k);
-      load4f<T>(reinterpret_cast<const T*>(a.v) + tau * a.lstride + kvoff, v);
-    }
-    float s = q[0] * k[0] + q[1] * k[1] + q[2] * k[2] + q[3] * k[3];
-    for (int off = lph >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    s *= a.scale;
-    const float mnew = fmaxf(mrun, s);
-    const float alpha = expf(mrun - mnew), p = expf(s - mnew);
-    lrun = lrun * alpha + p;
+  const float sc2 = a.scale * 1.4426950408889634f;   // scale * log2(e)
+  // the keys and values of CH loops are requested before any is used (loop
+  // indices past t repeat loop t: valid addresses, no branch around the
+  // loads), then taken in loop order
+  constexpr int CH = 8;
+  for (int tau0 = 0; tau0 <= a.t; tau0 += CH) {
+    float k[CH][4], v[CH][4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) o[x] = o[x] * alpha + p * v[x];
-    mrun = mnew;
+    for (int u = 0; u < CH; ++u) {
+      const int tau = tau0 + u <= a.t ? tau0 + u : a.t;
+      const long long off = (long long)tau * a.lstride + (on ? kvoff : 0);
+      load4f<T>(reinterpret_cast<const T*>(a.k) + off, k[u]);
+      load4f<T>(reinterpret_cast<const T*>(a.v) + off, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      if (tau0 + u > a.t) break;
+      float kk[4] = {0.f, 0.f, 0.f, 0.f}, vv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (on) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) { kk[x] = k[u][x]; vv[x] = v[u][x]; }
+      }
+      float s = q[0] * kk[0] + q[1] * kk[1] + q[2] * kk[2] + q[3] * kk[3];
+      for (int off = lph >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+      s *= sc2;   // scores in the base-2 domain: softmax is unchanged
+      const float mnew = fmaxf(mrun, s);
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew), p = __builtin_amdgcn_exp2f(s - mnew);
+      lrun = lrun * alpha + p;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) o[x] = o[x] * alpha + p * vv[x];
+      mrun = mnew;
+    }
   }
   if (on) {
     const float inv = 1.f / lrun;
