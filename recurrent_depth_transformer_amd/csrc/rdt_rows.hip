@@ -886,9 +886,83 @@ __global__ __launch_bounds__(256) void k_mla_norm(MlaNormArgs a) {
   }
 }
 
+// The same arithmetic with every value a row needs requested before any is
+// used (c_q up to 64 * NQ columns, the latent of kvl <= 128 columns, its
+// 32-wide rope part and the RoPE factors), so a wave waits on one round trip
+// rather than one per pass.
+template <typename T, int NQ>
+__global__ __launch_bounds__(256) void k_mla_norm_batched(MlaNormArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave;
+  const int n = a.ndev ? *a.ndev : a.n;
+  if (i >= n) return;
+  const int tok = a.rows ? a.rows[i] : i;
+  const int W = a.kvl + a.nr, half = a.nr >> 1;
+  const float* cs = a.cq_raw + (long long)tok * a.ql;
+  const float* src = a.lat_raw + (long long)tok * W;
+  const int pos = a.pos_dev ? *a.pos_dev : tok % a.S;
+  float cq[NQ], gqv[NQ], lk[2], gk[2];
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    const int c = lane + 64 * u;
+    cq[u] = c < a.ql ? cs[c] : 0.f;
+    gqv[u] = c < a.ql ? a.gq[c] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = lane + 64 * u;
+    lk[u] = c < a.kvl ? src[c] : 0.f;
+    gk[u] = c < a.kvl ? a.gkv[c] : 0.f;
+  }
+  const bool rj = lane < half;
+  const int j = rj ? lane : 0;
+  const float x1 = src[a.kvl + j], x2 = src[a.kvl + j + half];
+  const float co = a.cosb[pos * half + j], sn = a.sinb[pos * half + j];
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) ss += cq[u] * cq[u];
+    ss = wave_sum(ss);
+    const float inv = 1.f / sqrtf(ss / (float)a.ql + a.eps);
+    T* dst = reinterpret_cast<T*>(a.cqn) + (long long)tok * a.ql;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int c = lane + 64 * u;
+      if (c < a.ql) dst[c] = ST<T>::from_f(cq[u] * inv * gqv[u]);
+    }
+  }
+  T* dst = reinterpret_cast<T*>(a.latent) + (long long)tok * W;
+  {
+    float ss = lk[0] * lk[0];
+    ss += lk[1] * lk[1];
+    ss = wave_sum(ss);
+    const float inv = 1.f / sqrtf(ss / (float)a.kvl + a.eps);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = lane + 64 * u;
+      if (c < a.kvl) dst[c] = ST<T>::from_f(lk[u] * inv * gk[u]);
+    }
+  }
+  if (rj) {
+    dst[a.kvl + j] = ST<T>::from_f(x1 * co - x2 * sn);
+    dst[a.kvl + j + half] = ST<T>::from_f(x1 * sn + x2 * co);
+  }
+}
+
 hipError_t launch_mla_norm(const MlaNormArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   dim3 grid((a.n + 3) / 4);
+  const int nq = (a.ql + 63) / 64;
+  if (a.kvl <= 128 && a.nr <= 128 && nq <= 8) {
+#define RDT_MN(Q)                                                                                  \
+    if (nq <= Q) {                                                                                 \
+      if (a.dtype == DT_F32) hipLaunchKernelGGL((k_mla_norm_batched<float, Q>), grid, dim3(256), 0, s, a); \
+      else hipLaunchKernelGGL((k_mla_norm_batched<bf16_t, Q>), grid, dim3(256), 0, s, a);          \
+      return hipGetLastError();                                                                    \
+    }
+    RDT_MN(2) RDT_MN(4) RDT_MN(6) RDT_MN(8)
+#undef RDT_MN
+  }
   if (a.dtype == DT_F32) hipLaunchKernelGGL(k_mla_norm<float>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_mla_norm<bf16_t>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -915,8 +989,48 @@ __global__ __launch_bounds__(256) void k_qrope(QRopeArgs a) {
   d[j + half] = ST<T>::from_f(x1 * sn + x2 * cs);
 }
 
+// bf16, 32-wide rope slices at 16-byte aligned offsets: one thread per (row,
+// head) moves the slice and its RoPE factors as 16-byte vectors; the same
+// arithmetic per element as k_qrope
+__global__ __launch_bounds__(256) void k_qrope_vec(QRopeArgs a) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int n = a.ndev ? *a.ndev : a.n;
+  const int i = (int)(gid / a.H), h = (int)(gid % a.H);
+  if (i >= n) return;
+  const int tok = a.rows ? a.rows[i] : i;
+  const int pos = a.pos_dev ? *a.pos_dev : tok % a.S;
+  const uint4* s = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.src) + (long long)i * a.src_ld +
+                                                  (long long)h * a.src_hs + a.src_off);
+  uint4* d = reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(a.dst) + (long long)i * a.dst_ld +
+                                      (long long)h * a.dst_hs + a.dst_off);
+  const float4* cb = reinterpret_cast<const float4*>(a.cosb + pos * 16);
+  const float4* sb = reinterpret_cast<const float4*>(a.sinb + pos * 16);
+  uint4 xr[4];
+  float4 cr[4], sr[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) { xr[v] = s[v]; cr[v] = cb[v]; sr[v] = sb[v]; }
+  const bf16_t* x = reinterpret_cast<const bf16_t*>(xr);
+  const float* co = reinterpret_cast<const float*>(cr);
+  const float* sn = reinterpret_cast<const float*>(sr);
+  bf16_t y[32];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float x1 = bf2f(x[j]), x2 = bf2f(x[j + 16]);
+    y[j] = f2bf(x1 * co[j] - x2 * sn[j]);
+    y[j + 16] = f2bf(x1 * sn[j] + x2 * co[j]);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) d[v] = reinterpret_cast<const uint4*>(y)[v];
+}
+
 hipError_t launch_qrope(const QRopeArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
+  if (a.dtype == DT_BF16 && a.nr == 32 && a.src_ld % 8 == 0 && a.src_hs % 8 == 0 && a.src_off % 8 == 0 &&
+      a.dst_ld % 8 == 0 && a.dst_hs % 8 == 0 && a.dst_off % 8 == 0) {
+    const long long tot = (long long)a.n * a.H;
+    hipLaunchKernelGGL(k_qrope_vec, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const long long tot = (long long)a.n * a.H * (a.nr / 2);
   dim3 grid((unsigned)((tot + 255) / 256));
   if (a.dtype == DT_F32) hipLaunchKernelGGL(k_qrope<float>, grid, dim3(256), 0, s, a);
