@@ -644,7 +644,7 @@ __global__ __launch_bounds__(1024, (NV <= 8 && !LAT) ? 8 : 1) void k_norm_route(
   if constexpr (LAT) {
 #pragma unroll
     for (int c = 0; c < NV; ++c) x[c][0] = x[c][1] = x[c][2] = x[c][3] = 0.f;
-    if (live) {   // one row per wave; column chunks below the last lie inside the row
+    if (live) {   // one row per wave (NV may exceed the row's chunks: every column is checked)
       float4 t[4][NV];
       const float* src[4] = {na.h + (long long)tok * D, na.e + (long long)tok * D,
                              na.a2 ? na.a2 + (long long)i * D : nullptr, na.a ? na.a + (long long)i * D : nullptr};
@@ -654,7 +654,7 @@ __global__ __launch_bounds__(1024, (NV <= 8 && !LAT) ? 8 : 1) void k_norm_route(
         for (int c = 0; c < NV; ++c) {
           const int col = (c * 64 + lane) * 4;
           t[q][c] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (src[q] && (c < NV - 1 || col < D)) t[q][c] = *reinterpret_cast<const float4*>(src[q] + col);
+          if (src[q] && col < D) t[q][c] = *reinterpret_cast<const float4*>(src[q] + col);
         }
 #pragma unroll
       for (int c = 0; c < NV; ++c) {

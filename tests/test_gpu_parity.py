@@ -158,6 +158,8 @@ RAGGED = {
     "ragged_width_mla": dict(base="mla_small", dim=200, expert_dim=136),
     "ragged_width_depth": dict(base="dreamer_small", dim=200, expert_dim=120),
     "ragged_width_act": dict(base="act_small", dim=136, expert_dim=264),
+    # three 256-column chunks, run by the four-chunk instantiations
+    "three_chunk_width": dict(base="gqa_small", dim=640, expert_dim=200),
 }
 
 
