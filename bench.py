@@ -75,8 +75,11 @@ def flops_per_token_loop(cfg: dict) -> dict:
     else:
         ql, kvl, nr = cfg["q_lora_rank"], cfg["kv_lora_rank"], cfg["qk_rope_head_dim"]
         nope, vd = cfg["qk_nope_head_dim"], cfg["v_head_dim"]
-        f["qkv"] = 2 * D * (ql + kvl + nr) + 2 * ql * H * (nope + nr) + 2 * H * nope * kvl
-        f["attention"] = 2 * H * (kvl + nr) * keys + 2 * H * kvl * keys + 2 * H * kvl * vd
+        # the query absorb and the value up-projection run inside the bf16
+        # attention launch, so they are counted with it (fp32 runs the absorb
+        # as a launch of its own)
+        f["qkv"] = 2 * D * (ql + kvl + nr) + 2 * ql * H * (nope + nr)
+        f["attention"] = 2 * H * nope * kvl + 2 * H * (kvl + nr) * keys + 2 * H * kvl * keys + 2 * H * kvl * vd
         hv = H * vd
     f["out_proj"] = 2 * hv * D + (2 * cfg["lora_rank"] * (hv + D) if cfg["lora_rank"] else 0)
     f["router"] = 2 * D * cfg["n_experts"]
@@ -348,8 +351,8 @@ def kernel_figures(cfg: dict, counts, stage_avg: dict, elt: int, peak_tf: float)
     """Per-kernel roofline figures from the per-stage launch times: the GEMMs
     and attention against the MFMA peak, the router and combine against HBM.
     A stage's time per loop is its mean launch time times its launches per
-    loop (the MLA attention stage also holds the value up-projection; its
-    FLOPs are counted with it)."""
+    loop (the MLA attention stage also holds the query absorb and the value
+    up-projection; their FLOPs are counted with it)."""
     fl = flops_per_token_loop(cfg)
     rows = active_rows(cfg, counts)
     mean_rows = sum(rows) / max(1, len(rows))

@@ -554,23 +554,8 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g2.nseg = 1; g2.seg[0] = GemmSeg{w.Wuq, P.H * qw, qfull, P.H * qw, 0, 0, 0};
       pick_tile(N, P.H * qw, 16, &g2.bm, &g2.bn);
       LAUNCH(RDT_STAGE_QKV, dense_gemm(g2, sa));
-      // absorb: q_lat[h] = q_nope[h] . Wuk[h]  (per head, B = Wuk[h]^T)
-      DenseGemm g3{};
-      g3.dtype = dt; g3.A = qfull; g3.lda = P.H * qw; g3.a_bstride = qw; g3.K = P.nope; g3.epi = EPI_STORE;
-      g3.rows = cur; g3.gather = 0; g3.M = N; g3.Mdev = ncur; g3.batch = P.H;
-      g3.nseg = 1; g3.seg[0] = GemmSeg{wukT, P.kvl, qattn, P.H * W, 0, 0, 0};
-      g3.b_bstride = (long long)P.kvl * P.nope; g3.c_bstride = W;
-      pick_tile(N, (long long)P.kvl * P.H, 16, &g3.bm, &g3.bn);
-      LAUNCH(RDT_STAGE_QKV, dense_gemm(g3, sa));
-      QRopeArgs qr{};
-      qr.dtype = dt; qr.src = qfull; qr.src_ld = P.H * qw; qr.src_hs = qw; qr.src_off = P.nope;
-      qr.dst = qattn; qr.dst_ld = P.H * W; qr.dst_hs = W; qr.dst_off = P.kvl;
-      qr.H = P.H; qr.nr = P.nr; qr.rows = cur; qr.ndev = ncur; qr.n = N;
-      qr.cosb = cosb; qr.sinb = sinb; qr.S = P.S; qr.pos_dev = pos_dev;
-      LAUNCH(RDT_STAGE_QKV, launch_qrope(qr, sa));
       AttnArgs aa{};
       aa.dtype = dt; aa.dqk = W; aa.dv = P.kvl;
-      aa.q = qattn; aa.q_ld = P.H * W; aa.q_hs = W;
       const char* lat_src = f.decode ? cache_at(t, 0) : latent;
       aa.k = lat_src; aa.k_ld = W; aa.k_hs = 0;
       aa.v = lat_src; aa.v_ld = W; aa.v_hs = 0;
@@ -580,7 +565,6 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       aa.scale = 1.f / sqrtf((float)(P.nope + P.nr));
       aa.narrow = act && t >= kActSmallTilesFrom;
       set_split(aa);
-      LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, sa));
       // value up-projection per head: o[h] = o_lat[h] . Wuv[h]^T
       DenseGemm g4{};
       g4.dtype = dt; g4.A = olat; g4.lda = P.H * P.kvl; g4.a_bstride = P.kvl; g4.K = P.kvl; g4.epi = EPI_STORE;
@@ -588,7 +572,33 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g4.nseg = 1; g4.seg[0] = GemmSeg{w.Wuv, P.vd, o, P.hv, 0, 0, 0};
       g4.b_bstride = (long long)P.vd * P.kvl; g4.c_bstride = P.vd;
       pick_tile(N, (long long)P.vd * P.H, 16, &g4.bm, &g4.bn);
-      LAUNCH(RDT_STAGE_ATTN, dense_gemm(g4, sa));
+      if (bf) {
+        // bf16: the attention kernel forms q from q_nope and q_pe (absorb and
+        // RoPE) and, outside key-range splits, applies Wuv itself
+        aa.qn = qfull; aa.qn_ld = P.H * qw; aa.qn_hs = qw; aa.nope = P.nope;
+        aa.wukT = wukT; aa.cosb = cosb; aa.sinb = sinb;
+        aa.wuv = w.Wuv; aa.vd = P.vd; aa.ov = o; aa.ov_ld = P.hv;
+        LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, sa));
+        if (aa.nsplit > 1) LAUNCH(RDT_STAGE_ATTN, dense_gemm(g4, sa));
+      } else {
+        // absorb: q_lat[h] = q_nope[h] . Wuk[h]  (per head, B = Wuk[h]^T)
+        DenseGemm g3{};
+        g3.dtype = dt; g3.A = qfull; g3.lda = P.H * qw; g3.a_bstride = qw; g3.K = P.nope; g3.epi = EPI_STORE;
+        g3.rows = cur; g3.gather = 0; g3.M = N; g3.Mdev = ncur; g3.batch = P.H;
+        g3.nseg = 1; g3.seg[0] = GemmSeg{wukT, P.kvl, qattn, P.H * W, 0, 0, 0};
+        g3.b_bstride = (long long)P.kvl * P.nope; g3.c_bstride = W;
+        pick_tile(N, (long long)P.kvl * P.H, 16, &g3.bm, &g3.bn);
+        LAUNCH(RDT_STAGE_QKV, dense_gemm(g3, sa));
+        QRopeArgs qr{};
+        qr.dtype = dt; qr.src = qfull; qr.src_ld = P.H * qw; qr.src_hs = qw; qr.src_off = P.nope;
+        qr.dst = qattn; qr.dst_ld = P.H * W; qr.dst_hs = W; qr.dst_off = P.kvl;
+        qr.H = P.H; qr.nr = P.nr; qr.rows = cur; qr.ndev = ncur; qr.n = N;
+        qr.cosb = cosb; qr.sinb = sinb; qr.S = P.S; qr.pos_dev = pos_dev;
+        LAUNCH(RDT_STAGE_QKV, launch_qrope(qr, sa));
+        aa.q = qattn; aa.q_ld = P.H * W; aa.q_hs = W;
+        LAUNCH(RDT_STAGE_ATTN, launch_attention(aa, sa));
+        LAUNCH(RDT_STAGE_ATTN, dense_gemm(g4, sa));
+      }
     }
 
     // a5: output projection (+ depth-wise LoRA as a second K phase)

@@ -20,7 +20,10 @@
 // Multi-latent attention in absorbed form is the same computation with one kv
 // head whose key is [c_kv | k_rope] and whose value is the c_kv prefix of the
 // same row, shared by every query head; in bf16 (VK) the V^T fragments are
-// then read from the K tile itself and no V tile is loaded.
+// then read from the K tile itself and no V tile is loaded. In that form the
+// kernel also builds its queries (q_nope Wuk[h] on the MFMA, RoPE on q_pe) and
+// applies the value up-projection Wuv[h] to its output rows, so neither the
+// absorbed queries nor o_lat go through HBM.
 #include "rdt_device.h"
 #include "rdt_launch.h"
 
@@ -102,6 +105,7 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
     const bool valid = qq < nq;
     const int i = qfirst + qq;
     qpos[qs] = valid ? tok(i) - b * S : -1;
+    if constexpr (VK) continue;  // formed from q_nope and q_pe below
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = ks * 32 + lg * 8;
@@ -329,12 +333,90 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
       }
     }
   };
+  // Absorbed MLA queries: q_lat^T = Wuk[h]^T q_nope^T on the MFMA (k = nope,
+  // in order, as a GEMM of the same operands), rounded to bf16 and staged with
+  // RoPE(q_pe) in this wave's rows of the K buffers (free until the first K
+  // tile is stored), then read back as the query fragments. Runs while the
+  // first K tile's loads are in flight; every wave takes part (barriers).
+  auto build_q = [&]() {
+    static_assert(!VK || (DQK == DV + 32 && NW * QW <= 2 * KT), "absorbed MLA: 32 rope dims, staging fits Ks");
+    if constexpr (VK) {
+      T* Qs = &Ks[0][0] + wave * QW * KLD;
+      const T* qn = reinterpret_cast<const T*>(a.qn);
+      const T* wk = reinterpret_cast<const T*>(a.wukT) + (long long)h * DV * a.nope;
+      constexpr int CB = DV / 16;
+      f32x4 qa[CB][QS];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) qa[cb][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < a.nope; k0 += 32) {
+        const int kk = k0 + lg * 8;
+        const bool kin = kk < a.nope;  // nope is a multiple of 8: a lane's 8 k values are all in or all out
+        Frag<T> bq[QS];
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) {
+          const int qq = qs * 16 + lc;
+          bq[qs] = (qq < nq && kin)
+                       ? frag_lds<T>(qn + (long long)(qfirst + qq) * a.qn_ld + (long long)h * a.qn_hs + kk)
+                       : frag_zero<T>();
+        }
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const Frag<T> wf = kin ? frag_lds<T>(wk + (long long)(cb * 16 + lc) * a.nope + kk) : frag_zero<T>();
+#pragma unroll
+          for (int qs = 0; qs < QS; ++qs) mma(qa[cb][qs], wf, bq[qs]);
+        }
+      }
+      // lane (lg, lc) holds q_lat[query qs*16 + lc][c = cb*16 + 4lg + 0..3]
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
+        T* qrow = Qs + (qs * 16 + lc) * KLD;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          *reinterpret_cast<uint2*>(qrow + cb * 16 + 4 * lg) =
+              make_uint2(pack_bf16x2(qa[cb][qs][0], qa[cb][qs][1]), pack_bf16x2(qa[cb][qs][2], qa[cb][qs][3]));
+        // RoPE pairs (j, j + 16), j = 4lg .. 4lg + 3, of the 32 rope dims
+        const int qq = qs * 16 + lc;
+        uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
+        if (qq < nq) {
+          const T* src = qn + (long long)(qfirst + qq) * a.qn_ld + (long long)h * a.qn_hs + a.nope;
+          const uint2 u1 = *reinterpret_cast<const uint2*>(src + 4 * lg);
+          const uint2 u2 = *reinterpret_cast<const uint2*>(src + 16 + 4 * lg);
+          const float4 c4 = *reinterpret_cast<const float4*>(a.cosb + qpos[qs] * 16 + 4 * lg);
+          const float4 s4 = *reinterpret_cast<const float4*>(a.sinb + qpos[qs] * 16 + 4 * lg);
+          const float x1[4] = {__uint_as_float(u1.x << 16), __uint_as_float(u1.x & 0xffff0000u),
+                               __uint_as_float(u1.y << 16), __uint_as_float(u1.y & 0xffff0000u)};
+          const float x2[4] = {__uint_as_float(u2.x << 16), __uint_as_float(u2.x & 0xffff0000u),
+                               __uint_as_float(u2.y << 16), __uint_as_float(u2.y & 0xffff0000u)};
+          const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+          float y1[4], y2[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {  // explicit roundings: the same in every instantiation
+            y1[r] = __fmaf_rn(x1[r], cs[r], -(x2[r] * sn[r]));
+            y2[r] = __fmaf_rn(x1[r], sn[r], x2[r] * cs[r]);
+          }
+          lo = make_uint2(pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]));
+          hi = make_uint2(pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]));
+        }
+        *reinterpret_cast<uint2*>(qrow + DV + 4 * lg) = lo;
+        *reinterpret_cast<uint2*>(qrow + DV + 16 + 4 * lg) = hi;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[qs][ks] = frag_lds<T>(Qs + (qs * 16 + lc) * KLD + ks * 32 + lg * 8);
+      __syncthreads();  // every wave holds its queries before the K tiles overwrite the staging
+    }
+  };
   if constexpr (QW == 16) {
     // tile kt sits in LDS buffer kt & 1; register set (kt & 1) receives tile
     // kt + 2 while tile kt is multiplied, and tile kt + 1 (in the other set,
     // loaded one tile earlier) is written to the other LDS buffer afterwards
     if (kt_begin < nkt) gload(kt_begin * KT, rk0, rv0);
     if (kt_begin + 1 < nkt) gload((kt_begin + 1) * KT, rk1, rv1);
+    build_q();
     if (kt_begin < nkt) sstore(0, rk0, rv0);
     __syncthreads();
     for (int kt = kt_begin; kt < nkt; kt += 2) {
@@ -351,10 +433,9 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
   } else {
     // wide query slices keep one tile in flight (fewer registers, more
     // workgroups per CU)
-    if (kt_begin < nkt) {
-      gload(kt_begin * KT, rk0, rv0);
-      sstore(0, rk0, rv0);
-    }
+    if (kt_begin < nkt) gload(kt_begin * KT, rk0, rv0);
+    build_q();
+    if (kt_begin < nkt) sstore(0, rk0, rv0);
     __syncthreads();
     for (int kt = kt_begin; kt < nkt; ++kt) {
       const int buf = (kt - kt_begin) & 1;
@@ -429,6 +510,55 @@ __global__ __launch_bounds__(NW * 64) void k_attention(AttnArgs a) {
     }
     return;
   }
+  if constexpr (VK) {
+    // value up-projection o = o_lat Wuv[h]^T on the MFMA, o_lat normalised and
+    // rounded to bf16 as a stored o_lat would be. The accumulators hold o_lat
+    // transposed, so a lane's 8 k-slots of k-step ks are c = 32ks + 4lg + 0..3
+    // and 32ks + 16 + 4lg + 0..3 (the layout of P above); the Wuv fragments
+    // are read in the same order.
+    constexpr int KC = DV / 32;
+    Frag<T> of[KC][QS];
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      const float inv = lrow[qs] > 0.f ? 1.f / lrow[qs] : 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) {
+        const f32x4& p0 = oacc[2 * ks][qs];
+        const f32x4& p1 = oacc[2 * ks + 1][qs];
+        of[ks][qs].v[0] = make_uint4(pack_bf16x2(p0[0] * inv, p0[1] * inv), pack_bf16x2(p0[2] * inv, p0[3] * inv),
+                                     pack_bf16x2(p1[0] * inv, p1[1] * inv), pack_bf16x2(p1[2] * inv, p1[3] * inv));
+      }
+    }
+    const T* wv = reinterpret_cast<const T*>(a.wuv) + (long long)h * a.vd * DV;
+    T* Ov = reinterpret_cast<T*>(a.ov);
+    for (int j0 = 0; j0 < a.vd; j0 += 16) {
+      const int j = j0 + lc;
+      f32x4 acc[QS];
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) acc[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) {
+        Frag<T> wf = frag_zero<T>();
+        if (j < a.vd) {
+          const T* p = wv + (long long)j * DV + 32 * ks + 4 * lg;
+          const uint2 lo = *reinterpret_cast<const uint2*>(p), hi = *reinterpret_cast<const uint2*>(p + 16);
+          wf.v[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) mma(acc[qs], wf, of[ks][qs]);
+      }
+      // lane (lg, lc): output columns j0 + 4lg + 0..3 of query qs*16 + lc
+      const int jr = j0 + 4 * lg;
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
+        const int qq = qs * 16 + lc;
+        if (qq >= nq || jr >= a.vd) continue;
+        float v[4] = {acc[qs][0], acc[qs][1], acc[qs][2], acc[qs][3]};
+        store4<T>(Ov + (long long)(qfirst + qq) * a.ov_ld + (long long)h * a.vd + jr, v);
+      }
+    }
+    return;
+  }
   T* O = reinterpret_cast<T*>(a.o);
 #pragma unroll
   for (int qs = 0; qs < QS; ++qs) {
@@ -477,6 +607,10 @@ static hipError_t attn_dispatch(const AttnArgs& a, hipStream_t s) {
   // bf16 absorbed MLA: the value is the prefix of the key row; its V^T
   // fragments are read from the K tile
   const bool vk = sizeof(T) == 2 && a.v == a.k && a.v_ld == a.k_ld && a.v_hs == a.k_hs && dv <= dq;
+  const bool split = a.dec && a.nsplit > 1;
+  if (vk && (!a.qn || !a.wukT || !a.cosb || !a.sinb || a.nope <= 0 || a.nope % 8 ||
+             (!split && (!a.wuv || !a.ov || a.vd <= 0 || a.vd % 8))))
+    return hipErrorInvalidValue;
   if (dq == 16 && dv == 16) return attn_pick<T, 16, 16, false>(a, s);
   if (dq == 32 && dv == 32) return attn_pick<T, 32, 32, false>(a, s);
   if (dq == 64 && dv == 64) return attn_pick<T, 64, 64, false>(a, s);

@@ -120,6 +120,17 @@ struct AttnArgs {
   // forms o from all of them
   int nsplit; float* part_o; float* part_m; float* part_l; int* split_cnt;
   int narrow;            // 16-row query slices even where the launch has blocks to spare
+  // bf16 absorbed MLA (v == k): the kernel forms its queries itself, and
+  // outside key-range splits also the value up-projection. Query row i of
+  // head h is [q_nope Wuk[h] | RoPE(q_pe)] with q_nope = qn[i*qn_ld + h*qn_hs
+  // + (0..nope)], q_pe the 32 values after it, wukT[h] = Wuk[h]^T ([dv][nope]
+  // per head) and the RoPE factors of position p at cosb/sinb[p*16 + j]; q
+  // is then unused. Without a split, row i of head h is written as
+  // o_lat Wuv[h]^T to ov[i*ov_ld + h*vd + (0..vd)] (wuv: [H][vd][dv]) and o
+  // is unused; with one, o receives o_lat as for any other head.
+  const void* qn; int qn_ld, qn_hs, nope;
+  const void* wukT; const float* cosb; const float* sinb;
+  const void* wuv; int vd; void* ov; int ov_ld;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
