@@ -29,7 +29,11 @@ __device__ __forceinline__ void rope_entry(float* cosb, float* sinb, int dr, flo
   sinb[g] = sn;
 }
 
-template <typename T>
+// NV = float4 vectors per lane that cover a row (D <= 256 * NV). Rows up to
+// 1024 wide (NV <= 4) request all of their h, e and a vectors before using any
+// (addresses clamped into the row, so no branch guards a load); wider rows
+// take them a vector at a time. The sums are formed in the same order either way.
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row_blocks = (a.n + 3) / 4;
@@ -53,21 +57,52 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
   if (i >= n) return;
   const int tok = a.rows ? a.rows[i] : i;
   const int D = a.D;
-  float x[MAXV][4];
+  float x[NV][4];
   float ss = 0.f;
+  if constexpr (NV <= 4) {
+    float4 hv[NV], ev[NV], av[NV];
 #pragma unroll
-  for (int c = 0; c < MAXV; ++c) {
-    const int col = (c * 64 + lane) * 4;
-    if (col < D) {
-      const float4 hv = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + col);
-      if (a.h_copy) *reinterpret_cast<float4*>(a.h_copy + (long long)tok * D + col) = hv;
-      const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
-      x[c][0] = hv.x + ev.x; x[c][1] = hv.y + ev.y; x[c][2] = hv.z + ev.z; x[c][3] = hv.w + ev.w;
-      if (a.a) {
-        const float4 av = *reinterpret_cast<const float4*>(a.a + (long long)i * D + col);
-        x[c][0] += av.x; x[c][1] += av.y; x[c][2] += av.z; x[c][3] += av.w;
+    for (int c = 0; c < NV; ++c) {
+      const int col = (c * 64 + lane) * 4;
+      const int cc = col < D ? col : D - 4;
+      hv[c] = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + cc);
+      ev[c] = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + cc);
+    }
+    if (a.a) {
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        const int col = (c * 64 + lane) * 4;
+        av[c] = *reinterpret_cast<const float4*>(a.a + (long long)i * D + (col < D ? col : D - 4));
       }
-      ss += x[c][0] * x[c][0] + x[c][1] * x[c][1] + x[c][2] * x[c][2] + x[c][3] * x[c][3];
+    }
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      const int col = (c * 64 + lane) * 4;
+      if (col < D) {
+        if (a.h_copy) *reinterpret_cast<float4*>(a.h_copy + (long long)tok * D + col) = hv[c];
+        x[c][0] = hv[c].x + ev[c].x; x[c][1] = hv[c].y + ev[c].y; x[c][2] = hv[c].z + ev[c].z;
+        x[c][3] = hv[c].w + ev[c].w;
+        if (a.a) {
+          x[c][0] += av[c].x; x[c][1] += av[c].y; x[c][2] += av[c].z; x[c][3] += av[c].w;
+        }
+        ss += x[c][0] * x[c][0] + x[c][1] * x[c][1] + x[c][2] * x[c][2] + x[c][3] * x[c][3];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      const int col = (c * 64 + lane) * 4;
+      if (col < D) {
+        const float4 hv = *reinterpret_cast<const float4*>(a.h + (long long)tok * D + col);
+        if (a.h_copy) *reinterpret_cast<float4*>(a.h_copy + (long long)tok * D + col) = hv;
+        const float4 ev = *reinterpret_cast<const float4*>(a.e + (long long)tok * D + col);
+        x[c][0] = hv.x + ev.x; x[c][1] = hv.y + ev.y; x[c][2] = hv.z + ev.z; x[c][3] = hv.w + ev.w;
+        if (a.a) {
+          const float4 av = *reinterpret_cast<const float4*>(a.a + (long long)i * D + col);
+          x[c][0] += av.x; x[c][1] += av.y; x[c][2] += av.z; x[c][3] += av.w;
+        }
+        ss += x[c][0] * x[c][0] + x[c][1] * x[c][1] + x[c][2] * x[c][2] + x[c][3] * x[c][3];
+      }
     }
   }
   ss = wave_sum(ss);
@@ -75,7 +110,7 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
   T* out = reinterpret_cast<T*>(a.out) + (long long)(a.out_scatter ? tok : i) * D;
   T* dump = a.dump ? reinterpret_cast<T*>(a.dump) + (long long)tok * D : nullptr;
 #pragma unroll
-  for (int c = 0; c < MAXV; ++c) {
+  for (int c = 0; c < NV; ++c) {
     const int col = (c * 64 + lane) * 4;
     if (col < D) {
       const float4 gv = *reinterpret_cast<const float4*>(a.g + col);
@@ -87,14 +122,24 @@ __global__ __launch_bounds__(256) void k_norm(NormArgs a) {
   }
 }
 
+template <typename T>
+static void norm_nv(const NormArgs& a, dim3 grid, hipStream_t s) {
+  if (a.D <= 256) hipLaunchKernelGGL((k_norm<T, 1>), grid, dim3(256), 0, s, a);
+  else if (a.D <= 512) hipLaunchKernelGGL((k_norm<T, 2>), grid, dim3(256), 0, s, a);
+  else if (a.D <= 1024) hipLaunchKernelGGL((k_norm<T, 4>), grid, dim3(256), 0, s, a);
+  else if (a.D <= 2048) hipLaunchKernelGGL((k_norm<T, 8>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_norm<T, MAXV>), grid, dim3(256), 0, s, a);
+}
+
 hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   long long extra = 0;
   for (int j = 0; j < 2; ++j)
     if (a.rope_cos[j]) extra += (long long)a.rope_S[j] * (a.rope_dr[j] / 2);
   dim3 grid((unsigned)((a.n + 3) / 4 + (extra + 255) / 256));
-  if (a.dtype == DT_F32) hipLaunchKernelGGL(k_norm<float>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_norm<bf16_t>, grid, dim3(256), 0, s, a);
+  if (a.D > 256 * MAXV) return hipErrorInvalidValue;
+  if (a.dtype == DT_F32) norm_nv<float>(a, grid, s);
+  else norm_nv<bf16_t>(a, grid, s);
   return hipGetLastError();
 }
 
