@@ -61,7 +61,8 @@ def _prefill_decode(cfg, inputs, W, T):
 # widths that are multiples of 8 but not of the k-stages, row chunks or tiles
 RAGGED = {"ragged_gqa": dict(base="gqa_small", dim=328, expert_dim=200),
           "ragged_mla": dict(base="mla_small", dim=200, expert_dim=136),
-          "three_chunk_gqa": dict(base="gqa_small", dim=640, expert_dim=200)}
+          "three_chunk_gqa": dict(base="gqa_small", dim=640, expert_dim=200),
+          "ragged_heads_mla": dict(base="mla_small", qk_nope_head_dim=40, v_head_dim=24)}
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_bf16", "gqa_small", "mla_small", "act_small", "wide_small",

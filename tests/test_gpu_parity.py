@@ -160,6 +160,9 @@ RAGGED = {
     "ragged_width_act": dict(base="act_small", dim=136, expert_dim=264),
     # three 256-column chunks, run by the four-chunk instantiations
     "three_chunk_width": dict(base="gqa_small", dim=640, expert_dim=200),
+    # MLA head widths off the MFMA blocks: a half-empty last k-step of the
+    # query absorb (nope 40) and a half-empty last block of value columns (24)
+    "ragged_heads_mla": dict(base="mla_small", qk_nope_head_dim=40, v_head_dim=24),
 }
 
 
