@@ -362,8 +362,11 @@ rdt_status rdt_expert_depths(const int32_t* expert_counts, int32_t T, int32_t E,
 /* Stages of one loop iteration, for rdt_profile_forward. */
 typedef enum rdt_stage {
   RDT_STAGE_NORM1 = 0,    /* u = h + e, RMSNorm */
-  RDT_STAGE_QKV = 1,      /* q/k/v projections (+RoPE); MLA latent projections and norms */
-  RDT_STAGE_ATTN = 2,     /* causal flash attention (+ MLA value up-projection) */
+  RDT_STAGE_QKV = 1,      /* q/k/v projections (+RoPE); MLA latent projections and norms
+                             (fp32 MLA: also the query absorb and the query RoPE) */
+  RDT_STAGE_ATTN = 2,     /* causal flash attention (bf16 MLA: with the query absorb, the
+                             query RoPE and the value up-projection; fp32 MLA: with the
+                             value up-projection) */
   RDT_STAGE_OPROJ = 3,    /* output projection (+ depth-wise LoRA) */
   RDT_STAGE_NORM2 = 4,    /* reserved: x = u + a and its RMSNorm run inside the router launch */
   RDT_STAGE_ROUTER = 5,   /* x = u + a, RMSNorm, router logits, softmax, top-k, expert slots */
