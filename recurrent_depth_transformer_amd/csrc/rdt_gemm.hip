@@ -63,7 +63,6 @@ __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[S::FM][S::FN], char* 
     for (int j = 0; j < S::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint4 ra[S::A_LD], rb[S::B_LD];
-  const uint4 zero = make_uint4(0, 0, 0, 0);
 #define RDT_GLOAD(KT)                                                                  \
   {                                                                                    \
     const bool ph2 = TWO && (KT) >= nk1;                                               \

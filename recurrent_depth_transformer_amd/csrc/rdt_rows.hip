@@ -854,7 +854,7 @@ __global__ __launch_bounds__(1024, (NV <= 8 && !LAT) ? 8 : 1) void k_norm_route(
     local = atomicAdd(&s_cnt[ex], 1);
   }
   __syncthreads();
-  if (threadIdx.x < E && s_cnt[threadIdx.x] > 0) s_base[threadIdx.x] = atomicAdd(&a.cnt[threadIdx.x], s_cnt[threadIdx.x]);
+  if ((int)threadIdx.x < E && s_cnt[threadIdx.x] > 0) s_base[threadIdx.x] = atomicAdd(&a.cnt[threadIdx.x], s_cnt[threadIdx.x]);
   __syncthreads();
   if (ex >= 0) {
     const int sl = s_base[ex] + local;
