@@ -89,13 +89,16 @@ def flops_per_token_loop(cfg: dict) -> dict:
 
 def gate_up_kernel(cfg: dict) -> str:
     """Name of the gate/up launch the library picks for this workload: fp32
-    128x128; bf16 64x64 under 64 rows per expert, 160x128 up to 128, else
-    192x128 (the tile rule of the library's host code)."""
+    128x128; bf16 64x64 under 64 rows per expert, 160x128 up to 128, 192x128
+    under 256, else the eight-wave 256x256 ping-pong tile (the tile rule of the
+    library's host code)."""
     if cfg["dtype"] == "f32":
         return "k_grouped_gemm<f32,128,128,0,2,4>"
     rows = cfg["batch"] * cfg["seq"] * cfg["top_k"] / cfg["n_experts"]
     if rows < 64:
         return "k_grouped_gemm<bf16,64,64,0,3,4>"
+    if rows >= 256:
+        return "k_grouped_gemm<bf16,256,256,0,2,8>"
     return "k_grouped_gemm<bf16,160,128,0,2,4>" if rows <= 128 else "k_grouped_gemm<bf16,192,128,0,2,4>"
 
 

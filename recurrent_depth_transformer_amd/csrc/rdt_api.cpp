@@ -389,8 +389,11 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   // than 128x128), 64x32 for decode, else 64x64 with a three-stage ring.
   const long long rows_per_expert = (long long)N * k / E;
   const bool bf = dt == DT_BF16;
-  const int gu_bm = bf ? (rows_per_expert < 64 ? 64 : rows_per_expert <= 128 ? 160 : 192) : GU_BM;
-  const int gu_bn = bf && rows_per_expert < 64 ? 64 : GU_BN;
+  // Experts that see 256 rows or more on average: 256x256 ping-pong tiles for
+  // both projections (eight waves, one workgroup per CU; see rdt_gemm.hip).
+  const bool pp = bf && rows_per_expert >= 256;
+  const int gu_bm = pp ? 256 : bf ? (rows_per_expert < 64 ? 64 : rows_per_expert <= 128 ? 160 : 192) : GU_BM;
+  const int gu_bn = pp ? 256 : bf && rows_per_expert < 64 ? 64 : GU_BN;
   const int dn_bm = (rows_per_expert >= 256 && bf) ? 128 : 64;
   // grid bound of a grouped GEMM with bm-row tiles: sum_e ceil(c_e / bm) over
   // the routed experts is at most N*k/bm + E; each shared expert adds ceil(N/bm)
@@ -661,7 +664,8 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     const long long ystride = (long long)N * (k + P.Se) * D;
     gd.ksplit = P.ksplit; gd.part = P.ksplit > 1 ? reinterpret_cast<float*>(ybuf) : nullptr; gd.pstride = ystride;
     // many rows per expert: large tiles; few rows: small tiles, deeper ring
-    if (dn_bm == 128) { gd.bm = 192; gd.bn = 128; gd.ns = 2; }
+    if (pp) { gd.bm = 256; gd.bn = 256; gd.ns = 2; }
+    else if (dn_bm == 128) { gd.bm = 192; gd.bn = 128; gd.ns = 2; }
     else { gd.bm = 64; gd.bn = rows_per_expert < 64 && bf ? 32 : 64; gd.ns = 3; }
     gd.max_mtiles = max_mtiles(gd.bm);
     LAUNCH(RDT_STAGE_EXPERT_DOWN, launch_grouped_gemm(gd, s));

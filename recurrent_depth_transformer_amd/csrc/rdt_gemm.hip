@@ -330,6 +330,132 @@ __device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[S::FM][S::FN], flo
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 256x256 tiles on eight waves in two groups of four ("ping-pong").
+//
+// The k loop walks 64-wide blocks of the A and B rows (128 bytes per row, the
+// layout and load slots of LdsRing<256, 256, 2, 8>: two 64 KB buffers). Group g
+// (waves 4g..4g+3, one on each SIMD) owns tile rows 128g..128g+127; its wave q
+// owns columns 64q..64q+63, a 128x64 wave tile of 8x4 16x16 fragments. Each
+// block is used in two 32-wide half-steps. In every half-step a group first
+// reads that half-step's fragments from LDS into registers (memory phase) and
+// then runs its 32 MFMAs from registers only (compute phase). The two groups
+// are one phase apart, so on each SIMD one wave issues MFMAs while the other
+// waits on LDS, and a workgroup barrier separates the phases.
+//
+// Why this shape: a CU pulls global->LDS data at a fixed rate of cache-line
+// requests (about 0.44 lines per clock), so the bytes per MFMA of the tile set
+// the ceiling. A 256x256 tile needs 64 KB per 64-k block for 8.4 MFLOP, against
+// 40 KB for 3.1 MFLOP with a 192x128 tile. 128-byte row segments keep each
+// request a whole line (64-byte segments halve the rate).
+//
+// Loads of block j+1 are issued by both groups at the first half-step of block
+// j, into the buffer block j-1 used (read by both groups before the preceding
+// barrier); every wave waits for its own loads of block j+1 and zeroes its
+// chunks past K before the barrier that opens block j+1's first memory phase.
+// ---------------------------------------------------------------------------
+using PPRing = LdsRing<256, 256, 2, 8>;
+
+// 32 KB slots of the ping-pong ring: five of them (all 160 KB of a CU's LDS).
+// Part p of the k loop (p = 2j: the 256 A rows of 64-k block j, p = 2j + 1:
+// its 256 B rows; 128 bytes per row) lives in slot p % 5. A slot is refilled
+// once both groups have read the part before it. At the first half-step of
+// block j every wave issues B of block j + 1 and A of block j + 2, so 96 KB
+// are in flight while block j is multiplied.
+constexpr int PP_SLOT = 256 * 128;
+
+__device__ __forceinline__ void gemm_mainloop_pp(f32x4 (&acc)[8][4], char* ring,
+                                                 const bf16_t* (&ap)[PPRing::AL], const bf16_t* (&bp)[PPRing::BL],
+                                                 int K, const bf16_t* adummy, const bf16_t* bdummy) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave >> 2, q = wave & 3;
+  const int kchunk = ((tid & 7) ^ ((tid >> 4) & 7)) * 8;  // logical k offset this lane loads
+  const int nkb = (K + 63) >> 6;
+  const int nh = 2 * nkb;
+  const uint32_t rbase = (uint32_t)(uintptr_t)(lds_char*)ring + wave * 1024;
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto slot = [](int p) { return p % 5; };
+  auto issue_a = [&](int kb) {
+    const int k = kb * 64 + kchunk;
+    const uint32_t st = rbase + slot(2 * kb) * PP_SLOT;
+#pragma unroll
+    for (int i = 0; i < PPRing::AL; ++i)
+      dma16((ap[i] != nullptr && k < K) ? ap[i] + k : adummy, st + i * PPRing::RB);
+  };
+  auto issue_b = [&](int kb) {
+    const int k = kb * 64 + kchunk;
+    const uint32_t st = rbase + slot(2 * kb + 1) * PP_SLOT;
+#pragma unroll
+    for (int i = 0; i < PPRing::BL; ++i)
+      dma16((bp[i] != nullptr && k < K) ? bp[i] + k : bdummy, st + i * PPRing::RB);
+  };
+  // This wave's loads of block kb are in LDS: the only loads issued after its
+  // B rows are the A rows of block kb + 1 (vector-memory loads of a wave
+  // complete in order). Chunks past K are then zeroed.
+  auto land = [&](int kb) {
+    if (kb + 1 < nkb) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (kb * 64 + kchunk < K) return;
+    char* sa = ring + slot(2 * kb) * PP_SLOT + tid * 16;
+    char* sb = ring + slot(2 * kb + 1) * PP_SLOT + tid * 16;
+#pragma unroll
+    for (int i = 0; i < PPRing::AL; ++i) *reinterpret_cast<uint4*>(sa + i * PPRing::RB) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < PPRing::BL; ++i) *reinterpret_cast<uint4*>(sb + i * PPRing::RB) = make_uint4(0, 0, 0, 0);
+  };
+  auto bar = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int lrow = lane & 15, sw = (lrow >> 1) & 7;
+  Frag<bf16_t> fa[8], fb[4];
+
+  issue_a(0);
+  issue_b(0);
+  if (1 < nkb) issue_a(1);
+  land(0);
+  bar();
+  if (g == 1) bar();
+  for (int h = 0; h < nh; ++h) {
+    const int kb = h >> 1;
+    // memory phase
+    if (!(h & 1)) {
+      if (kb + 1 < nkb) issue_b(kb + 1);
+      if (kb + 2 < nkb) issue_a(kb + 2);
+    }
+    {
+      const char* sa = ring + slot(2 * kb) * PP_SLOT;
+      const char* sb = ring + slot(2 * kb + 1) * PP_SLOT;
+      const int off = lrow * 128 + ((((h & 1) * 4 + (lane >> 4)) ^ sw) << 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fa[i].v[0] = *reinterpret_cast<const uint4*>(sa + (128 * g + 16 * i) * 128 + off);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j].v[0] = *reinterpret_cast<const uint4*>(sb + (64 * q + 16 * j) * 128 + off);
+    }
+    if (g == 1 && (h & 1) && kb + 1 < nkb) land(kb + 1);
+    bar();
+    // compute phase
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mma(acc[i][j], fa[i], fb[j]);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g == 0 && (h & 1) && kb + 1 < nkb) land(kb + 1);
+    bar();
+  }
+  if (g == 0) bar();
+}
+
 // ============================================================== dense GEMM
 template <typename T, int BM, int BN, bool TWO, int NS, int NW>
 __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) void k_dense_gemm(DenseGemm g) {
@@ -408,7 +534,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
 #pragma unroll 1
   for (int c = 0; c < BM / S::CR; ++c) {
     acc_to_lds<T, BM, BN, NW>(acc, Cs, c);
-    __syncthreads();
+    lds_barrier();
     const int rbase = m0 + c * S::CR;
     const int nrows = S::CR;
     if (g.epi == EPI_STORE) {
@@ -513,7 +639,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
         if (re.dump_gap) re.dump_gap[tok] = gap;
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -571,12 +697,6 @@ template <typename T, int BM, int BN, int KIND, int NS, int NW>
 __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) void k_grouped_gemm(GroupedGemm g) {
   static_assert(sizeof(T) == 2 || NW == 4, "the fp32 path runs four waves");
   using S = GemmShape<T, BM, BN, NW>;
-  constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS, NW>::STAGE : S::SMEM;
-  __shared__ __align__(16) char L0[ST];
-  __shared__ __align__(16) char L1[sizeof(T) == 2 ? ST : 16];
-  __shared__ __align__(16) char L2[sizeof(T) == 2 && NS > 2 ? ST : 16];
-  __shared__ __align__(16) char L3[sizeof(T) == 2 && NS > 3 ? ST : 16];
-  char* smem = L0;
   const int G = g.E + g.Se;
   const int n = g.ndev ? *g.ndev : g.n_static;
   // KIND 0 produces BN/2 SwiGLU outputs per tile from BN/2 gate + BN/2 up rows
@@ -674,8 +794,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
 #pragma unroll
     for (int i = 0; i < S::B_LD; ++i) {
       const int c = (tid + i * S::NT) / S::VPR;
-      const int f = n0 + (c % (BN / 2));
-      bp[i] = f < g.N ? ((c < BN / 2 ? wg : wu) + (long long)f * g.K) : nullptr;
+      // 256x256 tiles: wave q's 64 columns are the gate then the up rows of
+      // features n0 + 32q .. +31, so one lane holds both halves of an output;
+      // other tiles: the gate rows of the BN/2 features, then their up rows
+      const bool up = BM == 256 ? ((c & 63) >= 32) : (c >= BN / 2);
+      const int f = n0 + (BM == 256 ? 32 * (c >> 6) + (c & 31) : c % (BN / 2));
+      bp[i] = f < g.N ? ((up ? wu : wg) + (long long)f * g.K) : nullptr;
     }
   } else {
     const T* wd = reinterpret_cast<const T*>(routed ? g.W1 : g.S1) + (routed ? grp : grp - g.E) * wsz;
@@ -686,6 +810,108 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
     }
   }
 
+  if constexpr (BM == 256) {  // 256x256 ping-pong tiles (bf16, eight waves)
+    const T* bd = bp[0] ? bp[0] : reinterpret_cast<const T*>(routed ? g.W1 : g.S1);
+    int Kl = g.K;
+    if (KIND == 1 && gridDim.y > 1) {   // K slice blockIdx.y of gridDim.y (whole 64-wide blocks)
+      const int Ks = (((g.K + 63) / 64 + (int)gridDim.y - 1) / (int)gridDim.y) * 64;
+      const int k0 = (int)blockIdx.y * Ks;
+      Kl = g.K - k0 < Ks ? g.K - k0 : Ks;
+#pragma unroll
+      for (int i = 0; i < S::A_LD; ++i)
+        if (ap[i]) ap[i] += k0;
+#pragma unroll
+      for (int i = 0; i < S::B_LD; ++i)
+        if (bp[i]) bp[i] += k0;
+    }
+    __shared__ __align__(16) char ring[5 * PP_SLOT];
+    f32x4 acc[8][4];
+    gemm_mainloop_pp(acc, ring, ap, bp, Kl, A, bd);
+    // Epilogue, wave by wave (no workgroup barrier): the wave's outputs go
+    // through its own 20 KB slice of the ring (free once every wave has passed
+    // the loop's last barrier) and out as 16-byte row vectors. Rows of the
+    // wave: tile rows 128g .. 128g + 127.
+    constexpr int WSLICE = 5 * PP_SLOT / 8;
+    const int lane = tid & 63, wave = tid >> 6, wg = wave >> 2, wq = wave & 3;
+    char* wbuf = ring + wave * WSLICE;
+    auto wave_lds_sync = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+    if constexpr (KIND == 0) {
+      // SwiGLU of features n0 + 32wq .. +31: fragments 0, 1 hold the gate and
+      // 2, 3 the up projections of the same 16-feature columns
+      constexpr int P = 40;  // staging row pitch (bf16)
+      static_assert(128 * P * 2 <= WSLICE, "SwiGLU staging exceeds the wave's slice");
+      bf16_t* sb = reinterpret_cast<bf16_t*>(wbuf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gt = acc[i][jj][r], up = acc[i][jj + 2][r];
+            sb[(16 * i + 4 * (lane >> 4) + r) * P + 16 * jj + (lane & 15)] = f2bf(gt / (1.f + expf(-gt)) * up);
+          }
+      wave_lds_sync();
+      T* C = reinterpret_cast<T*>(g.C);
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int v = lane + 64 * it, row = v >> 2, c4 = v & 3;
+        const int m = ml0 + 128 * wg + row, f = n0 + 32 * wq + 8 * c4;
+        const uint4 val = *reinterpret_cast<const uint4*>(sb + row * P + 8 * c4);
+        if (m < rows_g && f < g.N) *reinterpret_cast<uint4*>(C + (long long)(pbase + m) * g.ldc + f) = val;
+      }
+    } else if (gridDim.y == 1) {
+      constexpr int P = 72;  // staging row pitch (bf16)
+      static_assert(128 * P * 2 <= WSLICE, "output staging exceeds the wave's slice");
+      bf16_t* sb = reinterpret_cast<bf16_t*>(wbuf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sb[(16 * i + 4 * (lane >> 4) + r) * P + 16 * j + (lane & 15)] = f2bf(acc[i][j][r]);
+      wave_lds_sync();
+      T* C = reinterpret_cast<T*>(g.C);
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int v = lane + 64 * it, row = v >> 3, c8 = v & 7;
+        const int m = ml0 + 128 * wg + row, col = n0 + 64 * wq + 8 * c8;
+        const uint4 val = *reinterpret_cast<const uint4*>(sb + row * P + 8 * c8);
+        if (m < rows_g && col < g.N) *reinterpret_cast<uint4*>(C + (long long)(pbase + m) * g.ldc + col) = val;
+      }
+    } else {  // K slice: float partial sums, 64 rows at a time
+      constexpr int P = 68;  // staging row pitch (float)
+      static_assert(64 * P * 4 <= WSLICE, "partial-sum staging exceeds the wave's slice");
+      float* sf = reinterpret_cast<float*>(wbuf);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              sf[(16 * i + 4 * (lane >> 4) + r) * P + 16 * j + (lane & 15)] = acc[4 * half + i][j][r];
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          const int v = lane + 64 * it, row = v >> 4, c4 = v & 15;
+          const int m = ml0 + 128 * wg + 64 * half + row, col = n0 + 64 * wq + 4 * c4;
+          const float4 val = *reinterpret_cast<const float4*>(sf + row * P + 4 * c4);
+          if (m < rows_g && col < g.N)
+            *reinterpret_cast<float4*>(g.part + (long long)blockIdx.y * g.pstride + (long long)(pbase + m) * g.ldc + col) = val;
+        }
+        wave_lds_sync();
+      }
+    }
+    return;
+  } else {
+  constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS, NW>::STAGE : S::SMEM;
+  __shared__ __align__(16) char L0[ST];
+  __shared__ __align__(16) char L1[sizeof(T) == 2 ? ST : 16];
+  __shared__ __align__(16) char L2[sizeof(T) == 2 && NS > 2 ? ST : 16];
+  __shared__ __align__(16) char L3[sizeof(T) == 2 && NS > 3 ? ST : 16];
+  char* smem = L0;
   f32x4 acc[S::FM][S::FN];
   if constexpr (sizeof(T) == 2) {
     const T* bd = bp[0] ? bp[0] : reinterpret_cast<const T*>(routed ? g.W1 : g.S1);
@@ -713,7 +939,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
 #pragma unroll 1
   for (int c = 0; c < BM / S::CR; ++c) {
     acc_to_lds<T, BM, BN, NW>(acc, Cs, c);
-    __syncthreads();
+    lds_barrier();
     const int nrows = S::CR;
     for (int idx = tid; idx < nrows * (OUTW / 8); idx += S::NT) {
       const int r = idx / (OUTW / 8), c8 = (idx % (OUTW / 8)) * 8;
@@ -737,7 +963,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
       else
         store8<T>(C + (long long)(pbase + m) * g.ldc + col, v);
     }
-    __syncthreads();
+    lds_barrier();
+  }
   }
 }
 
@@ -762,6 +989,9 @@ static hipError_t grouped_dispatch(const GroupedGemm& g, hipStream_t s) {
     RDT_G(0, 64, 64, 3) RDT_G(0, 128, 128, 2) RDT_G(0, 160, 128, 2) RDT_G(0, 192, 128, 2)
     RDT_G(1, 64, 32, 3) RDT_G(1, 64, 64, 3) RDT_G(1, 64, 64, 4) RDT_G(1, 192, 128, 2)
 #undef RDT_G
+    // 256x256 ping-pong tiles: eight waves, one workgroup per CU
+    if (g.bm == 256 && g.bn == 256 && g.ns == 2)
+      return g.kind == 0 ? grouped_launch<T, 256, 256, 0, 2, 8>(g, s) : grouped_launch<T, 256, 256, 1, 2, 8>(g, s);
     return hipErrorInvalidValue;
   }
 }
