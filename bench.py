@@ -89,15 +89,18 @@ def flops_per_token_loop(cfg: dict) -> dict:
 
 def gate_up_kernel(cfg: dict) -> str:
     """Name of the gate/up launch the library picks for this workload: fp32
-    128x128; bf16 64x64 under 64 rows per expert, 160x128 up to 128, 192x128
-    under 256, else the eight-wave 256x256 ping-pong tile (the tile rule of the
-    library's host code)."""
+    128x128; bf16 64x64 under 64 rows per expert, 160x128 up to 128, the
+    eight-wave 256x256 ping-pong tile from 256 rows when the launch has at
+    least four rounds of such tiles over 256 CUs, else 192x128 (the tile rule
+    of the library's host code)."""
     if cfg["dtype"] == "f32":
         return "k_grouped_gemm<f32,128,128,0,2,4>"
     rows = cfg["batch"] * cfg["seq"] * cfg["top_k"] / cfg["n_experts"]
     if rows < 64:
         return "k_grouped_gemm<bf16,64,64,0,3,4>"
-    if rows >= 256:
+    n_tok = cfg["batch"] * cfg["seq"]
+    mt = n_tok * cfg["top_k"] // 256 + cfg["n_experts"] // 2 + cfg["n_shared_experts"] * -(-n_tok // 256)
+    if rows >= 256 and mt * -(-cfg["expert_dim"] // 128) >= 4 * 256:
         return "k_grouped_gemm<bf16,256,256,0,2,8>"
     return "k_grouped_gemm<bf16,160,128,0,2,4>" if rows <= 128 else "k_grouped_gemm<bf16,192,128,0,2,4>"
 

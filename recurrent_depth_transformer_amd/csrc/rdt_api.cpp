@@ -389,11 +389,20 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
   // than 128x128), 64x32 for decode, else 64x64 with a three-stage ring.
   const long long rows_per_expert = (long long)N * k / E;
   const bool bf = dt == DT_BF16;
-  // Experts that see 256 rows or more on average: 256x256 ping-pong tiles for
-  // both projections (eight waves, one workgroup per CU; see rdt_gemm.hip).
-  const bool pp = bf && rows_per_expert >= 256;
-  const int gu_bm = pp ? 256 : bf ? (rows_per_expert < 64 ? 64 : rows_per_expert <= 128 ? 160 : 192) : GU_BM;
-  const int gu_bn = pp ? 256 : bf && rows_per_expert < 64 ? 64 : GU_BN;
+  // Experts that see 256 rows or more on average: 256x256 ping-pong tiles
+  // (eight waves, one workgroup per CU; see rdt_gemm.hip) for a projection
+  // that yields at least four rounds of such tiles over 256 CUs. With fewer,
+  // the last round leaves CUs idle and two 192x128 workgroups per CU do better
+  // (measured on the MLA expert shape: down projection, about 544 tiles, 123
+  // against 105 us; wide MoE, 2560 tiles each: gate/up 683 against 799 us,
+  // down 352 against 412 us).
+  auto pp_rounds_ok = [&](int outw, int ncols) {
+    const long long mt = (long long)N * k / 256 + E / 2 + (long long)P.Se * ((N + 255) / 256);
+    return bf && rows_per_expert >= 256 && mt * ((ncols + outw - 1) / outw) >= 4 * 256;
+  };
+  const bool pp_gu = pp_rounds_ok(128, P.F), pp_dn = pp_rounds_ok(256, D) && P.ksplit <= 1;
+  const int gu_bm = pp_gu ? 256 : bf ? (rows_per_expert < 64 ? 64 : rows_per_expert <= 128 ? 160 : 192) : GU_BM;
+  const int gu_bn = pp_gu ? 256 : bf && rows_per_expert < 64 ? 64 : GU_BN;
   const int dn_bm = (rows_per_expert >= 256 && bf) ? 128 : 64;
   // grid bound of a grouped GEMM with bm-row tiles: sum_e ceil(c_e / bm) over
   // the routed experts is at most N*k/bm + E; each shared expert adds ceil(N/bm)
@@ -664,7 +673,7 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
     const long long ystride = (long long)N * (k + P.Se) * D;
     gd.ksplit = P.ksplit; gd.part = P.ksplit > 1 ? reinterpret_cast<float*>(ybuf) : nullptr; gd.pstride = ystride;
     // many rows per expert: large tiles; few rows: small tiles, deeper ring
-    if (pp) { gd.bm = 256; gd.bn = 256; gd.ns = 2; }
+    if (pp_dn) { gd.bm = 256; gd.bn = 256; gd.ns = 2; }
     else if (dn_bm == 128) { gd.bm = 192; gd.bn = 128; gd.ns = 2; }
     else { gd.bm = 64; gd.bn = rows_per_expert < 64 && bf ? 32 : 64; gd.ns = 3; }
     gd.max_mtiles = max_mtiles(gd.bm);

@@ -55,7 +55,10 @@ def test_dense_and_expert_flops_of_the_gqa_workload():
 
 def test_gate_up_kernel_label_follows_rows_per_expert():
     assert bench.gate_up_kernel(get_config("gqa")) == "k_grouped_gemm<bf16,160,128,0,2,4>"      # 128 rows
-    assert bench.gate_up_kernel(get_config("mla")) == "k_grouped_gemm<bf16,256,256,0,2,8>"      # 1024 rows
+    # 1024 rows, 72 row tiles x 11 column tiles of 256x256: under four rounds of 256
+    assert bench.gate_up_kernel(get_config("mla")) == "k_grouped_gemm<bf16,192,128,0,2,4>"
+    # 1024 rows, 320 row tiles x 8 column tiles
+    assert bench.gate_up_kernel(get_config("wide_moe")) == "k_grouped_gemm<bf16,256,256,0,2,8>"
     assert bench.gate_up_kernel(get_config("gqa_small")) == "k_grouped_gemm<bf16,64,64,0,3,4>"  # 40 rows
     assert bench.gate_up_kernel(get_config("tiny")) == "k_grouped_gemm<f32,128,128,0,2,4>"
 
