@@ -435,13 +435,23 @@ __device__ __forceinline__ void gemm_mainloop_pp(f32x4 (&acc)[8][4], char* ring,
       const char* sa = ring + slot(2 * kb) * PP_SLOT;
       const char* sb = ring + slot(2 * kb + 1) * PP_SLOT;
       const int off = lrow * 128 + ((((h & 1) * 4 + (lane >> 4)) ^ sw) << 4);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) fa[i].v[0] = *reinterpret_cast<const uint4*>(sa + (128 * g + 16 * i) * 128 + off);
+      // B first: the first MFMAs need only the B fragments and one A fragment
 #pragma unroll
       for (int j = 0; j < 4; ++j) fb[j].v[0] = *reinterpret_cast<const uint4*>(sb + (64 * q + 16 * j) * 128 + off);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fa[i].v[0] = *reinterpret_cast<const uint4*>(sa + (128 * g + 16 * i) * 128 + off);
     }
-    if (g == 1 && (h & 1) && kb + 1 < nkb) land(kb + 1);
-    bar();
+    // Group 1's reads of a block's second half are the block's last: they
+    // must land before the barrier after which its slots are refilled. Other
+    // reads may still be in flight (each MFMA waits for its own fragments).
+    if (g == 1 && (h & 1)) {
+      if (kb + 1 < nkb) land(kb + 1);
+      bar();
+    } else {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // compute phase
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
