@@ -360,11 +360,12 @@ using PPRing = LdsRing<256, 256, 2, 8>;
 // 32 KB slots of the ping-pong ring: five of them (all 160 KB of a CU's LDS).
 // Part p of the k loop (p = 2j: the 256 A rows of 64-k block j, p = 2j + 1:
 // its 256 B rows; 128 bytes per row) lives in slot p % 5. A slot is refilled
-// once both groups have read the part before it. At the first half-step of
-// block j every wave issues B of block j + 1 and A of block j + 2, so 96 KB
-// are in flight while block j is multiplied.
+// once both groups have read the part five before it. Every wave issues B of
+// block j + 1 at the first half-step of block j and A of block j + 2 at the
+// second, so up to 96 KB are in flight while block j is multiplied.
 constexpr int PP_SLOT = 256 * 128;
 
+template <bool HALF>
 __device__ __forceinline__ void gemm_mainloop_pp(f32x4 (&acc)[8][4], char* ring,
                                                  const bf16_t* (&ap)[PPRing::AL], const bf16_t* (&bp)[PPRing::BL],
                                                  int K, const bf16_t* adummy, const bf16_t* bdummy) {
@@ -426,20 +427,25 @@ __device__ __forceinline__ void gemm_mainloop_pp(f32x4 (&acc)[8][4], char* ring,
   if (g == 1) bar();
   for (int h = 0; h < nh; ++h) {
     const int kb = h >> 1;
-    // memory phase
-    if (!(h & 1)) {
-      if (kb + 1 < nkb) issue_b(kb + 1);
-      if (kb + 2 < nkb) issue_a(kb + 2);
-    }
+    // memory phase: this half-step's fragment reads, then (after them, so
+    // the reads start first) B of block kb + 1 at the first half-step and A
+    // of block kb + 2 at the second
     {
       const char* sa = ring + slot(2 * kb) * PP_SLOT;
       const char* sb = ring + slot(2 * kb + 1) * PP_SLOT;
       const int off = lrow * 128 + ((((h & 1) * 4 + (lane >> 4)) ^ sw) << 4);
       // B first: the first MFMAs need only the B fragments and one A fragment
+      if (!HALF || g == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j].v[0] = *reinterpret_cast<const uint4*>(sb + (64 * q + 16 * j) * 128 + off);
+        for (int j = 0; j < 4; ++j) fb[j].v[0] = *reinterpret_cast<const uint4*>(sb + (64 * q + 16 * j) * 128 + off);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) fa[i].v[0] = *reinterpret_cast<const uint4*>(sa + (128 * g + 16 * i) * 128 + off);
+        for (int i = 0; i < 8; ++i) fa[i].v[0] = *reinterpret_cast<const uint4*>(sa + (128 * g + 16 * i) * 128 + off);
+      }
+    }
+    if (!(h & 1)) {
+      if (kb + 1 < nkb) issue_b(kb + 1);
+    } else {
+      if (kb + 2 < nkb) issue_a(kb + 2);
     }
     // Group 1's reads of a block's second half are the block's last: they
     // must land before the barrier after which its slots are refilled. Other
@@ -454,10 +460,12 @@ __device__ __forceinline__ void gemm_mainloop_pp(f32x4 (&acc)[8][4], char* ring,
     }
     // compute phase
     __builtin_amdgcn_s_setprio(1);
+    if (!HALF || g == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mma(acc[i][j], fa[i], fb[j]);
+        for (int j = 0; j < 4; ++j) mma(acc[i][j], fa[i], fb[j]);
+    }
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if (g == 0 && (h & 1) && kb + 1 < nkb) land(kb + 1);
@@ -836,7 +844,11 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
     }
     __shared__ __align__(16) char ring[5 * PP_SLOT];
     f32x4 acc[8][4];
-    gemm_mainloop_pp(acc, ring, ap, bp, Kl, A, bd);
+    // an expert's last tile with at most 128 rows of data: group 1's half of
+    // the tile holds none, so it skips its fragment reads and MFMAs (a
+    // separate instantiation keeps both loops free of branches)
+    if (rows_g - ml0 <= 128) gemm_mainloop_pp<true>(acc, ring, ap, bp, Kl, A, bd);
+    else gemm_mainloop_pp<false>(acc, ring, ap, bp, Kl, A, bd);
     // Epilogue, wave by wave (no workgroup barrier): the wave's outputs go
     // through its own 20 KB slice of the ring (free once every wave has passed
     // the loop's last barrier) and out as 16-byte row vectors. Rows of the
