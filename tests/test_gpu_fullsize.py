@@ -188,3 +188,26 @@ def test_fullsize_decode_last_position(name):
         assert err <= TOL
     dev = float(np.max(np.abs(last - hf[:, S - 1]))) / rms(hf[:, S - 1])
     print(f"[fullsize-decode] {name}: decode vs full forward max|dh|/rms={dev:.3e}", flush=True)
+
+
+def test_expert_tiles_ragged_many_rows():
+    """The 256x256 expert tiles at widths off their blocks: 256 sequences of 128
+    tokens, dim 328 and expert width 200 (k-blocks of 64 and column tiles of
+    128 / 256 end part-way), 8 experts top-4, so experts see ~16 384 rows and
+    both projections have over four rounds of 256x256 tiles (the rule that
+    selects them). Routing of every row teacher-forced each loop; end to end
+    on the first and last sequence against the oracle with routing forced."""
+    import bench
+    cfg = get_config("gqa_small", batch=256, seq=128, dim=328, expert_dim=200, n_experts=8, top_k=4, T=2)
+    T, N = cfg["T"], cfg["batch"] * cfg["seq"]
+    mt = N * cfg["top_k"] // 256 + cfg["n_experts"] // 2
+    assert mt * -(-cfg["expert_dim"] // 128) >= 1024 and mt * -(-cfg["dim"] // 256) >= 1024
+    assert bench.gate_up_kernel(cfg) == "k_grouped_gemm<bf16,256,256,0,2,8>"
+    print(f"[tiles] ragged 256x256 expert tiles: {N} tokens, dim 328, F 200", flush=True)
+    res, inp, *_ = run_gpu(cfg, T=T)
+    assert np.all(np.isfinite(res["h"]))
+    stats = {}
+    mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro, stats)
+    print(f"[tiles] routing mismatches={mism} near_ties={near} compared={comp}", flush=True)
+    assert mism == 0
+    assert end_to_end_prefix("ragged_tiles", cfg, inp, res, T, P=cfg["seq"]) <= TOL
