@@ -334,9 +334,10 @@ __device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[S::FM][S::FN], flo
 // ---------------------------------------------------------------------------
 // bf16 256x256 tiles on eight waves in two groups of four ("ping-pong").
 //
-// The k loop walks 64-wide blocks of the A and B rows (128 bytes per row, the
-// layout and load slots of LdsRing<256, 256, 2, 8>: two 64 KB buffers). Group g
-// (waves 4g..4g+3, one on each SIMD) owns tile rows 128g..128g+127; its wave q
+// The k loop walks 64-wide blocks of the A and B rows (128 bytes per row, in
+// the row layout, chunk swizzle and per-wave load slots of LdsRing<256, 256,
+// 2, 8>, held in the five-slot ring below). Group g (waves 4g..4g+3, one on
+// each SIMD) owns tile rows 128g..128g+127; its wave q
 // owns columns 64q..64q+63, a 128x64 wave tile of 8x4 16x16 fragments. Each
 // block is used in two 32-wide half-steps. In every half-step a group first
 // reads that half-step's fragments from LDS into registers (memory phase) and
@@ -350,10 +351,8 @@ __device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[S::FM][S::FN], flo
 // 40 KB for 3.1 MFLOP with a 192x128 tile. 128-byte row segments keep each
 // request a whole line (64-byte segments halve the rate).
 //
-// Loads of block j+1 are issued by both groups at the first half-step of block
-// j, into the buffer block j-1 used (read by both groups before the preceding
-// barrier); every wave waits for its own loads of block j+1 and zeroes its
-// chunks past K before the barrier that opens block j+1's first memory phase.
+// Every wave waits for its own loads of block j+1 and zeroes its chunks past K
+// before the barrier that opens block j+1's first memory phase.
 // ---------------------------------------------------------------------------
 using PPRing = LdsRing<256, 256, 2, 8>;
 
