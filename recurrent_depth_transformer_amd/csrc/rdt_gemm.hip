@@ -827,20 +827,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
     }
   }
 
-  if constexpr (BM == 256) {  // 256x256 ping-pong tiles (bf16, eight waves)
+  if constexpr (BM == 256) {  // 256x256 ping-pong tiles (bf16, eight waves, no K slices)
     const T* bd = bp[0] ? bp[0] : reinterpret_cast<const T*>(routed ? g.W1 : g.S1);
-    int Kl = g.K;
-    if (KIND == 1 && gridDim.y > 1) {   // K slice blockIdx.y of gridDim.y (whole 64-wide blocks)
-      const int Ks = (((g.K + 63) / 64 + (int)gridDim.y - 1) / (int)gridDim.y) * 64;
-      const int k0 = (int)blockIdx.y * Ks;
-      Kl = g.K - k0 < Ks ? g.K - k0 : Ks;
-#pragma unroll
-      for (int i = 0; i < S::A_LD; ++i)
-        if (ap[i]) ap[i] += k0;
-#pragma unroll
-      for (int i = 0; i < S::B_LD; ++i)
-        if (bp[i]) bp[i] += k0;
-    }
+    const int Kl = g.K;
     __shared__ __align__(16) char ring[5 * PP_SLOT];
     f32x4 acc[8][4];
     // an expert's last tile with at most 128 rows of data: group 1's half of
@@ -880,7 +869,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
         const uint4 val = *reinterpret_cast<const uint4*>(sb + row * P + 8 * c4);
         if (m < rows_g && f < g.N) *reinterpret_cast<uint4*>(C + (long long)(pbase + m) * g.ldc + f) = val;
       }
-    } else if (gridDim.y == 1) {
+    } else {
       constexpr int P = 72;  // staging row pitch (bf16)
       static_assert(128 * P * 2 <= WSLICE, "output staging exceeds the wave's slice");
       bf16_t* sb = reinterpret_cast<bf16_t*>(wbuf);
@@ -899,30 +888,6 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
         const int m = ml0 + 128 * wg + row, col = n0 + 64 * wq + 8 * c8;
         const uint4 val = *reinterpret_cast<const uint4*>(sb + row * P + 8 * c8);
         if (m < rows_g && col < g.N) *reinterpret_cast<uint4*>(C + (long long)(pbase + m) * g.ldc + col) = val;
-      }
-    } else {  // K slice: float partial sums, 64 rows at a time
-      constexpr int P = 68;  // staging row pitch (float)
-      static_assert(64 * P * 4 <= WSLICE, "partial-sum staging exceeds the wave's slice");
-      float* sf = reinterpret_cast<float*>(wbuf);
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              sf[(16 * i + 4 * (lane >> 4) + r) * P + 16 * j + (lane & 15)] = acc[4 * half + i][j][r];
-        wave_lds_sync();
-#pragma unroll
-        for (int it = 0; it < 16; ++it) {
-          const int v = lane + 64 * it, row = v >> 4, c4 = v & 15;
-          const int m = ml0 + 128 * wg + 64 * half + row, col = n0 + 64 * wq + 4 * c4;
-          const float4 val = *reinterpret_cast<const float4*>(sf + row * P + 4 * c4);
-          if (m < rows_g && col < g.N)
-            *reinterpret_cast<float4*>(g.part + (long long)blockIdx.y * g.pstride + (long long)(pbase + m) * g.ldc + col) = val;
-        }
-        wave_lds_sync();
       }
     }
     return;
@@ -1010,9 +975,11 @@ static hipError_t grouped_dispatch(const GroupedGemm& g, hipStream_t s) {
     RDT_G(0, 64, 64, 3) RDT_G(0, 128, 128, 2) RDT_G(0, 160, 128, 2) RDT_G(0, 192, 128, 2)
     RDT_G(1, 64, 32, 3) RDT_G(1, 64, 64, 3) RDT_G(1, 64, 64, 4) RDT_G(1, 192, 128, 2)
 #undef RDT_G
-    // 256x256 ping-pong tiles: eight waves, one workgroup per CU
-    if (g.bm == 256 && g.bn == 256 && g.ns == 2)
+    // 256x256 ping-pong tiles: eight waves, one workgroup per CU, no K slices
+    if (g.bm == 256 && g.bn == 256 && g.ns == 2) {
+      if (g.ksplit > 1) return hipErrorInvalidValue;
       return g.kind == 0 ? grouped_launch<T, 256, 256, 0, 2, 8>(g, s) : grouped_launch<T, 256, 256, 1, 2, 8>(g, s);
+    }
     return hipErrorInvalidValue;
   }
 }
