@@ -221,7 +221,11 @@ size_t rdt_workspace_size(const rdt_handle* h, int32_t T);
 rdt_status rdt_spectral_radius(const float* A_host, int32_t dim, float* rho);
 
 /* Use captured HIP graphs for the T-loop (enabled != 0, the default) or launch
- * the kernels one by one. Both produce bit-identical results. */
+ * the kernels one by one. Both produce bit-identical results. A graph is
+ * captured once per set of pointers (inputs, weights, out, aux, workspace) and
+ * T and replayed while they repeat; the handle keeps the last 16. A caller that
+ * passes a new out (or workspace) address every call captures every call:
+ * reuse the buffers to replay. */
 rdt_status rdt_set_graph_mode(rdt_handle* h, int32_t enabled);
 
 /*

@@ -222,7 +222,10 @@ class RecurrentBlock:
     def forward(self, h0, e, weights: dict, T: int | None = None, out=None, aux: dict | None = None,
                 workspace=None, stream=None):
         """out = h_T. Tensors live on the GPU; aux maps rdt_aux field names to
-        preallocated device tensors."""
+        preallocated device tensors. In graph mode the library replays the graph
+        it captured for the same pointers and T: pass the same out (and
+        workspace) on every call to replay it; a fresh out per call (out=None)
+        captures a new graph whenever the allocator returns a new address."""
         return self._run(False, h0, e, weights, T, out, aux, workspace, stream)[0]
 
     def forward_noalloc(self, h0, e, weights: dict, T: int | None = None, out=None, aux: dict | None = None,
