@@ -76,6 +76,15 @@ RDT_DEV void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
 // and waiting for them at every chunk cost a 256x256 tile about 20 us.
 RDT_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// SiLU(g) * u of the SwiGLU experts, g / (1 + e^-g) * u, with the hardware
+// 2^x and reciprocal (v_exp_f32, v_rcp_f32, about 1 ulp each; e^-g is
+// 2^(-g log2 e)). Every expert epilogue uses this one definition, so tile
+// shapes do not change results. The IEEE expf and division cost the 256x256
+// gate/up launch on the wide MoE shape 6 % (662 -> 623 us).
+RDT_DEV float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g)) * u;
+}
+
 // wave64 reductions
 RDT_DEV float wave_sum(float v) {
 #pragma unroll

@@ -858,7 +858,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float gt = acc[i][jj][r], up = acc[i][jj + 2][r];
-            sb[(16 * i + 4 * (lane >> 4) + r) * P + 16 * jj + (lane & 15)] = f2bf(gt / (1.f + expf(-gt)) * up);
+            sb[(16 * i + 4 * (lane >> 4) + r) * P + 16 * jj + (lane & 15)] = f2bf(silu_mul(gt, up));
           }
       wave_lds_sync();
       T* C = reinterpret_cast<T*>(g.C);
@@ -938,7 +938,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const float gt = crow[c8 + x], up = crow[BN / 2 + c8 + x];
-          v[x] = gt / (1.f + expf(-gt)) * up;
+          v[x] = silu_mul(gt, up);
         }
       } else {
 #pragma unroll
