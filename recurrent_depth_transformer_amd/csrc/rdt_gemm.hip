@@ -839,8 +839,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
     else gemm_mainloop_pp<false>(acc, ring, ap, bp, Kl, A, bd);
     // Epilogue, wave by wave (no workgroup barrier): the wave's outputs go
     // through its own 20 KB slice of the ring (free once every wave has passed
-    // the loop's last barrier) and out as 16-byte row vectors. Rows of the
-    // wave: tile rows 128g .. 128g + 127.
+    // the loop's last barrier) as fp32 (whole-dword LDS writes; single bf16
+    // writes measured 2.5 % slower on the down projection) and leave as
+    // 16-byte bf16 row vectors. Rows of the wave: tile rows 128g .. 128g + 127.
     constexpr int WSLICE = 5 * PP_SLOT / 8;
     const int lane = tid & 63, wave = tid >> 6, wg = wave >> 2, wq = wave & 3;
     char* wbuf = ring + wave * WSLICE;
@@ -848,9 +849,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
     if constexpr (KIND == 0) {
       // SwiGLU of features n0 + 32wq .. +31: fragments 0, 1 hold the gate and
       // 2, 3 the up projections of the same 16-feature columns
-      constexpr int P = 40;  // staging row pitch (bf16)
-      static_assert(128 * P * 2 <= WSLICE, "SwiGLU staging exceeds the wave's slice");
-      bf16_t* sb = reinterpret_cast<bf16_t*>(wbuf);
+      constexpr int P = 36;  // fp32 staging row pitch (full-dword LDS writes)
+      static_assert(128 * P * 4 <= WSLICE, "SwiGLU staging exceeds the wave's slice");
+      float* sf = reinterpret_cast<float*>(wbuf);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -858,7 +859,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float gt = acc[i][jj][r], up = acc[i][jj + 2][r];
-            sb[(16 * i + 4 * (lane >> 4) + r) * P + 16 * jj + (lane & 15)] = f2bf(silu_mul(gt, up));
+            sf[(16 * i + 4 * (lane >> 4) + r) * P + 16 * jj + (lane & 15)] = silu_mul(gt, up);
           }
       wave_lds_sync();
       T* C = reinterpret_cast<T*>(g.C);
@@ -866,28 +867,37 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
       for (int it = 0; it < 8; ++it) {
         const int v = lane + 64 * it, row = v >> 2, c4 = v & 3;
         const int m = ml0 + 128 * wg + row, f = n0 + 32 * wq + 8 * c4;
-        const uint4 val = *reinterpret_cast<const uint4*>(sb + row * P + 8 * c4);
-        if (m < rows_g && f < g.N) *reinterpret_cast<uint4*>(C + (long long)(pbase + m) * g.ldc + f) = val;
+        const float4 x0 = *reinterpret_cast<const float4*>(sf + row * P + 8 * c4);
+        const float4 x1 = *reinterpret_cast<const float4*>(sf + row * P + 8 * c4 + 4);
+        const float vv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        if (m < rows_g && f < g.N) store8<T>(C + (long long)(pbase + m) * g.ldc + f, vv);
       }
     } else {
-      constexpr int P = 72;  // staging row pitch (bf16)
-      static_assert(128 * P * 2 <= WSLICE, "output staging exceeds the wave's slice");
-      bf16_t* sb = reinterpret_cast<bf16_t*>(wbuf);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sb[(16 * i + 4 * (lane >> 4) + r) * P + 16 * j + (lane & 15)] = f2bf(acc[i][j][r]);
-      wave_lds_sync();
+      // fp32 staging (full-dword LDS writes), 64 rows per pass
+      constexpr int P = 68;
+      static_assert(64 * P * 4 <= WSLICE, "output staging exceeds the wave's slice");
+      float* sf = reinterpret_cast<float*>(wbuf);
       T* C = reinterpret_cast<T*>(g.C);
 #pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int v = lane + 64 * it, row = v >> 3, c8 = v & 7;
-        const int m = ml0 + 128 * wg + row, col = n0 + 64 * wq + 8 * c8;
-        const uint4 val = *reinterpret_cast<const uint4*>(sb + row * P + 8 * c8);
-        if (m < rows_g && col < g.N) *reinterpret_cast<uint4*>(C + (long long)(pbase + m) * g.ldc + col) = val;
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              sf[(16 * i + 4 * (lane >> 4) + r) * P + 16 * j + (lane & 15)] = acc[4 * half + i][j][r];
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int v = lane + 64 * it, row = v >> 3, c8 = v & 7;
+          const int m = ml0 + 128 * wg + 64 * half + row, col = n0 + 64 * wq + 8 * c8;
+          const float4 x0 = *reinterpret_cast<const float4*>(sf + row * P + 8 * c8);
+          const float4 x1 = *reinterpret_cast<const float4*>(sf + row * P + 8 * c8 + 4);
+          const float vv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          if (m < rows_g && col < g.N) store8<T>(C + (long long)(pbase + m) * g.ldc + col, vv);
+        }
+        wave_lds_sync();
       }
     }
     return;
