@@ -275,8 +275,19 @@ static void pick_tile(long long M, long long N, int min_bn, int* bm, int* bn) {
 // stream a tile about 1.5x faster. Measured in place against four waves:
 // forwards 1-6 % faster (MLA -4 %, ACT -5 %, Dreamer -2 % with 128x128 tiles
 // instead of 128x192 ones), one-token decode -3 %.
+//
+// A plain store (one weight segment, no RoPE, rows stored in place) that fills
+// whole rounds of 256x256 tiles over 256 CUs, or at least four, runs on the
+// 256x256 ping-pong tiles of the expert GEMMs with a per-wave epilogue (wide
+// MoE output projection: 256 tiles). The RoPE projections stay on 128x128:
+// on 256x256 tiles the wide MoE QKV projection (384 tiles) measured slower.
 static hipError_t dense_gemm(DenseGemm& g, hipStream_t s) {
-  if (g.dtype == DT_BF16 && g.bm == g.bn && (g.bm == 64 || g.bm == 128)) g.nw = 8;
+  if (g.dtype == DT_BF16 && g.bm == 128 && g.bn == 128 && !g.A2 && g.batch <= 1 && g.epi == EPI_STORE &&
+      g.nseg == 1 && !g.seg[0].rope && !g.seg[0].scatter && !g.seg[0].row_mul) {
+    const long long tiles = (long long)((g.M + 255) / 256) * ((g.seg[0].ncols + 255) / 256);
+    if (tiles >= 256 && (tiles % 256 == 0 || tiles >= 4 * 256)) g.bm = g.bn = 256;
+  }
+  if (g.dtype == DT_BF16 && g.bm == g.bn && (g.bm == 64 || g.bm == 128 || g.bm == 256)) g.nw = 8;
   return launch_dense_gemm(g, s);
 }
 

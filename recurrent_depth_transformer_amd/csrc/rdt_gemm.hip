@@ -478,12 +478,7 @@ template <typename T, int BM, int BN, bool TWO, int NS, int NW>
 __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) void k_dense_gemm(DenseGemm g) {
   static_assert(sizeof(T) == 2 || NW == 4, "the fp32 path runs four waves");
   using S = GemmShape<T, BM, BN, NW>;
-  constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS, NW>::STAGE : S::SMEM;
-  __shared__ __align__(16) char L0[ST];
-  __shared__ __align__(16) char L1[sizeof(T) == 2 ? ST : 16];
-  __shared__ __align__(16) char L2[sizeof(T) == 2 && NS > 2 ? ST : 16];
-  __shared__ __align__(16) char L3[sizeof(T) == 2 && NS > 3 ? ST : 16];
-  char* smem = L0;
+  static_assert(BM != 256 || (sizeof(T) == 2 && BN == 256 && NW == 8 && !TWO), "256x256 tiles: bf16, one K phase");
   const int Mact = g.Mdev ? *g.Mdev : g.M;
   int ntot = 0;
   for (int s = 0; s < g.nseg; ++s) ntot += g.seg[s].ncols;
@@ -536,6 +531,53 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
     }
   }
 
+  if constexpr (BM == 256) {
+    // 256x256 ping-pong tiles (the expert GEMMs' main loop) for plain stores:
+    // one B segment, no RoPE, output row = the compacted row (the host's rule).
+    // Each wave writes its 128 x 64 outputs through its own LDS slice (fp32,
+    // 64 rows per pass), no workgroup barrier.
+    __shared__ __align__(16) char ring[5 * PP_SLOT];
+    const T* bd = reinterpret_cast<const T*>(g.seg[0].B) + (long long)z * g.b_bstride;
+    f32x4 acc[8][4];
+    gemm_mainloop_pp<false>(acc, ring, ap, bp, g.K, A, bd);
+    constexpr int P = 68;
+    static_assert(64 * P * 4 <= 5 * PP_SLOT / 8, "staging exceeds the wave's slice");
+    const int lane = tid & 63, wave = tid >> 6, wg = wave >> 2, wq = wave & 3;
+    float* sf = reinterpret_cast<float*>(ring + wave * (5 * PP_SLOT / 8));
+    const GemmSeg& sg = g.seg[0];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sf[(16 * i + 4 * (lane >> 4) + r) * P + 16 * j + (lane & 15)] = acc[4 * half + i][j][r];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int v = lane + 64 * it, row = v >> 3, c8 = v & 7;
+        const int m = m0 + 128 * wg + 64 * half + row, col = n0 + 64 * wq + 8 * c8;
+        const float4 x0 = *reinterpret_cast<const float4*>(sf + row * P + 8 * c8);
+        const float4 x1 = *reinterpret_cast<const float4*>(sf + row * P + 8 * c8 + 4);
+        const float vv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        if (m < Mact && col < ntot) {
+          const long long off = (long long)z * g.c_bstride + (long long)m * sg.ldc + col;
+          if (sg.out_f32) store8<float>(reinterpret_cast<float*>(sg.C) + off, vv);
+          else store8<T>(reinterpret_cast<T*>(sg.C) + off, vv);
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    return;
+  } else {
+  constexpr int ST = sizeof(T) == 2 ? LdsRing<BM, BN, NS, NW>::STAGE : S::SMEM;
+  __shared__ __align__(16) char L0[ST];
+  __shared__ __align__(16) char L1[sizeof(T) == 2 ? ST : 16];
+  __shared__ __align__(16) char L2[sizeof(T) == 2 && NS > 2 ? ST : 16];
+  __shared__ __align__(16) char L3[sizeof(T) == 2 && NS > 3 ? ST : 16];
+  char* smem = L0;
   f32x4 acc[S::FM][S::FN];
   if constexpr (sizeof(T) == 2) {
     const T* bd = reinterpret_cast<const T*>(g.seg[0].B) + (long long)z * g.b_bstride;
@@ -658,6 +700,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
     }
     lds_barrier();
   }
+  }
 }
 
 template <typename T, int BM, int BN, int NS, int NW = 4>
@@ -667,7 +710,8 @@ static hipError_t dense_launch(const DenseGemm& g, hipStream_t s) {
   const int ntn = (ntot + BN - 1) / BN, ntm = (g.M + BM - 1) / BM;
   dim3 grid(ntn * ntm, 1, g.batch > 0 ? g.batch : 1);
   if (g.A2) {
-    hipLaunchKernelGGL((k_dense_gemm<T, BM, BN, true, NS, NW>), grid, dim3(NW * 64), 0, s, g);
+    if constexpr (BM == 256) return hipErrorInvalidValue;  // one K phase only
+    else hipLaunchKernelGGL((k_dense_gemm<T, BM, BN, true, NS, NW>), grid, dim3(NW * 64), 0, s, g);
   } else {
     hipLaunchKernelGGL((k_dense_gemm<T, BM, BN, false, NS, NW>), grid, dim3(NW * 64), 0, s, g);
   }
@@ -692,7 +736,12 @@ static hipError_t dense_ns(const DenseGemm& g, hipStream_t s) {
 template <typename T>
 static hipError_t dense_dispatch(const DenseGemm& g, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (g.nw == 8) {  // eight waves: 64x64 tiles with three stages, 128x128 with two
+    if (g.nw == 8) {  // eight waves: 64x64 tiles with three stages, 128x128 with two, 256x256 ping-pong
+      if (g.bm == 256 && g.bn == 256) {
+        const GemmSeg& sg = g.seg[0];
+        if (g.A2 || g.nseg != 1 || g.epi != EPI_STORE || sg.rope || sg.scatter || sg.row_mul) return hipErrorInvalidValue;
+        return dense_launch<T, 256, 256, 2, 8>(g, s);
+      }
       if (g.bm == 64 && g.bn == 64) return dense_launch<T, 64, 64, 3, 8>(g, s);
       if (g.bm == 128 && g.bn == 128) return dense_launch<T, 128, 128, 2, 8>(g, s);
       return hipErrorInvalidValue;
