@@ -814,15 +814,17 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
   // band walked m-tile by m-tile with its n-tiles innermost. Tiles that share
   // A rows start together, and so do (GUB tiles apart) tiles that share weight
   // rows; L2 keeps data only for a few of the 32 k-stages of a tile, so tiles
-  // that start far apart fetch shared operands again (wide MoE shape: 2.7 ->
-  // 1.8 GB fetched per launch, 1-2 % faster). Otherwise n-tiles innermost.
+  // that start far apart fetch shared operands again (wide MoE shape, 256x256
+  // tiles: 2.7 GB fetched per launch with n-tiles innermost, 1.64 GB with
+  // bands of 2, 1.46 GB with bands of 4, 1.61 GB with bands of 8, the last
+  // three equally fast). Otherwise n-tiles innermost.
   int mt, nt;
   if constexpr (KIND == 1 && BM == 64) {
     const int r = L - tstart * ntn;
     nt = r / tlg;
     mt = tstart + r % tlg;
   } else if constexpr (KIND == 0) {
-    constexpr int GUB = 2;
+    constexpr int GUB = 4;
     const int r = L - tstart * ntn;
     const int band = r / (tlg * GUB), rem = r % (tlg * GUB);
     const int bsz = ntn - band * GUB < GUB ? ntn - band * GUB : GUB;
