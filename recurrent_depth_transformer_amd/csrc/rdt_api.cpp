@@ -276,17 +276,24 @@ static void pick_tile(long long M, long long N, int min_bn, int* bm, int* bn) {
 // forwards 1-6 % faster (MLA -4 %, ACT -5 %, Dreamer -2 % with 128x128 tiles
 // instead of 128x192 ones), one-token decode -3 %.
 //
-// A plain store (one weight segment, no RoPE, rows stored in place) that fills
-// whole rounds of 256x256 tiles over 256 CUs, or at least four, runs on the
-// 256x256 ping-pong tiles of the expert GEMMs with a per-wave epilogue (wide
-// MoE output projection: 256 tiles). The RoPE projections stay on 128x128:
-// on 256x256 tiles the wide MoE QKV projection (384 tiles) measured slower.
+// A projection with one weight segment (rows stored in place or scattered to
+// their token, RoPE over 64- or 128-wide heads or none, no depth RoPE, no
+// cache rows) that fills whole rounds of 256x256 tiles over 256 CUs, or at
+// least four, runs on the 256x256 ping-pong tiles of the expert GEMMs with a
+// per-wave epilogue (wide MoE: the output projection and the query projection,
+// 256 tiles each).
+static bool big_tiles_ok(const DenseGemm& g) {
+  const GemmSeg& s0 = g.seg[0];
+  if (g.dtype != DT_BF16 || g.bm != 128 || g.bn != 128 || g.A2 || g.batch > 1 || g.epi != EPI_STORE ||
+      g.nseg != 1 || s0.row_mul)
+    return false;
+  if (s0.rope && (g.drope || (g.rope_dim != 64 && g.rope_dim != 128) || s0.ncols % g.rope_dim)) return false;
+  const long long tiles = (long long)((g.M + 255) / 256) * ((s0.ncols + 255) / 256);
+  return tiles >= 256 && (tiles % 256 == 0 || tiles >= 4 * 256);
+}
+
 static hipError_t dense_gemm(DenseGemm& g, hipStream_t s) {
-  if (g.dtype == DT_BF16 && g.bm == 128 && g.bn == 128 && !g.A2 && g.batch <= 1 && g.epi == EPI_STORE &&
-      g.nseg == 1 && !g.seg[0].rope && !g.seg[0].scatter && !g.seg[0].row_mul) {
-    const long long tiles = (long long)((g.M + 255) / 256) * ((g.seg[0].ncols + 255) / 256);
-    if (tiles >= 256 && (tiles % 256 == 0 || tiles >= 4 * 256)) g.bm = g.bn = 256;
-  }
+  if (big_tiles_ok(g)) g.bm = g.bn = 256;
   if (g.dtype == DT_BF16 && g.bm == g.bn && (g.bm == 64 || g.bm == 128 || g.bm == 256)) g.nw = 8;
   return launch_dense_gemm(g, s);
 }
@@ -510,8 +517,19 @@ static rdt_status enqueue(const Fwd& f, hipStream_t s, Prof* prof = nullptr) {
       g.M = N;
       if (!act) {
         g.rows = nullptr; g.gather = 0; g.Mdev = nullptr;
-        g.nseg = 3; g.seg[0] = sq; g.seg[1] = sk; g.seg[2] = sv;
-        pick_tile(N, Hd + 2 * KVd, P.d, &g.bm, &g.bn);
+        // the query projection alone when it fills the 256x256 tiles (wide
+        // MoE: 114 against 140 us per loop for q, k and v on 128x128 tiles),
+        // else q, k and v in one launch
+        DenseGemm gq = g;
+        gq.nseg = 1; gq.seg[0] = sq; gq.bm = gq.bn = 128;
+        if (big_tiles_ok(gq)) {
+          LAUNCH(RDT_STAGE_QKV, dense_gemm(gq, sa));
+          g.nseg = 2; g.seg[0] = sk; g.seg[1] = sv;
+          pick_tile(N, 2 * KVd, P.d, &g.bm, &g.bn);
+        } else {
+          g.nseg = 3; g.seg[0] = sq; g.seg[1] = sk; g.seg[2] = sv;
+          pick_tile(N, Hd + 2 * KVd, P.d, &g.bm, &g.bn);
+        }
         LAUNCH(RDT_STAGE_QKV, dense_gemm(g, sa));
       } else {
         DenseGemm gq = g;

@@ -517,9 +517,16 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
       if (TWO) ap2[i] = reinterpret_cast<const T*>(g.A2) + (long long)row * g.lda2;
     }
   }
+  // 256x256 tiles with RoPE over 128-wide heads: wave q's 64 columns are dims
+  // 32(q & 1) .. +31 of head q >> 1 and then their partners 64 dims on, so a
+  // lane holds both members of its rotation pairs (64-wide heads already lie
+  // that way: one head per wave, partners 32 columns apart)
+  const bool perm128 = BM == 256 && g.seg[0].rope && g.rope_dim == 128;
 #pragma unroll
   for (int i = 0; i < S::B_LD; ++i) {
-    const int c = n0 + (tid + i * S::NT) / S::VPR;
+    int r = (tid + i * S::NT) / S::VPR;
+    if (perm128) r = 128 * (r >> 7) + 32 * ((r >> 6) & 1) + (r & 31) + ((r & 32) ? 64 : 0);
+    const int c = n0 + r;
     bp[i] = nullptr;
     bp2[i] = nullptr;
     if (c < ntot) {
@@ -532,10 +539,11 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
   }
 
   if constexpr (BM == 256) {
-    // 256x256 ping-pong tiles (the expert GEMMs' main loop) for plain stores:
-    // one B segment, no RoPE, output row = the compacted row (the host's rule).
-    // Each wave writes its 128 x 64 outputs through its own LDS slice (fp32,
-    // 64 rows per pass), no workgroup barrier.
+    // 256x256 ping-pong tiles (the expert GEMMs' main loop) for one B segment
+    // whose rows are stored in place or scattered to their token, with or
+    // without RoPE over 64- or 128-wide heads (no depth RoPE, no cache rows:
+    // the host's rule). Each wave writes its 128 x 64 outputs through its own
+    // LDS slice (fp32, 64 rows per pass), no workgroup barrier.
     __shared__ __align__(16) char ring[5 * PP_SLOT];
     const T* bd = reinterpret_cast<const T*>(g.seg[0].B) + (long long)z * g.b_bstride;
     f32x4 acc[8][4];
@@ -555,17 +563,59 @@ __global__ __launch_bounds__(NW * 64, (NW == 8 && BM * BN <= 16384) ? 4 : 1) voi
           for (int r = 0; r < 4; ++r)
             sf[(16 * i + 4 * (lane >> 4) + r) * P + 16 * j + (lane & 15)] = acc[4 * half + i][j][r];
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (!sg.rope) {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int v = lane + 64 * it, row = v >> 3, c8 = v & 7;
-        const int m = m0 + 128 * wg + 64 * half + row, col = n0 + 64 * wq + 8 * c8;
-        const float4 x0 = *reinterpret_cast<const float4*>(sf + row * P + 8 * c8);
-        const float4 x1 = *reinterpret_cast<const float4*>(sf + row * P + 8 * c8 + 4);
-        const float vv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        if (m < Mact && col < ntot) {
-          const long long off = (long long)z * g.c_bstride + (long long)m * sg.ldc + col;
-          if (sg.out_f32) store8<float>(reinterpret_cast<float*>(sg.C) + off, vv);
-          else store8<T>(reinterpret_cast<T*>(sg.C) + off, vv);
+        for (int it = 0; it < 8; ++it) {
+          const int v = lane + 64 * it, row = v >> 3, c8 = v & 7;
+          const int m = m0 + 128 * wg + 64 * half + row, col = n0 + 64 * wq + 8 * c8;
+          const float4 x0 = *reinterpret_cast<const float4*>(sf + row * P + 8 * c8);
+          const float4 x1 = *reinterpret_cast<const float4*>(sf + row * P + 8 * c8 + 4);
+          const float vv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          if (m < Mact && col < ntot) {
+            const long long orow = sg.scatter && g.rows ? g.rows[m] : m;
+            const long long off = (long long)z * g.c_bstride + orow * sg.ldc + col;
+            if (sg.out_f32) store8<float>(reinterpret_cast<float*>(sg.C) + off, vv);
+            else store8<T>(reinterpret_cast<T*>(sg.C) + off, vv);
+          }
+        }
+      } else {
+        // RoPE: lane item (row, c4) takes 8 dims j .. j+7 of the first half of
+        // a head (staged columns 8c4 ..) and their partners j + rh .. (staged
+        // 32 columns on); same arithmetic as the smaller tiles' epilogue
+        const int rh = g.rope_dim >> 1;  // 32 or 64
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int v = lane + 64 * it, row = v >> 2, c4 = v & 3;
+          const int m = m0 + 128 * wg + 64 * half + row;
+          const int jj = (rh == 64 ? 32 * (wq & 1) : 0) + 8 * c4;  // dim inside the half
+          const int colA = n0 + (rh == 64 ? 128 * (wq >> 1) : 64 * wq) + jj, colB = colA + rh;
+          const float* xa = sf + row * P + 8 * c4;
+          const float* xb = xa + 32;
+          if (m < Mact && colB < ntot) {
+            const int tok = g.rows ? g.rows[m] : m;
+            const long long orow = sg.scatter ? tok : m;
+            const int pp = g.pos_dev ? *g.pos_dev : tok % g.seq;
+            const float4 c0 = *reinterpret_cast<const float4*>(g.cosb + pp * rh + jj);
+            const float4 c1 = *reinterpret_cast<const float4*>(g.cosb + pp * rh + jj + 4);
+            const float4 s0 = *reinterpret_cast<const float4*>(g.sinb + pp * rh + jj);
+            const float4 s1 = *reinterpret_cast<const float4*>(g.sinb + pp * rh + jj + 4);
+            const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            float va[8], vb[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+              va[x] = xa[x] * cs[x] - xb[x] * sn[x];
+              vb[x] = xa[x] * sn[x] + xb[x] * cs[x];
+            }
+            const long long off = (long long)z * g.c_bstride + orow * sg.ldc;
+            if (sg.out_f32) {
+              store8<float>(reinterpret_cast<float*>(sg.C) + off + colA, va);
+              store8<float>(reinterpret_cast<float*>(sg.C) + off + colB, vb);
+            } else {
+              store8<T>(reinterpret_cast<T*>(sg.C) + off + colA, va);
+              store8<T>(reinterpret_cast<T*>(sg.C) + off + colB, vb);
+            }
+          }
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -739,7 +789,10 @@ static hipError_t dense_dispatch(const DenseGemm& g, hipStream_t s) {
     if (g.nw == 8) {  // eight waves: 64x64 tiles with three stages, 128x128 with two, 256x256 ping-pong
       if (g.bm == 256 && g.bn == 256) {
         const GemmSeg& sg = g.seg[0];
-        if (g.A2 || g.nseg != 1 || g.epi != EPI_STORE || sg.rope || sg.scatter || sg.row_mul) return hipErrorInvalidValue;
+        if (g.A2 || g.nseg != 1 || g.epi != EPI_STORE || sg.row_mul) return hipErrorInvalidValue;
+        if (sg.rope && (g.drope || (g.rope_dim != 64 && g.rope_dim != 128) || sg.ncols % g.rope_dim ||
+                        !g.cosb || !g.sinb || (!g.pos_dev && g.seq <= 0)))
+          return hipErrorInvalidValue;
         return dense_launch<T, 256, 256, 2, 8>(g, s);
       }
       if (g.bm == 64 && g.bn == 64) return dense_launch<T, 64, 64, 3, 8>(g, s);

@@ -211,3 +211,26 @@ def test_expert_tiles_ragged_many_rows():
     print(f"[tiles] routing mismatches={mism} near_ties={near} compared={comp}", flush=True)
     assert mism == 0
     assert end_to_end_prefix("ragged_tiles", cfg, inp, res, T, P=cfg["seq"]) <= TOL
+
+
+@pytest.mark.parametrize("heads,kv,hd", [(15, 5, 128), (30, 6, 64)])
+def test_query_projection_big_tiles_ragged(heads, kv, hd):
+    """The query projection on 256x256 tiles with RoPE in the per-wave
+    epilogue: 129 sequences of 257 tokens (33 153 rows, the last row tile
+    part-filled) and 1920 query columns (the last column tile holds one
+    128-wide head, or two 64-wide ones), over four rounds of tiles (the rule
+    that selects them); 128-wide heads permute their weight rows so a lane
+    holds both members of a rotation pair. End to end on the first and last
+    sequence against the oracle with routing forced."""
+    cfg = get_config("gqa_small", batch=129, seq=257, dim=256, n_heads=heads, n_kv_heads=kv, head_dim=hd, T=2)
+    T, N = cfg["T"], cfg["batch"] * cfg["seq"]
+    tiles = -(-N // 256) * -(-heads * hd // 256)
+    assert tiles >= 1024 and N % 256 and (heads * hd) % 256
+    print(f"[tiles] query projection on 256x256 tiles: {N} tokens, {heads} heads of {hd}", flush=True)
+    res, inp, *_ = run_gpu(cfg, T=T)
+    assert np.all(np.isfinite(res["h"]))
+    stats = {}
+    mism, near, comp = check_routing_teacher_forced(cfg, inp, res, T, ro, stats)
+    print(f"[tiles] routing mismatches={mism} near_ties={near} compared={comp}", flush=True)
+    assert mism == 0
+    assert end_to_end_prefix(f"q_tiles_{hd}", cfg, inp, res, T, P=cfg["seq"]) <= TOL
